@@ -1,0 +1,277 @@
+// kernel_copy.hip -- full-grid round trip global -> LDS -> global through two
+// tensor maps, with a multi-stage LDS ring ([MLC] "TMA in a pipeline": fill
+// stage k+1 while stage k is consumed).
+//
+// Design for gfx950.  A box of B bytes is split into 1 KiB groups (64 lanes x
+// 16 bytes, one global_load_lds_dwordx4 each).  The swizzle only permutes
+// chunks inside a 128-byte unit, so the wave that loads a group holds every
+// chunk it later stores: each wave owns GPW groups of every box and runs its
+// own S-deep ring without any workgroup barrier.  Completion of a stage is the
+// wave's s_waitcnt vmcnt, counted in DMA instructions issued after that stage;
+// LDS reads are inline-asm ds_read_b128 at the swizzled address and go out as
+// coalesced global_store_dwordx4 in logical order.  Edge tiles, element
+// strides or shapes that do not split evenly take the generic path: one
+// workgroup per box through tile_load_issue / tile_store_issue.
+#include <hip/hip_runtime.h>
+
+#include "host_util.hpp"
+#include "tile_device.hpp"
+#include "tmap.h"
+
+namespace att {
+
+struct CopyArgs {
+    TmapImpl src;
+    TmapImpl dst;
+    uint32_t ntiles;
+    uint32_t nt[5];     // tiles per dimension
+};
+
+constexpr uint32_t kCopyWaves = 4;
+
+// Byte offsets of tile t's origin in src and dst (tiles innermost first).
+__device__ __forceinline__ void tile_origin(const CopyArgs& a, uint32_t t, uint64_t& so, uint64_t& dof,
+                                            int32_t c[5]) {
+    so = 0;
+    dof = 0;
+#pragma unroll
+    for (int d = 0; d < 5; ++d) {
+        const uint32_t n = a.nt[d];
+        const uint32_t td = t % n;
+        t /= n;
+        c[d] = (int32_t)(td * (a.src.box_m1[d] + 1u));
+        const uint64_t e = (uint64_t)c[d];
+        so += d == 0 ? e * a.src.esize : e * a.src.stride[d - 1];
+        dof += d == 0 ? e * a.dst.esize : e * a.dst.stride[d - 1];
+    }
+}
+
+template <int GPW>
+__device__ __forceinline__ void lds_read_group(const uint32_t (&addr)[GPW], u32x4 (&v)[GPW]);
+
+template <>
+__device__ __forceinline__ void lds_read_group<1>(const uint32_t (&a)[1], u32x4 (&v)[1]) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v[0]) : "v"(a[0]) : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read_group<2>(const uint32_t (&a)[2], u32x4 (&v)[2]) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]) : "v"(a[0]), "v"(a[1]) : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read_group<4>(const uint32_t (&a)[4], u32x4 (&v)[4]) {
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
+                 "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
+}
+template <>
+__device__ __forceinline__ void lds_read_group<8>(const uint32_t (&a)[8], u32x4 (&v)[8]) {
+    asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\t"
+                 "ds_read_b128 %3, %11\n\tds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
+                 "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
+                   "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]),
+                   "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]) : "memory");
+}
+
+// Wait until at most `pending_groups` of this wave's DMA instructions are in
+// flight.  Loads complete in issue order, so this retires every load issued
+// before the last `pending_groups` of them.
+template <int GPW, int S>
+__device__ __forceinline__ void wait_stage(uint32_t later_stages) {
+    if constexpr (S >= 4) { if (later_stages >= 3) { wait_vmcnt<3 * GPW>(); return; } }
+    if constexpr (S >= 3) { if (later_stages >= 2) { wait_vmcnt<2 * GPW>(); return; } }
+    if constexpr (S >= 2) { if (later_stages >= 1) { wait_vmcnt<GPW>(); return; } }
+    wait_vmcnt<0>();
+}
+
+template <int GPW, int S, bool NT>
+__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t lane = lane_id();
+    const uint32_t B = a.src.box_bytes;
+    const uint32_t sw = a.src.swizzle;
+
+    // Per-lane constants, identical for every tile: where the chunk this lane
+    // loads comes from, where the chunk it stores goes, and which LDS slot
+    // holds the latter.
+    uint64_t ld_off[GPW], st_off[GPW];
+    uint32_t rd[GPW];
+    const int32_t zero[5] = {0, 0, 0, 0, 0};
+    const uint32_t lds0 = lds_addr_of(smem);
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        const uint32_t grp = wave * GPW + j;
+        const uint32_t p = grp * 64u + lane;
+        const ChunkLoc ls = chunk_locate(a.src, zero, swz_chunk(p, sw));
+        ld_off[j] = (uint64_t)(ls.g0 * a.src.esize + ls.rest_off);
+        const ChunkLoc ld = chunk_locate(a.dst, zero, p);
+        st_off[j] = (uint64_t)(ld.g0 * a.dst.esize + ld.rest_off);
+        rd[j] = lds0 + swz_chunk(p, sw) * 16u;
+    }
+
+    const uint32_t T = a.ntiles;
+    const uint32_t first = blockIdx.x;
+    if (first >= T) return;
+    const uint32_t nmine = (T - 1 - first) / gridDim.x + 1;
+
+    auto issue = [&](uint32_t n) {
+        uint64_t so, dof;
+        int32_t c[5];
+        tile_origin(a, first + n * gridDim.x, so, dof, c);
+        uint8_t* stage = smem + (n % S) * B;
+        const uint64_t sb = a.src.base + so;
+#pragma unroll
+        for (int j = 0; j < GPW; ++j)
+            dma16((const void*)(uintptr_t)(sb + ld_off[j]), stage + (wave * GPW + j) * 1024u);
+    };
+
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+        if ((uint32_t)s < nmine) issue(s);
+
+    for (uint32_t n = 0; n < nmine; ++n) {
+        if (n + S - 1 < nmine) issue(n + S - 1);
+        const uint32_t left = nmine - 1 - n;
+        wait_stage<GPW, S>(left < (uint32_t)(S - 1) ? left : (uint32_t)(S - 1));
+        uint32_t addr[GPW];
+        const uint32_t soff = (n % S) * B;
+#pragma unroll
+        for (int j = 0; j < GPW; ++j) addr[j] = rd[j] + soff;
+        u32x4 v[GPW];
+        lds_read_group<GPW>(addr, v);
+        uint64_t so, dof;
+        int32_t c[5];
+        tile_origin(a, first + n * gridDim.x, so, dof, c);
+        gbyte* db = gptr(a.dst.base + dof);
+#pragma unroll
+        for (int j = 0; j < GPW; ++j) {
+            ATT_GLOBAL u32x4* p = (ATT_GLOBAL u32x4*)(db + st_off[j]);
+            if constexpr (NT) __builtin_nontemporal_store(v[j], p);
+            else *p = v[j];
+        }
+    }
+}
+
+// Generic round trip: one workgroup per tile, any geometry.
+__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_generic(CopyArgs a) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    const uint32_t wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    uint64_t so, dof;
+    int32_t c[5];
+    tile_origin(a, blockIdx.x, so, dof, c);
+    tile_load_issue(a.src, c, smem, wave, nwaves);
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    __syncthreads();
+    tile_store_issue<false>(a.dst, c, smem, wave, nwaves);
+}
+
+template <int GPW, int S, bool NT>
+static tmap_status launch_ring(const CopyArgs& a, uint32_t grid, hipStream_t st) {
+    const uint32_t lds = (uint32_t)S * a.src.box_bytes;
+    hipError_t e = hipFuncSetAttribute((const void*)k_tile_copy_ring<GPW, S, NT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+    hipLaunchKernelGGL((k_tile_copy_ring<GPW, S, NT>), dim3(grid), dim3(kCopyWaves * 64), lds, st, a);
+    return check_launch("tile_copy");
+}
+
+template <int GPW, bool NT>
+static tmap_status launch_ring_s(const CopyArgs& a, uint32_t stages, uint32_t grid, hipStream_t st) {
+    switch (stages) {
+    case 1: return launch_ring<GPW, 1, NT>(a, grid, st);
+    case 2: return launch_ring<GPW, 2, NT>(a, grid, st);
+    case 3: return launch_ring<GPW, 3, NT>(a, grid, st);
+    default: return launch_ring<GPW, 4, NT>(a, grid, st);
+    }
+}
+
+template <bool NT>
+static tmap_status launch_ring_g(const CopyArgs& a, uint32_t gpw, uint32_t stages, uint32_t grid, hipStream_t st) {
+    switch (gpw) {
+    case 1: return launch_ring_s<1, NT>(a, stages, grid, st);
+    case 2: return launch_ring_s<2, NT>(a, stages, grid, st);
+    case 4: return launch_ring_s<4, NT>(a, stages, grid, st);
+    default: return launch_ring_s<8, NT>(a, stages, grid, st);
+    }
+}
+
+// Persistent grid: workgroups per CU chosen to minimise the tail of the last
+// round of tiles, within what LDS allows.
+static uint32_t auto_grid(uint32_t ntiles, uint32_t cus, uint32_t lds_per_wg) {
+    uint32_t max_k = lds_per_wg ? (uint32_t)(TMAP_LDS_CAPACITY / lds_per_wg) : 8u;
+    if (max_k > 8) max_k = 8;
+    if (max_k < 1) max_k = 1;
+    uint32_t best = cus, best_k = 1;
+    double best_eff = -1.0;
+    for (uint32_t k = 1; k <= max_k; ++k) {
+        const uint64_t g = (uint64_t)cus * k;
+        const uint64_t per = (ntiles + g - 1) / g;
+        const double eff = (double)ntiles / (double)(g * per);
+        if (eff > best_eff + 1e-9 || (eff > best_eff - 1e-9 && k > best_k)) {
+            best_eff = eff;
+            best = (uint32_t)g;
+            best_k = k;
+        }
+    }
+    return best < ntiles ? best : ntiles;
+}
+
+}  // namespace att
+
+using namespace att;
+
+extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32_t stages, uint32_t grid,
+                                    uint32_t variant, void* stream) {
+    if (!src || !dst) return TMAP_ERR_NULL;
+    if (stages < 1 || stages > 4 || variant > 2) return TMAP_ERR_UNSUPPORTED;
+    CopyArgs a;
+    a.src = load_map(src);
+    a.dst = load_map(dst);
+    if (a.src.dtype != a.dst.dtype || a.src.rank != a.dst.rank || a.src.swizzle != a.dst.swizzle)
+        return TMAP_ERR_UNSUPPORTED;
+    bool even = true;
+    uint64_t T = 1;
+    for (int d = 0; d < 5; ++d) {
+        if (a.src.dim[d] != a.dst.dim[d] || a.src.L[d] != a.dst.L[d] || a.src.es[d] != 1 || a.dst.es[d] != 1)
+            return TMAP_ERR_UNSUPPORTED;
+        const uint64_t bx = (uint64_t)a.src.box_m1[d] + 1u;
+        const uint64_t n = ((uint64_t)a.src.dim[d] + bx - 1) / bx;
+        a.nt[d] = (uint32_t)n;
+        even = even && ((uint64_t)a.src.dim[d] % bx == 0);
+        T *= n;
+    }
+    if (T == 0 || T > 0x7FFFFFFFull) return TMAP_ERR_UNSUPPORTED;
+    a.ntiles = (uint32_t)T;
+    uint32_t limit = 0, cus = 0;
+    tmap_status st = device_lds_limit(&limit);
+    if (st) return st;
+    st = device_cu_count(&cus);
+    if (st) return st;
+    const uint32_t B = a.src.box_bytes;
+    const uint32_t groups = B / 1024u;
+    const uint32_t gpw = (B % 1024u == 0) ? groups / kCopyWaves : 0u;
+    const bool ring_ok = even && variant != 2 && gpw * kCopyWaves == groups &&
+                         (gpw == 1 || gpw == 2 || gpw == 4 || gpw == 8) && stages * B <= limit;
+    hipStream_t s = as_stream(stream);
+    if (ring_ok) {
+        const uint32_t g = grid ? grid : auto_grid(a.ntiles, cus, stages * B);
+        if (variant == 1) return launch_ring_g<true>(a, gpw, stages, g, s);
+        return launch_ring_g<false>(a, gpw, stages, g, s);
+    }
+    const uint32_t lds = round_up(B, 1024u);
+    if (lds > limit) return TMAP_ERR_LDS_CAPACITY;
+    hipError_t e = hipFuncSetAttribute((const void*)k_tile_copy_generic, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+    hipLaunchKernelGGL(k_tile_copy_generic, dim3(a.ntiles), dim3(kCopyWaves * 64), lds, s, a);
+    return check_launch("tile_copy");
+}
+
+extern "C" tmap_status tile_copy(const tmap_t* src, const tmap_t* dst, uint32_t stages, void* stream) {
+    return tile_copy_ex(src, dst, stages, 0u, 0u, stream);
+}

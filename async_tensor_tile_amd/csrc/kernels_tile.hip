@@ -1,0 +1,226 @@
+// kernels_tile.hip -- batch load / store / reduce-add kernels, the
+// byte-counted barrier self-test and the LDS bank-sector probe, with their
+// C-ABI launchers.
+//
+// Batch kernels run one workgroup (4 waves) per box: the box goes through a
+// real LDS image, exactly as a single copy of [HPC] "single-tile load" /
+// "TMA store" / "TMA reduce" would, and the image is dumped or consumed.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "host_util.hpp"
+#include "tile_device.hpp"
+#include "tmap.h"
+
+namespace att {
+
+constexpr uint32_t kBatchThreads = 256;
+
+__device__ __forceinline__ void read_coords(const TmapImpl& m, const int32_t* __restrict__ coords,
+                                            uint32_t b, int32_t c[5]) {
+#pragma unroll
+    for (int d = 0; d < 5; ++d) c[d] = d < m.rank ? coords[(size_t)b * m.rank + d] : 0;
+}
+
+// Load box b into LDS with the byte-counted barrier, then dump the image.
+__global__ __launch_bounds__(kBatchThreads) void k_tile_load(TmapImpl m, const int32_t* __restrict__ coords,
+                                                            uint8_t* __restrict__ out, uint32_t bar_off) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    TxBar* bar = reinterpret_cast<TxBar*>(smem + bar_off);
+    const uint32_t b = blockIdx.x;
+    const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
+    int32_t c[5];
+    read_coords(m, coords, b, c);
+    if (tid == 0) {
+        txbar_init(bar, 1);
+        txbar_arrive_expect_tx(bar, (int32_t)m.box_bytes);   // expect before any copy is issued
+    }
+    __syncthreads();
+    const uint32_t bytes = tile_load_issue(m, c, smem, wave, nwaves);
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    if (lane_id() == 0 && bytes) txbar_complete_tx(bar, (int32_t)bytes);
+    txbar_wait(bar, 0);
+    const uint32_t nchunk = m.box_bytes >> 4;
+    uint8_t* dst = out + (size_t)b * m.box_bytes;
+    for (uint32_t i = tid; i < nchunk; i += blockDim.x)
+        *reinterpret_cast<u32x4*>(dst + i * 16u) = *reinterpret_cast<const u32x4*>(smem + i * 16u);
+}
+
+// Stage the raw image of box b into LDS, then store / reduce it through the map.
+template <bool REDUCE>
+__global__ __launch_bounds__(kBatchThreads) void k_tile_store(TmapImpl m, const int32_t* __restrict__ coords,
+                                                             const uint8_t* __restrict__ in) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    const uint32_t b = blockIdx.x;
+    const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
+    int32_t c[5];
+    read_coords(m, coords, b, c);
+    const uint32_t nchunk = m.box_bytes >> 4;
+    const uint8_t* src = in + (size_t)b * m.box_bytes;
+    for (uint32_t grp = wave; grp * 64u < nchunk; grp += nwaves) {
+        const uint32_t p = grp * 64u + lane_id();
+        if (p < nchunk) dma16(src + p * 16u, smem + grp * 1024u);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    tile_store_issue<REDUCE>(m, c, smem, wave, nwaves);
+}
+
+// Byte-counted barrier self-test: one barrier (arrival count 1) completes
+// after `ntile` copies signal their own byte counts.  Trace records are
+// (who, arrivals_left, pending, phase); who = -1 init, -2 arrive.expect_tx,
+// t >= 0 the complete-tx of tile t.
+__global__ __launch_bounds__(kBatchThreads) void k_txbar_selftest(TmapImpl m, const int32_t* __restrict__ coords,
+                                                                 uint32_t ntile, int32_t* __restrict__ trace,
+                                                                 uint8_t* __restrict__ out, uint32_t img_stride,
+                                                                 uint32_t bar_off) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    TxBar* bar = reinterpret_cast<TxBar*>(smem + bar_off);
+    uint32_t* counter = reinterpret_cast<uint32_t*>(smem + bar_off + sizeof(TxBar));
+    const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
+    if (tid == 0) {
+        txbar_init(bar, 1);
+        trace[0] = -1; trace[1] = bar->expected; trace[2] = 0; trace[3] = 0;
+        const TxState s = txbar_arrive_expect_tx(bar, (int32_t)(m.box_bytes * ntile));
+        trace[4] = -2; trace[5] = s.arrivals_left; trace[6] = s.pending; trace[7] = (int32_t)s.phase;
+        *counter = 0;
+    }
+    __syncthreads();
+    for (uint32_t t = wave; t < ntile; t += nwaves) {
+        int32_t c[5];
+        read_coords(m, coords, t, c);
+        const uint32_t bytes = tile_load_issue(m, c, smem + t * img_stride, 0, 1);
+        wait_vmcnt<0>();
+        wait_lgkm0();
+        if (lane_id() == 0) {
+            const TxState s = txbar_complete_tx(bar, (int32_t)bytes);
+            const uint32_t slot = 2u + atomicAdd(counter, 1u);
+            trace[slot * 4 + 0] = (int32_t)t;
+            trace[slot * 4 + 1] = s.arrivals_left;
+            trace[slot * 4 + 2] = s.pending;
+            trace[slot * 4 + 3] = (int32_t)s.phase;
+        }
+    }
+    txbar_wait(bar, 0);
+    for (uint32_t t = 0; t < ntile; ++t) {
+        const uint32_t nchunk = m.box_bytes >> 4;
+        for (uint32_t i = tid; i < nchunk; i += blockDim.x)
+            *reinterpret_cast<u32x4*>(out + (size_t)t * m.box_bytes + i * 16u) =
+                *reinterpret_cast<const u32x4*>(smem + t * img_stride + i * 16u);
+    }
+}
+
+// Physical LDS address (bytes) of the 16-byte sector (row r, column col) of
+// the 16 x 256-byte grid under the 128-byte swizzle.
+//   layout 1: grouped as a (group, row, col) box of 2 x 16 x 128 bytes.
+//   layout 0: kept at a 256-byte row stride (a reference layout only).
+__device__ __forceinline__ uint32_t probe_addr(int32_t layout, uint32_t r, uint32_t col) {
+    const uint32_t q = layout == 1 ? ((col >> 3) * 16u + r) * 8u + (col & 7u) : r * 16u + col;
+    return swz_chunk(q, TMAP_SWIZZLE_128B) * 16u;
+}
+
+__global__ __launch_bounds__(64) void k_lds_bank_probe(int32_t layout, uint32_t iters, int32_t* __restrict__ hist) {
+    __shared__ __attribute__((aligned(1024))) uint8_t grid[4096];
+    const uint32_t lane = threadIdx.x;
+    for (uint32_t i = lane; i < 256; i += 64) reinterpret_cast<u32x4*>(grid)[i] = u32x4{i, i, i, i};
+    __syncthreads();
+    uint32_t sink = 0;
+    for (uint32_t row0 = 0; row0 <= 8; ++row0) {
+        for (uint32_t col = 0; col < 16; ++col) {
+            const uint32_t a = probe_addr(layout, row0 + (lane & 7u), col);
+            const uint32_t sector = (a >> 4) & 7u;
+            if (lane < 8) {
+                const uint32_t la = lds_addr_of(grid) + a;
+                for (uint32_t it = 0; it < iters; ++it) {
+                    const u32x4 v = lds_read16(la);
+                    wait_lgkm0();
+                    sink ^= v.x;
+                }
+            }
+            for (uint32_t s = 0; s < 8; ++s) {
+                const uint64_t hit = __ballot(lane < 8 && sector == s);
+                if (lane == 0) hist[(row0 * 16 + col) * 8 + s] = (int32_t)__popcll(hit);
+            }
+        }
+    }
+    if (sink == 0xFFFFFFFFu) hist[0] = -1;   // keeps the timed reads alive
+}
+
+static tmap_status prepare_dynamic_lds(const void* fn, uint32_t bytes) {
+    uint32_t limit = 0;
+    tmap_status st = device_lds_limit(&limit);
+    if (st) return st;
+    if (bytes > limit) return TMAP_ERR_LDS_CAPACITY;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+    return TMAP_OK;
+}
+
+}  // namespace att
+
+using namespace att;
+
+extern "C" tmap_status tile_load(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
+                                 void* d_lds_image_out, void* stream) {
+    if (!m) return TMAP_ERR_NULL;
+    if (nbox == 0) return TMAP_OK;
+    if (!d_coords || !d_lds_image_out) return TMAP_ERR_NULL;
+    const TmapImpl t = load_map(m);
+    const uint32_t bar_off = round_up(t.box_bytes, 1024u);
+    const uint32_t lds = bar_off + 64u;
+    tmap_status st = prepare_dynamic_lds((const void*)k_tile_load, lds);
+    if (st) return st;
+    hipLaunchKernelGGL(k_tile_load, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), t, d_coords,
+                       static_cast<uint8_t*>(d_lds_image_out), bar_off);
+    return check_launch("tile_load");
+}
+
+template <bool REDUCE>
+static tmap_status launch_store(const tmap_t* m, const int32_t* d_coords, uint32_t nbox, const void* d_in,
+                                void* stream, const char* name) {
+    if (!m) return TMAP_ERR_NULL;
+    if (nbox == 0) return TMAP_OK;
+    if (!d_coords || !d_in) return TMAP_ERR_NULL;
+    const TmapImpl t = load_map(m);
+    const uint32_t lds = round_up(t.box_bytes, 1024u);
+    tmap_status st = prepare_dynamic_lds((const void*)k_tile_store<REDUCE>, lds);
+    if (st) return st;
+    hipLaunchKernelGGL(k_tile_store<REDUCE>, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), t,
+                       d_coords, static_cast<const uint8_t*>(d_in));
+    return check_launch(name);
+}
+
+extern "C" tmap_status tile_store(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
+                                  const void* d_lds_image_in, void* stream) {
+    return launch_store<false>(m, d_coords, nbox, d_lds_image_in, stream, "tile_store");
+}
+
+extern "C" tmap_status tile_reduce_add(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
+                                       const void* d_lds_image_in, void* stream) {
+    return launch_store<true>(m, d_coords, nbox, d_lds_image_in, stream, "tile_reduce_add");
+}
+
+extern "C" tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, uint32_t ntile,
+                                      int32_t* d_trace, void* d_lds_image_out, void* stream) {
+    if (!m || !d_coords || !d_trace || !d_lds_image_out) return TMAP_ERR_NULL;
+    if (ntile < 1 || ntile > 8) return TMAP_ERR_UNSUPPORTED;
+    const TmapImpl t = load_map(m);
+    if ((uint64_t)t.box_bytes * ntile > (1u << 30)) return TMAP_ERR_LDS_CAPACITY;
+    const uint32_t img_stride = round_up(t.box_bytes, 1024u);
+    const uint32_t bar_off = img_stride * ntile;
+    const uint32_t lds = bar_off + 64u;
+    tmap_status st = prepare_dynamic_lds((const void*)k_txbar_selftest, lds);
+    if (st) return st;
+    hipLaunchKernelGGL(k_txbar_selftest, dim3(1), dim3(kBatchThreads), lds, as_stream(stream), t, d_coords, ntile,
+                       d_trace, static_cast<uint8_t*>(d_lds_image_out), img_stride, bar_off);
+    return check_launch("txbar_selftest");
+}
+
+extern "C" tmap_status lds_bank_probe(int32_t layout, uint32_t iters, int32_t* d_hist, void* stream) {
+    if (!d_hist) return TMAP_ERR_NULL;
+    if (layout != 0 && layout != 1) return TMAP_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(k_lds_bank_probe, dim3(1), dim3(64), 0, as_stream(stream), layout, iters, d_hist);
+    return check_launch("lds_bank_probe");
+}

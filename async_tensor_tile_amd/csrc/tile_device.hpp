@@ -1,0 +1,376 @@
+// tile_device.hpp -- gfx950 device side of the tile mover.
+//
+// What the reference pages give to a dedicated copy engine (one thread hands
+// a descriptor plus box origin to hardware, [MLC] "one thread describes the
+// whole tile") is done here by the wavefront itself: every lane computes the
+// global address of one 16-byte chunk of the box and the wave issues
+// global_load_lds_dwordx4, which writes lane l's 16 bytes to LDS at
+// M0 + 16*l.  Because the LDS side of that instruction is lane-linear, the
+// swizzle-on-write ([MLC] "TMA writes swizzled layout") is realised on the
+// source side: the lane that fills physical chunk p fetches logical chunk
+// swz(p); the XOR swizzle is an involution, so the same function maps both
+// ways.  Completion is tracked per wave with s_waitcnt vmcnt; a byte-counted
+// LDS barrier (TxBar) gives the expect-tx / complete-tx accounting of [MLC]
+// "waiting for TMA load" when several waves share a box.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tmap_impl.hpp"
+
+namespace att {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Global-memory pointers carry address space 1 so that accesses compile to
+// global_* instructions rather than flat_* ones.
+#define ATT_GLOBAL __attribute__((address_space(1)))
+typedef ATT_GLOBAL uint8_t gbyte;
+
+__device__ __forceinline__ gbyte* gptr(uint64_t addr) { return (gbyte*)addr; }
+__device__ __forceinline__ gbyte* gptr(const void* p) { return (gbyte*)(uintptr_t)p; }
+
+// 16-byte out-of-bounds fill rows, indexed by TmapImpl::fill_idx.
+static __device__ __attribute__((aligned(16))) const uint32_t g_fill_rows[5][4] = {
+    {0u, 0u, 0u, 0u},
+    {0x7FC00000u, 0x7FC00000u, 0x7FC00000u, 0x7FC00000u},   // f32 quiet NaN
+    {0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u},   // f16 quiet NaN
+    {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u},   // bf16 quiet NaN
+    {0x00000000u, 0x7FF80000u, 0x00000000u, 0x7FF80000u},   // f64 quiet NaN
+};
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, uint32_t magic) {
+    return magic ? __umulhi(n, magic) : n;
+}
+
+// Physical <-> logical 16-byte chunk inside a box image.  Chunk bits 0..2
+// (position in a 128-byte unit) are XORed with bits 3..5 (the 128-byte unit
+// index), keeping `sw` of them: 3 for 128B, 2 for 64B, 1 for 32B, 0 for NONE.
+__device__ __forceinline__ uint32_t swz_chunk(uint32_t c, uint32_t sw) {
+    return c ^ ((c >> 3) & ((1u << sw) - 1u));
+}
+
+// Box coordinates of logical chunk q: k[0] is the first element's index in
+// dimension 0, k[1..4] the LDS row's coordinates.
+__device__ __forceinline__ void chunk_box_coords(const TmapImpl& m, uint32_t q, uint32_t k[5]) {
+    const uint32_t row = fdiv(q, m.magic_cpr);
+    const uint32_t j = q - row * m.cpr;
+    k[0] = j * (16u / m.esize);
+    const uint32_t r1 = fdiv(row, m.magic_L[0]);
+    k[1] = row - r1 * m.L[1];
+    const uint32_t r2 = fdiv(r1, m.magic_L[1]);
+    k[2] = r1 - r2 * m.L[2];
+    const uint32_t r3 = fdiv(r2, m.magic_L[2]);
+    k[3] = r2 - r3 * m.L[3];
+    k[4] = r3;
+}
+
+// Byte offset of the box element k (k[0] along dim 0) from the box origin's
+// address (origin given separately), and whether dims 1..4 are in range.
+struct ChunkLoc {
+    int64_t g0;        // global index of the chunk's first element in dim 0
+    int64_t rest_off;  // sum over dims >= 1 of g_i * stride_i (bytes)
+    bool rest_in;      // dims >= 1 inside the tensor
+};
+
+__device__ __forceinline__ ChunkLoc chunk_locate(const TmapImpl& m, const int32_t c[5], uint32_t q) {
+    uint32_t k[5];
+    chunk_box_coords(m, q, k);
+    ChunkLoc r;
+    r.g0 = (int64_t)c[0] + (int64_t)k[0] * m.es[0];
+    r.rest_off = 0;
+    r.rest_in = true;
+#pragma unroll
+    for (int d = 1; d < 5; ++d) {
+        const int64_t g = (int64_t)c[d] + (int64_t)k[d] * m.es[d];
+        r.rest_in = r.rest_in && (g >= 0) && (g < m.dim[d]);
+        r.rest_off += g * (int64_t)m.stride[d - 1];
+    }
+    return r;
+}
+
+// Gather one 16-byte chunk element by element (element stride in dim 0,
+// unaligned origin, or a chunk cut by the tensor edge).  Out-of-range
+// elements take the fill pattern and are never read.
+template <typename T>
+__device__ __forceinline__ u32x4 gather_chunk_t(const TmapImpl& m, const ChunkLoc& L) {
+    constexpr int N = 16 / (int)sizeof(T);
+    union { u32x4 v; T e[N]; } u;
+    const T fillv = *reinterpret_cast<const T*>(g_fill_rows[m.fill_idx]);
+    const ATT_GLOBAL T* row = (const ATT_GLOBAL T*)gptr(m.base + (uint64_t)L.rest_off);
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        const int64_t g = L.g0 + (int64_t)e * m.es[0];
+        const bool in = L.rest_in && g >= 0 && g < m.dim[0];
+        u.e[e] = in ? row[g] : fillv;
+    }
+    return u.v;
+}
+
+__device__ __forceinline__ u32x4 gather_chunk(const TmapImpl& m, const ChunkLoc& L) {
+    switch (m.esize) {
+    case 1: return gather_chunk_t<uint8_t>(m, L);
+    case 2: return gather_chunk_t<uint16_t>(m, L);
+    case 4: return gather_chunk_t<uint32_t>(m, L);
+    default: return gather_chunk_t<uint64_t>(m, L);
+    }
+}
+
+// One async 16-byte global->LDS copy per active lane; `lds_group` is the
+// wave-uniform LDS address of lane 0's slot.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_group) {
+    __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_group, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// ds_read_b128 issued as inline asm: the compiler's own LDS-DMA alias
+// tracking would otherwise put vmcnt(0) in front of every LDS read and
+// serialise the staging ring.  The caller waits lgkmcnt before use.
+__device__ __forceinline__ u32x4 lds_read16(uint32_t lds_addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(lds_addr) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+// Load one box into LDS image `lds` (this wave's share of the 64-chunk
+// groups grp = wave, wave + nwaves, ...).  Returns the bytes this wave wrote
+// to LDS; they have landed once the wave has waited vmcnt(0) and lgkmcnt(0).
+//
+// Fast path (dim-0 element stride 1 and a 16-byte-aligned dim-0 origin, so
+// every chunk is one aligned 16-byte global read): in-range chunks and
+// wholly out-of-range chunks (redirected to the fill row) go through
+// global_load_lds; chunks cut by the dim-0 edge are gathered per element and
+// written with ds_write_b128 by their lane, which sits out the DMA.
+__device__ __forceinline__ uint32_t tile_load_issue(const TmapImpl& m, const int32_t c[5], uint8_t* lds,
+                                                    uint32_t wave, uint32_t nwaves) {
+    const uint32_t lane = lane_id();
+    const uint32_t nchunk = m.box_bytes >> 4;
+    const bool fast = (m.es[0] == 1) && ((((int64_t)c[0] * m.esize) & 15) == 0);
+    const int64_t n_el = 16 / m.esize;
+    const void* fill = g_fill_rows[m.fill_idx];
+    uint32_t bytes = 0;
+    for (uint32_t grp = wave; grp * 64u < nchunk; grp += nwaves) {
+        const uint32_t p = grp * 64u + lane;
+        const bool active = p < nchunk;
+        const uint32_t rem = nchunk - grp * 64u;
+        bytes += 16u * (rem < 64u ? rem : 64u);
+        const uint32_t q = swz_chunk(p, m.swizzle);
+        const ChunkLoc L = chunk_locate(m, c, active ? q : 0u);
+        bool partial = !fast;
+        const void* src = fill;
+        if (fast) {
+            const bool full_in = L.rest_in && L.g0 >= 0 && L.g0 + n_el <= m.dim[0];
+            const bool full_out = !L.rest_in || L.g0 >= m.dim[0] || L.g0 + n_el <= 0;
+            partial = !full_in && !full_out;
+            if (full_in) src = (const void*)(uintptr_t)(m.base + (uint64_t)(L.g0 * m.esize + L.rest_off));
+        }
+        if (active && !partial) dma16(src, lds + grp * 1024u);
+        if (active && partial) {
+            const u32x4 v = gather_chunk(m, L);
+            *reinterpret_cast<u32x4*>(lds + p * 16u) = v;
+        }
+    }
+    return bytes;
+}
+
+// ---- reduce-add element helpers ------------------------------------------
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// 8- and 16-bit lanes of a 32-bit word updated with compare-and-swap.  The
+// aligned word never leaves the page that holds the element.
+template <typename F>
+__device__ __forceinline__ void cas_update_sub(gbyte* addr, int bits, F f) {
+    const uint64_t a = (uint64_t)(uintptr_t)addr;
+    ATT_GLOBAL uint32_t* w = (ATT_GLOBAL uint32_t*)(a & ~(uint64_t)3);
+    const uint32_t shift = (uint32_t)(a & 3u) * 8u;
+    const uint32_t mask = (bits == 8 ? 0xFFu : 0xFFFFu) << shift;
+    uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (true) {
+        const uint32_t cur = (old & mask) >> shift;
+        const uint32_t nw = (old & ~mask) | ((f(cur) << shift) & mask);
+        if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            break;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void atomic_add_g(gbyte* dst, T v) {
+    __hip_atomic_fetch_add((ATT_GLOBAL T*)dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void reduce_add_element(uint8_t dtype, gbyte* dst, const uint8_t* src) {
+    switch (dtype) {
+    case TMAP_U32: case TMAP_I32:
+        atomic_add_g<uint32_t>(dst, *reinterpret_cast<const uint32_t*>(src));
+        break;
+    case TMAP_U64: case TMAP_I64:
+        atomic_add_g<uint64_t>(dst, *reinterpret_cast<const uint64_t*>(src));
+        break;
+    case TMAP_F32:
+        atomic_add_g<float>(dst, *reinterpret_cast<const float*>(src));
+        break;
+    case TMAP_F64:
+        atomic_add_g<double>(dst, *reinterpret_cast<const double*>(src));
+        break;
+    case TMAP_U8: {
+        const uint32_t v = *src;
+        cas_update_sub(dst, 8, [v](uint32_t cur) { return (cur + v) & 0xFFu; });
+        break;
+    }
+    case TMAP_U16: {
+        const uint32_t v = *reinterpret_cast<const uint16_t*>(src);
+        cas_update_sub(dst, 16, [v](uint32_t cur) { return (cur + v) & 0xFFFFu; });
+        break;
+    }
+    case TMAP_BF16: {
+        const float v = bf16_to_f32(*reinterpret_cast<const uint16_t*>(src));
+        cas_update_sub(dst, 16, [v](uint32_t cur) {
+            return (uint32_t)f32_to_bf16_rne(bf16_to_f32((uint16_t)cur) + v);
+        });
+        break;
+    }
+    case TMAP_F16: {
+        const float v = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(src));
+        cas_update_sub(dst, 16, [v](uint32_t cur) {
+            const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)cur) + v;
+            return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
+        });
+        break;
+    }
+    default: break;
+    }
+}
+
+// Write one box from LDS image `lds` back through the map (inverse swizzle).
+// Lane l of group grp handles logical chunk grp*64 + l so that global writes
+// are in address order; it reads the chunk's physical LDS slot.  Elements
+// outside the tensor are skipped; REDUCE adds atomically instead of storing.
+template <bool REDUCE>
+__device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_t c[5], const uint8_t* lds,
+                                                 uint32_t wave, uint32_t nwaves) {
+    const uint32_t lane = lane_id();
+    const uint32_t nchunk = m.box_bytes >> 4;
+    const bool fast = (m.es[0] == 1) && ((((int64_t)c[0] * m.esize) & 15) == 0);
+    const int64_t n_el = 16 / m.esize;
+    for (uint32_t grp = wave; grp * 64u < nchunk; grp += nwaves) {
+        const uint32_t q = grp * 64u + lane;
+        if (q >= nchunk) continue;
+        const uint32_t p = swz_chunk(q, m.swizzle);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + p * 16u);
+        const ChunkLoc L = chunk_locate(m, c, q);
+        if (!L.rest_in) continue;
+        gbyte* rowp = gptr(m.base + (uint64_t)L.rest_off);
+        if (!REDUCE && fast && L.g0 >= 0 && L.g0 + n_el <= m.dim[0]) {
+            *(ATT_GLOBAL u32x4*)(rowp + L.g0 * m.esize) = v;
+            continue;
+        }
+        union { u32x4 v; uint8_t b[16]; } u;
+        u.v = v;
+        for (int64_t e = 0; e < n_el; ++e) {
+            const int64_t g = L.g0 + e * m.es[0];
+            if (g < 0 || g >= m.dim[0]) continue;
+            gbyte* dst = rowp + g * m.esize;
+            const uint8_t* src = u.b + e * m.esize;
+            if (REDUCE) {
+                reduce_add_element(m.dtype, dst, src);
+            } else {
+                switch (m.esize) {
+                case 1: *dst = *src; break;
+                case 2: *(ATT_GLOBAL uint16_t*)dst = *reinterpret_cast<const uint16_t*>(src); break;
+                case 4: *(ATT_GLOBAL uint32_t*)dst = *reinterpret_cast<const uint32_t*>(src); break;
+                default: *(ATT_GLOBAL uint64_t*)dst = *reinterpret_cast<const uint64_t*>(src); break;
+                }
+            }
+        }
+    }
+}
+
+// ---- byte-counted LDS barrier -----------------------------------------------
+// state = arrivals_left * 2^32 + pending_bytes (pending signed, |pending| <
+// 2^31), so one 64-bit LDS atomic applies an arrival and a byte count
+// together and "both zero" is state == 0.  The operation that brings the
+// state to zero re-arms the arrival count and flips the phase ([MLC]
+// "waiting for TMA load"; [HPC] async completion: a phase needs its arrivals
+// and its transaction bytes).
+struct TxBar {
+    int64_t state;
+    uint32_t phase;
+    int32_t expected;
+};
+
+struct TxState { int32_t arrivals_left; int32_t pending; uint32_t phase; };
+
+__device__ __forceinline__ void txbar_init(TxBar* b, int32_t count) {
+    b->state = (int64_t)count << 32;
+    b->phase = 0u;
+    b->expected = count;
+}
+
+// Applies (d_arrivals, d_bytes); returns the state right after this
+// operation (phase already flipped if it completed the phase).
+__device__ __forceinline__ TxState txbar_op(TxBar* b, int32_t d_arrivals, int32_t d_bytes) {
+    const int64_t delta = ((int64_t)d_arrivals << 32) + (int64_t)d_bytes;
+    const int64_t old = __hip_atomic_fetch_add(&b->state, delta, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int64_t now = old + delta;
+    TxState s;
+    if (now == 0) {
+        const int32_t exp = __hip_atomic_load(&b->expected, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&b->state, (int64_t)exp << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint32_t ph = __hip_atomic_fetch_xor(&b->phase, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        s.arrivals_left = exp;
+        s.pending = 0;
+        s.phase = ph ^ 1u;
+    } else {
+        s.pending = (int32_t)(uint32_t)(uint64_t)now;
+        s.arrivals_left = (int32_t)((now - (int64_t)s.pending) >> 32);
+        s.phase = __hip_atomic_load(&b->phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    return s;
+}
+
+__device__ __forceinline__ TxState txbar_expect_tx(TxBar* b, int32_t bytes) { return txbar_op(b, 0, bytes); }
+__device__ __forceinline__ TxState txbar_arrive(TxBar* b, int32_t count) { return txbar_op(b, -count, 0); }
+__device__ __forceinline__ TxState txbar_arrive_expect_tx(TxBar* b, int32_t bytes) { return txbar_op(b, -1, bytes); }
+__device__ __forceinline__ TxState txbar_complete_tx(TxBar* b, int32_t bytes) { return txbar_op(b, 0, -bytes); }
+
+__device__ __forceinline__ bool txbar_try_wait(TxBar* b, uint32_t parity) {
+    return __hip_atomic_load(&b->phase, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != (parity & 1u);
+}
+
+// Bounded wait: returns false if the phase did not complete within
+// `max_polls` polls (the caller's data is then not valid), so that a broken
+// accounting can never hang the GPU.
+__device__ __forceinline__ bool txbar_wait(TxBar* b, uint32_t parity, uint32_t max_polls = 1u << 22) {
+    for (uint32_t i = 0; i < max_polls; ++i) {
+        if (txbar_try_wait(b, parity)) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
+}  // namespace att

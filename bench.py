@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark: tiled box copy of a bf16 8192 x 8192 tensor through LDS.
+
+One step = one full-grid round trip (8192 boxes of 128 rows x 64 columns,
+128-byte swizzle, 2-stage LDS ring per wave): every box is loaded
+global -> LDS with the swizzle applied on write and stored LDS -> global
+through a second map.  Algorithmic bytes per step: 128 MiB read + 128 MiB
+written = 268,435,456 B.  Four source/destination pairs (1 GiB) rotate so
+the 256 MB last-level cache cannot serve the working set.
+
+Prints one JSON line (rank 0).  Secondary workloads (rank-5 load, reduce-add
+store, GEMM mainloop) are timed with --extra.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BYTES_PER_STEP = 2 * 8192 * 8192 * 2
+HBM_PEAK_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+COUNTERS_FILE = os.path.join(PROFILE_DIR, "tile_copy_bf16_8192_counters.json")
+KERNEL_SOURCES = ("async_tensor_tile_amd/csrc/kernel_copy.hip", "async_tensor_tile_amd/csrc/tile_device.hpp",
+                  "async_tensor_tile_amd/csrc/tmap_impl.hpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_counters():
+    """HBM traffic and LDS bank conflicts measured by rocprofv3 for this exact
+    kernel source; None once the kernel has changed since."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return c
+
+
+def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 8):
+    """The oracle (single-threaded C) doing the same round trip on the host:
+    every box loaded into an LDS image and stored back, full passes over the
+    8192-box grid until min_seconds have elapsed."""
+    import numpy as np
+
+    import oracle
+    import synthgen
+
+    src = synthgen.u16_bits(2, (8192, 8192))
+    dst = np.zeros_like(src)
+    m = oracle.Map("bf16", (8192, 8192), (16384,), (64, 128), swizzle="128b")
+    coords = np.array([[64 * (t % 128), 128 * (t // 128)] for t in range(8192)], dtype=np.int32)
+    passes, t0 = 0, time.perf_counter()
+    while passes < max_passes:
+        for b0 in range(0, 8192, 512):
+            img = m.load(src, coords[b0:b0 + 512])
+            m.store(dst, coords[b0:b0 + 512], img)
+        passes += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    ok = bool(np.array_equal(dst, src))
+    return {"value": round(passes * BYTES_PER_STEP / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "verified": ok,
+            "sample": f"{passes} full pass(es) of the 8192-box bf16 8192x8192 round trip "
+                      f"(load to LDS image + store), {dt:.1f} s on one host thread"}
+
+
+def run_extra(att, torch, stream, reps: int):
+    """Secondary workloads: rank-5 fp32 edge-crossing load, int32 reduce-add
+    pass, bf16 GEMM 8192^3.  Each timed with events on the launch stream."""
+    import numpy as np
+
+    import synthgen
+    from synthgen import workloads as W
+
+    out = {}
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(n):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n
+
+    # rank-5 fp32, 2048 boxes of 32 KiB, a quarter straddling edges (NaN fill)
+    ex = W.RANK5
+    dims, strides = ex["dims"], [1040, 134160, 4427280, 30990960]
+    vals = synthgen.uniform_f32(ex["seed"], strides[-1] * dims[-1] // 4)
+    sd = torch.from_numpy(vals.view(np.uint8)).cuda()
+    coords = synthgen.edge_mix_coords(ex["seed"] * 1000, dims, [32, 16, 8, 2, 1], ex["estride"], ex["nbox"])
+    cd = torch.from_numpy(coords).cuda()
+    img = torch.empty(ex["nbox"] * 32768, dtype=torch.uint8, device="cuda")
+    m = att.tmap_encode("f32", 5, sd.data_ptr(), dims, strides, ex["box"], ex["estride"], "128b", "nan")
+    ms = timed(lambda: att.tile_load(m, cd.data_ptr(), ex["nbox"], img.data_ptr(), stream), reps)
+    out["rank5_load_f32"] = {"ms": round(ms, 4), "GBps_lds_image_written": round(ex["nbox"] * 32768 / ms / 1e6, 1)}
+
+    # reduce-add int32: one pass of 1024 boxes of 64x64 into 4096^2
+    ex = W.REDUCE_4096
+    dst = torch.from_numpy(synthgen.int32_range(ex["seed"], (4096, 4096), -(1 << 20), 1 << 20)).cuda()
+    rc = torch.from_numpy(synthgen.uniform_coords(ex["seed"] * 1000 + 10, ex["nbox"], (0, 0), (4032, 4032))).cuda()
+    srcs = torch.from_numpy(synthgen.int32_range(ex["seed"] * 1000 + 20, (ex["nbox"], 64, 64), -(1 << 20), 1 << 20)).cuda()
+    mr = att.tmap_encode("i32", 2, dst.data_ptr(), ex["dims"], ex["strides"], ex["box"], None, "none")
+    ms = timed(lambda: att.tile_reduce_add(mr, rc.data_ptr(), ex["nbox"], srcs.data_ptr(), stream), reps)
+    out["reduce_add_i32_pass"] = {"ms": round(ms, 4),
+                                  "GBps_algorithmic": round(ex["nbox"] * 16384 * 3 / ms / 1e6, 1)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--stages", type=int, default=2)
+    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--pairs", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import async_tensor_tile_amd as att
+    import synthgen
+    from synthgen import workloads as W
+
+    att.lib()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream().cuda_stream
+    ex = W.COPY_8192
+    src_host = torch.from_numpy(synthgen.u16_bits(ex["seed"], (8192, 8192)).view(np.uint8).reshape(-1))
+    pairs = []
+    for p in range(args.pairs):
+        s = src_host.to("cuda")
+        d = torch.empty_like(s)
+        ms_ = att.tmap_encode("bf16", 2, s.data_ptr(), ex["dims"], ex["strides"], ex["box"], None, ex["swizzle"])
+        md_ = att.tmap_encode("bf16", 2, d.data_ptr(), ex["dims"], ex["strides"], ex["box"], None, ex["swizzle"])
+        pairs.append((s, d, ms_, md_))
+
+    def step(k):
+        _, _, ms_, md_ = pairs[k % len(pairs)]
+        att.tile_copy_ex(ms_, md_, args.stages, args.grid, args.variant, stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(args.steps):
+        step(k)
+    end.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    gbs = BYTES_PER_STEP / (ms_step / 1e3) / 1e9
+
+    verified = all(torch.equal(s, d) for s, d, _, _ in pairs)
+
+    ctr = committed_counters()
+    traffic = None
+    conflicts = None
+    if ctr:
+        traffic = ctr.get("hbm_bytes_per_launch")
+        conflicts = ctr.get("lds_bank_conflict_cycles_per_tile")
+
+    result = {
+        "metric": "tiled box copy GB/s (% of 8 TB/s HBM) bf16 8192^2, LDS bank conflicts/tile",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 8192x8192 tile round trip global->LDS->global, box 128x64, "
+                               "128B swizzle, 2-stage ring",
+                   "box": [64, 128], "tiles": 8192, "stages": args.stages, "variant": args.variant,
+                   "grid": args.grid or "auto", "buffer_pairs": args.pairs},
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "lds_bank_conflicts_per_tile": conflicts,
+        "verified_bit_exact": verified,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+    if args.extra:
+        result["extra"] = run_extra(att, torch, stream, 20)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,234 @@
+/*
+ * tmap.h -- C ABI of the MI355X (gfx950) descriptor-driven tile mover.
+ *
+ * A tensor map (tmap_t) describes how a tensor lies in device memory and
+ * which box a single copy moves; per-call box origins then drive
+ * global->LDS loads (with the swizzle applied on write), LDS->global stores
+ * and reduce-add stores.  Everything runs in hand-written HIP kernels for
+ * gfx950; this header exposes only plain pointers, sizes and integers.
+ *
+ * Reference pages cited below:
+ *   [MLC]  Modern GPU Programming for MLSys (zh), chapter "TMA".
+ *   [H200] blog.coolgpu.cn, "H200 // TMA" feature card.
+ *   [HPC]  gpu-hpc-book, chapter 08 "Cuda TMA".
+ *
+ * Conventions shared by every call
+ *   - Dimensions, strides, box extents and coordinates are listed innermost
+ *     (fastest varying) first, as on the pages ([H200] section 04 example 1).
+ *   - "d_" pointers are device (HBM) addresses; all other pointers are host
+ *     addresses read before the call returns.  The library never allocates
+ *     per call and never frees caller memory.
+ *   - Launch calls are asynchronous and ordered on `stream` (a hipStream_t;
+ *     NULL = the null stream).  No call synchronises implicitly.
+ *   - Errors are returned as tmap_status; nothing aborts or throws across the
+ *     ABI.  Launch-time failures return TMAP_ERR_HIP and keep the HIP error
+ *     text for tmap_last_error().
+ *   - Calls are reentrant; concurrent calls on different streams are safe as
+ *     long as their destination memory does not overlap.
+ */
+#ifndef ATT_TMAP_H
+#define ATT_TMAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- types ---------------------------------------------------------------- */
+
+/* Opaque 128-byte descriptor, 64-byte aligned, copyable by value.  Created on
+ * the host only ([H200] section 05: build the map on the host, rebase it with
+ * an address replacement rather than rebuilding it on the device). */
+typedef struct tmap_t {
+    uint8_t opaque[128];
+} __attribute__((aligned(64))) tmap_t;
+
+typedef enum {
+    TMAP_U8 = 0, TMAP_U16 = 1, TMAP_U32 = 2, TMAP_I32 = 3, TMAP_U64 = 4,
+    TMAP_I64 = 5, TMAP_F16 = 6, TMAP_BF16 = 7, TMAP_F32 = 8, TMAP_F64 = 9
+} tmap_dtype;
+
+/* XOR swizzle applied on the LDS byte offset relative to the box image:
+ * bits 4..(3+b) of the offset are XORed with bits 7..(6+b), b = 1, 2, 3 for
+ * the 32-, 64- and 128-byte spans.  With 128-byte rows the 128-byte mode puts
+ * logical 16-byte sector c of row r at physical sector c XOR (r % 8) ([MLC]
+ * "TMA writes swizzled layout"; atoms of 8 rows, [MLC] "3D TMA").  The pages
+ * only name the 32- and 64-byte modes; their bit pattern is this library's
+ * reading. */
+typedef enum {
+    TMAP_SWIZZLE_NONE = 0, TMAP_SWIZZLE_32B = 1, TMAP_SWIZZLE_64B = 2, TMAP_SWIZZLE_128B = 3
+} tmap_swizzle;
+
+/* Out-of-bounds fill for loads ([H200] section 02 table: zero or NaN).
+ * NAN writes the type's canonical quiet NaN (f32 0x7FC00000, f16 0x7E00,
+ * bf16 0x7FC0, f64 0x7FF8000000000000) and is accepted for float types only. */
+typedef enum { TMAP_OOB_ZERO = 0, TMAP_OOB_NAN = 1 } tmap_oob;
+
+typedef int32_t tmap_status;
+enum {
+    TMAP_OK = 0,
+    TMAP_ERR_NULL = 1,            /* a required pointer is NULL               */
+    TMAP_ERR_RANK = 2,            /* rank outside [1, 5]                      */
+    TMAP_ERR_DTYPE = 3,           /* unknown element type                     */
+    TMAP_ERR_ALIGN = 4,           /* base address not 16-byte aligned         */
+    TMAP_ERR_DIM = 5,             /* globalDim outside [1, 2^32]              */
+    TMAP_ERR_STRIDE = 6,          /* stride 0, not a multiple of 16, >= 2^40  */
+    TMAP_ERR_BOX = 7,             /* box outside [1, 256] or box[0]*esize%16  */
+    TMAP_ERR_ESTRIDE = 8,         /* element stride outside [1, 8], or the
+                                     LDS row ceil(box0/es0)*esize not a
+                                     multiple of 16 bytes                     */
+    TMAP_ERR_SWIZZLE_WIDTH = 9,   /* swizzled LDS row bytes != span           */
+    TMAP_ERR_OOB_FILL_DTYPE = 10, /* NaN fill requested for an integer type   */
+    TMAP_ERR_LDS_CAPACITY = 11,   /* box image larger than one workgroup's LDS*/
+    TMAP_ERR_UNSUPPORTED = 12,    /* enum value or shape this call cannot do  */
+    TMAP_ERR_HIP = 13             /* HIP runtime error; see tmap_last_error() */
+};
+
+/* Largest box image (bytes) a map may describe: the 160 KiB of LDS per CU
+ * less 1 KiB kept for the completion barrier beside the image. */
+#define TMAP_LDS_CAPACITY 162816u
+
+typedef struct {
+    int32_t  dtype;          /* tmap_dtype                                  */
+    int32_t  rank;
+    int32_t  esize;          /* bytes per element                           */
+    int32_t  swizzle;        /* tmap_swizzle                                */
+    int32_t  oob;            /* tmap_oob                                    */
+    uint32_t lds_extent[5];  /* ceil(box[i] / estride[i]); 1 beyond rank    */
+    uint32_t box_bytes;      /* esize * prod(lds_extent): expect_tx amount  */
+    uint32_t row_bytes;      /* lds_extent[0] * esize                       */
+    uint32_t atom_bytes;     /* 8 rows of the swizzle span, 0 for NONE      */
+    uint64_t base;           /* current global base address                 */
+} tmap_info_t;
+
+/* ---- host-only descriptor calls --------------------------------------------- */
+
+/* Encode and validate a tensor map ([H200] section 03 constraint table and
+ * section 04 example 1; [HPC] "Tensor descriptor" field list).
+ *   out            receives the descriptor (caller-owned storage).
+ *   dtype          tmap_dtype.
+ *   rank           1..5.
+ *   gaddr          device base address, 16-byte aligned.
+ *   gdim[rank]     globalDim, each in [1, 2^32].
+ *   gstride[rank-1] byte strides of dims 1..rank-1: multiples of 16, nonzero,
+ *                  below 2^40, in any order (may be NULL when rank == 1).
+ *   box[rank]      box extents, each in [1, 256]; box[0]*esize % 16 == 0.
+ *   estride[rank]  element strides in [1, 8] (NULL = all 1).  The box reads
+ *                  elements c + k*estride for k < ceil(box/estride); the LDS
+ *                  image is dense ([HPC] field list; this library's reading of
+ *                  a garbled passage).
+ *   swizzle        tmap_swizzle; when not NONE the LDS row
+ *                  ceil(box0/estride0)*esize must equal the span exactly
+ *                  ([MLC] "3D TMA" and "grouping requirement").
+ *   oob            tmap_oob.
+ * Validation order (first failure is reported): NULL, RANK, DTYPE,
+ * UNSUPPORTED (enums), NULL/ALIGN (base), DIM, STRIDE, BOX, ESTRIDE,
+ * SWIZZLE_WIDTH, OOB_FILL_DTYPE, LDS_CAPACITY.  On error *out is zeroed. */
+tmap_status tmap_encode(tmap_t* out, int32_t dtype, uint32_t rank, void* gaddr,
+                        const uint64_t* gdim, const uint64_t* gstride,
+                        const uint32_t* box, const uint32_t* estride,
+                        int32_t swizzle, int32_t oob);
+
+/* Point an encoded map at another base address of identical layout ([H200]
+ * sections 03 and 05: runtime rebasing).  Errors: NULL, ALIGN. */
+tmap_status tmap_replace_address(tmap_t* m, void* gaddr);
+
+/* Bytes one box occupies on chip: the amount a load expects ([MLC] "waiting
+ * for TMA load"); 0 for a NULL map. */
+uint32_t tmap_box_bytes(const tmap_t* m);
+
+/* Fill *info from an encoded map.  Errors: NULL. */
+tmap_status tmap_query(const tmap_t* m, tmap_info_t* info);
+
+/* Static text for a status code. */
+const char* tmap_strerror(tmap_status s);
+
+/* Text of the last TMAP_ERR_HIP on the calling thread ("" if none). */
+const char* tmap_last_error(void);
+
+/* ---- launches (asynchronous, stream-ordered) ------------------------------ */
+
+/* Load nbox boxes global->LDS and dump each box's raw LDS image.
+ * [MLC] "one thread describes the whole tile", "TMA writes swizzled layout";
+ * [HPC] single-tile load.  Box b starts at d_coords[b*rank .. b*rank+rank-1]
+ * (int32, any value: elements outside the tensor take the OOB fill).  The
+ * image of box b (physical LDS bytes, swizzle included) is written to
+ * d_lds_image_out + b * tmap_box_bytes(m).  Completion inside the kernel is
+ * byte-counted.  Errors: NULL, LDS_CAPACITY (image larger than the device's
+ * per-workgroup LDS), HIP.  nbox == 0 is a no-op. */
+tmap_status tile_load(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
+                      void* d_lds_image_out, void* stream);
+
+/* Store nbox boxes LDS->global ([HPC] "TMA store").  The raw LDS image of box
+ * b is read from d_lds_image_in + b * tmap_box_bytes(m), staged in LDS, and
+ * each element inside the tensor is written through the map (inverse
+ * swizzle); elements outside are skipped.  Boxes that overlap race (last
+ * writer unspecified).  Errors as tile_load. */
+tmap_status tile_store(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
+                       const void* d_lds_image_in, void* stream);
+
+/* Reduce-add store ([HPC] "TMA reduce"): like tile_store but every in-bounds
+ * element is added to global memory atomically.  Integer types wrap modulo
+ * 2^w; f32/f64 use IEEE addition (round to nearest even), f16/bf16 add in
+ * f32 and round once to nearest even.  Overlapping boxes are applied in an
+ * unspecified order (bit-exact for integers).  Errors as tile_load. */
+tmap_status tile_reduce_add(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
+                            const void* d_lds_image_in, void* stream);
+
+/* Full-grid round trip: every box of the grid covering `src` (origins at
+ * multiples of box[i]) is loaded global->LDS through `src` and stored
+ * LDS->global through `dst`, with `stages` LDS buffers per workgroup
+ * (producer/consumer ring, [MLC] "TMA in a pipeline").  src and dst must have
+ * the same dtype, rank, dims, box and swizzle, all element strides 1, and
+ * must not overlap.  stages in [1, 4].  Errors: NULL, UNSUPPORTED (geometry
+ * mismatch, stages, element strides), LDS_CAPACITY, HIP. */
+tmap_status tile_copy(const tmap_t* src, const tmap_t* dst, uint32_t stages, void* stream);
+
+/* Same as tile_copy with an explicit persistent grid size (0 = automatic)
+ * and launch variant (0 = default); for tuning sweeps. */
+tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32_t stages,
+                         uint32_t grid, uint32_t variant, void* stream);
+
+/* Byte-counted barrier self-test ([MLC] "waiting for TMA load": several tile
+ * copies complete one barrier phase by byte count).  One workgroup initialises a barrier
+ * with arrival count 1, performs arrive.expect_tx(sum of tile bytes), then
+ * loads `ntile` boxes of map `m` (origins d_coords) and lets each copy signal
+ * complete-tx with its own byte count as it lands.  After every barrier
+ * operation the state (arrivals_left, pending_bytes, phase) is appended to
+ * d_trace (int32 triples, 3 * (2 + ntile) entries: after init, after
+ * arrive.expect_tx, after each complete-tx, in completion order); the loaded
+ * images are written to d_lds_image_out.  ntile in [1, 8]; the images must
+ * fit LDS together.  Errors: NULL, UNSUPPORTED, LDS_CAPACITY, HIP. */
+tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, uint32_t ntile,
+                           int32_t* d_trace, void* d_lds_image_out, void* stream);
+
+/* LDS bank-sector probe ([MLC] "128-byte swizzle grouping requirement").
+ * For a 16 x 256-byte sector grid laid out in LDS either grouped (two
+ * 128-byte groups per row, a 3-D box, layout 1) or with a 256-byte row
+ * stride (layout 0), both under the 128-byte swizzle, eight lanes read one
+ * 16-byte column of eight consecutive rows with ds_read_b128 at the
+ * swizzled addresses the device address generator produces.  For row0 in
+ * 0..8 and col in 0..15 the kernel writes the hit count of each bank sector
+ * ((addr >> 4) & 7) to d_hist[(row0*16 + col)*8 + s], and repeats the reads
+ * `iters` times so hardware counters can be sampled.  Errors: NULL, HIP. */
+tmap_status lds_bank_probe(int32_t layout, uint32_t iters, int32_t* d_hist, void* stream);
+
+/* Consumer: bf16 GEMM mainloop C = A * B ([MLC] overview and "TMA in a
+ * pipeline"; [H200] section 02 result).  A is M x K row-major (map dims
+ * {K, M}), B is K x N column-major (map dims {K, N}), both bf16 with box
+ * {64, 256} and TMAP_SWIZZLE_128B; tiles are staged by the tile loader into a
+ * `stages`-deep LDS ring and consumed by MFMA bf16 with fp32 accumulation.
+ * d_C is M x N row-major bf16 (round to nearest even), leading dimension
+ * ldc >= N elements.  Ragged M, N, K are handled by the maps' zero fill and a
+ * masked epilogue.  stages in [2, 2] on gfx950 (two 64 KiB stages fill the
+ * 160 KiB LDS; three do not fit).  Errors: NULL, UNSUPPORTED (map shape,
+ * dtype, box, swizzle, stages), HIP. */
+tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
+                      uint32_t K, uint32_t ldc, uint32_t stages, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATT_TMAP_H */

@@ -1,0 +1,125 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every symbol that include/*.h declares, and its descriptor validator agrees
+with the oracle's on the constraint table of the reference pages."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import async_tensor_tile_amd as att
+import oracle
+import synthgen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(([^;{]*?)\)\s*;", text, flags=re.M):
+            names.append(m.group(1))
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "tmap_encode" in names and "tile_load" in names and "gemm_bf16" in names
+    L = ctypes.CDLL(att.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_invariant_division_exact():
+    assert att.lib().tmap_selftest_divide() == 0
+
+
+BASE = 0x7F0000000000   # a 16-byte aligned stand-in address; encode never dereferences it
+
+CASES = [
+    dict(),
+    dict(dims=(16,) * 6, strides=(32,) * 5, box=(16,) * 6, swizzle="none"),
+    dict(box=(64, 257)), dict(box=(64, 0)), dict(box=(4, 8), swizzle="none"),
+    dict(strides=(264,)), dict(strides=(1 << 40,)), dict(strides=((1 << 40) - 16,)), dict(strides=(0,)),
+    dict(base=BASE + 8), dict(box=(128, 8)), dict(box=(32, 8)), dict(box=(32, 8), swizzle="64b"),
+    dict(box=(16, 8), swizzle="32b"), dict(box=(256, 8), swizzle="none"),
+    dict(dtype="i32", box=(32, 8), fill="nan"), dict(dtype="f32", box=(32, 8), fill="nan"),
+    dict(estride=(1, 9)), dict(estride=(2, 1), box=(128, 8)), dict(estride=(3, 1), box=(128, 8), swizzle="none"),
+    dict(dims=(0, 64)), dict(dims=((1 << 32) + 1, 64)), dict(dims=((1 << 32), 64)),
+    dict(dims=(256, 256, 8), strides=(512, 131072), box=(64, 256, 8)),
+    dict(dims=(256, 256, 8), strides=(512, 131072), box=(64, 256, 5)),
+    dict(dims=(256, 256, 8), strides=(512, 131072), box=(64, 256, 4)),
+    dict(dtype="f32", dims=(32, 159, 8), strides=(128, 20352), box=(32, 159, 8)),
+    dict(dtype="f32", dims=(32, 160, 8), strides=(128, 20480), box=(32, 160, 8)),
+    dict(dtype="u8", box=(128, 8)), dict(dtype="f64", box=(16, 8), fill="nan"),
+]
+
+
+def _both(dtype="bf16", dims=(128, 64), strides=(256,), box=(64, 32), estride=None, swizzle="128b",
+          fill="zero", base=BASE):
+    om = oracle.Map(dtype, dims, strides, box, estride, swizzle, fill, base_addr=base)
+    want = om.validate()
+    try:
+        att.tmap_encode(dtype, len(dims), base, dims, strides, box, estride, swizzle, fill)
+        got = "OK"
+    except att.TmapError as e:
+        got = e.name
+    return got, want
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_encode_agrees_with_oracle_validator(case):
+    got, want = _both(**CASES[case])
+    assert got == want
+
+
+def test_encode_random_agreement():
+    g = synthgen.rng(99)
+    dts = list(att.DTYPE)
+    for _ in range(3000):
+        rank = int(g.integers(1, 6))
+        dtype = dts[int(g.integers(0, len(dts)))]
+        dims = [int(g.choice([0, 1, 7, 300, 1 << 32, (1 << 32) + 1])) if g.random() < 0.1
+                else int(g.integers(1, 5000)) for _ in range(rank)]
+        strides = [int(g.choice([0, 8, 16, 48, 1 << 40, (1 << 40) - 16, 4096])) for _ in range(rank - 1)]
+        box = [int(g.choice([0, 1, 2, 4, 8, 16, 32, 64, 128, 256, 257])) for _ in range(rank)]
+        es = [int(g.integers(0, 10)) for _ in range(rank)] if g.random() < 0.5 else None
+        sw = ["none", "32b", "64b", "128b"][int(g.integers(0, 4))]
+        fill = ["zero", "nan"][int(g.integers(0, 2))]
+        base = BASE + int(g.choice([0, 0, 0, 8]))
+        got, want = _both(dtype, dims, strides, box, es, sw, fill, base)
+        assert got == want, (dtype, dims, strides, box, es, sw, fill, base)
+
+
+def test_encode_query_and_replace():
+    m = att.tmap_encode("f32", 5, BASE, (260, 129, 33, 7, 3), (1040, 134160, 4427280, 30990960),
+                        (32, 32, 8, 2, 1), (1, 2, 1, 1, 1), "128b", "nan")
+    q = att.tmap_query(m)
+    assert q["lds_extent"] == [32, 16, 8, 2, 1]
+    assert q["box_bytes"] == 32768 == att.tmap_box_bytes(m)
+    assert q["row_bytes"] == 128 and q["atom_bytes"] == 1024 and q["esize"] == 4
+    assert q["base"] == BASE
+    att.tmap_replace_address(m, BASE + 4096)
+    assert att.tmap_query(m)["base"] == BASE + 4096
+    with pytest.raises(att.TmapError) as ei:
+        att.tmap_replace_address(m, BASE + 4)
+    assert ei.value.name == "ERR_ALIGN"
+    # the 4096-byte expectation of two 2048-byte operand tiles ([MLC] load wait)
+    a = att.tmap_encode("bf16", 2, BASE, (64, 64), (128,), (64, 16), None, "128b")
+    assert 2 * att.tmap_box_bytes(a) == 4096
+
+
+def test_launch_argument_errors_without_gpu():
+    m = att.tmap_encode("bf16", 2, BASE, (64, 64), (128,), (64, 16), None, "128b")
+    # nbox == 0 is a no-op and NULL pointers are rejected before any HIP call
+    att.tile_load(m, 0, 0, 0)
+    with pytest.raises(att.TmapError) as ei:
+        att.tile_load(m, 0, 3, 0)
+    assert ei.value.name == "ERR_NULL"
+    with pytest.raises(att.TmapError) as ei:
+        att.lds_bank_probe(0, 1, 0)
+    assert ei.value.name == "ERR_NULL"

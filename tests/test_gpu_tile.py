@@ -1,0 +1,255 @@
+"""GPU parity: the HIP tile loader / storer / reducer against the CPU oracle,
+element by element on the same seeded inputs (bit-exact for all moves and
+integer reductions).  Every call goes through the C ABI."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import async_tensor_tile_amd as att  # noqa: E402
+import oracle  # noqa: E402
+import synthgen  # noqa: E402
+from synthgen import workloads as W  # noqa: E402
+
+from cases import ESIZE, random_case, sweep_coords  # noqa: E402
+from gpu_util import empty_dev, encode, require_native, stream, to_dev, to_host  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    require_native()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_load(c, buf_dev, coords):
+    m = encode(buf_dev, c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, c.fill)
+    bb = att.tmap_box_bytes(m)
+    cd = to_dev(np.ascontiguousarray(coords, dtype=np.int32))
+    out = empty_dev(bb * len(coords), 0x5A)
+    att.tile_load(m, cd, len(coords), out, stream())
+    return to_host(out).reshape(len(coords), bb), m
+
+
+# ----------------------------- worked examples ------------------------------
+
+@pytest.mark.parametrize("mode", ["none", "128b"])
+def test_example_2d(mode, table):
+    """[MLC] 16x128 fp16 tensor, 8x64 box at (row 0, col 0) and (row 8, col 64)."""
+    ex = W.EXAMPLE_2D
+    src = synthgen.u16_bits(ex["seed"], (16, 128))
+    sd = to_dev(src)
+    m = encode(sd, "f16", ex["dims"], ex["strides"], ex["box"], swizzle=mode)
+    coords = np.array(ex["coords"], dtype=np.int32)
+    out = empty_dev(2 * 1024, 0)
+    att.tile_load(m, to_dev(coords), 2, out, stream())
+    got = to_host(out).reshape(2, 1024)
+    om = oracle.Map("f16", ex["dims"], ex["strides"], ex["box"], swizzle=mode)
+    np.testing.assert_array_equal(got, om.load(src, coords))
+    # the page's own table, independently of the oracle
+    for b, (c0, c1) in enumerate(coords):
+        img = got[b].view(np.uint16).reshape(8, 8, 8)
+        for rec in table("mlc_example_2d_sectors.txt"):
+            if rec[0] != mode:
+                continue
+            r = int(rec[1])
+            for p in range(8):
+                lg = int(rec[2 + p])
+                np.testing.assert_array_equal(img[r, p], src[c1 + r, c0 + 8 * lg: c0 + 8 * lg + 8])
+    # round trip LDS -> global into a sentinel buffer
+    dst = to_dev(np.full((16, 128), 0xDEAD, dtype=np.uint16))
+    md = encode(dst, "f16", ex["dims"], ex["strides"], ex["box"], swizzle=mode)
+    att.tile_store(md, to_dev(coords), 2, out, stream())
+    want = np.full((16, 128), 0xDEAD, dtype=np.uint16)
+    om.store(want, coords, got)
+    np.testing.assert_array_equal(to_host(dst).view(np.uint16).reshape(16, 128), want)
+
+
+def test_example_3d_four_atoms(table):
+    """[MLC] (group=2, row=16, col=64) view of a 16x256 fp16 matrix."""
+    ex = W.EXAMPLE_3D
+    src = synthgen.u16_bits(ex["seed"], (16, 256))
+    sd = to_dev(src)
+    m = encode(sd, "f16", ex["dims"], ex["strides"], ex["box"], swizzle="128b")
+    coords = np.array(ex["coords"], dtype=np.int32)
+    out = empty_dev(2 * 4096, 0)
+    att.tile_load(m, to_dev(coords), 2, out, stream())
+    got = to_host(out).reshape(2, 4096)
+    om = oracle.Map("f16", ex["dims"], ex["strides"], ex["box"], swizzle="128b")
+    np.testing.assert_array_equal(got, om.load(src, coords))
+    for rec in table("mlc_example_3d_atoms.txt"):
+        off, grp, row, p, grow, gcol = map(int, rec)
+        img = got[off // 128]
+        lds = grp * 2048 + row * 128 + p * 16
+        np.testing.assert_array_equal(img[lds:lds + 16].view(np.uint16), src[grow, gcol:gcol + 8])
+
+
+def test_bank_sector_probe(table):
+    """[MLC] grouping requirement: sector histograms of the device's
+    swizzled addresses, grouped and 256-byte-stride layouts."""
+    for layout in (0, 1):
+        h = empty_dev(9 * 16 * 8 * 4, 0)
+        att.lds_bank_probe(layout, 4, h, stream())
+        got = to_host(h).view(np.int32).reshape(9, 16, 8)
+        for row0 in range(9):
+            for col in range(16):
+                want = oracle.bank_sector_hist(layout == 1, row0, col)
+                assert got[row0, col].tolist() == want, (layout, row0, col)
+
+
+def test_txbar_4096_bytes(table):
+    """[MLC] waiting for a TMA load: two 2048-byte tiles complete one phase
+    with expect_tx(4096); states replayed on the oracle barrier model."""
+    src = synthgen.u16_bits(7, (64, 64))
+    sd = to_dev(src)
+    m = encode(sd, "bf16", (64, 64), (128,), (64, 16), swizzle="128b")
+    assert att.tmap_box_bytes(m) == 2048
+    coords = np.array([[0, 0], [0, 16]], dtype=np.int32)
+    trace = empty_dev(4 * 4 * 4, 0xFF)
+    out = empty_dev(2 * 2048, 0)
+    att.txbar_selftest(m, to_dev(coords), 2, trace, out, stream())
+    tr = to_host(trace).view(np.int32).reshape(4, 4)
+    ob = oracle.Txbar(1)
+    assert tuple(tr[0]) == (-1,) + ob.state()
+    ob.arrive_expect_tx(4096)
+    assert tuple(tr[1]) == (-2,) + ob.state() == (-2, 0, 4096, 0)
+    seen = set()
+    for rec in tr[2:]:
+        t = int(rec[0])
+        assert t in (0, 1) and t not in seen
+        seen.add(t)
+        ob.complete_tx(2048)
+        assert tuple(int(x) for x in rec[1:]) == ob.state()
+    assert ob.try_wait(0) and tuple(tr[3, 1:]) == (1, 0, 1)
+    om = oracle.Map("bf16", (64, 64), (128,), (64, 16), swizzle="128b")
+    np.testing.assert_array_equal(to_host(out).reshape(2, 2048), om.load(src, coords))
+
+
+@pytest.mark.parametrize("ntile", [1, 3, 8])
+def test_txbar_several_tiles(ntile):
+    src = synthgen.u16_bits(8, (128, 64))
+    sd = to_dev(src)
+    m = encode(sd, "bf16", (64, 128), (128,), (64, 16), swizzle="128b")
+    coords = np.array([[0, 16 * t] for t in range(ntile)], dtype=np.int32)
+    trace = empty_dev(4 * 4 * (2 + ntile), 0xFF)
+    out = empty_dev(ntile * 2048, 0)
+    att.txbar_selftest(m, to_dev(coords), ntile, trace, out, stream())
+    tr = to_host(trace).view(np.int32).reshape(2 + ntile, 4)
+    ob = oracle.Txbar(1)
+    ob.arrive_expect_tx(2048 * ntile)
+    for rec in tr[2:]:
+        ob.complete_tx(2048)
+        assert tuple(int(x) for x in rec[1:]) == ob.state()
+    assert sorted(tr[2:, 0].tolist()) == list(range(ntile))
+    om = oracle.Map("bf16", (64, 128), (128,), (64, 16), swizzle="128b")
+    np.testing.assert_array_equal(to_host(out).reshape(ntile, 2048), om.load(src, coords))
+
+
+# --------------------------- brute force, tiny ------------------------------
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_maps_load_store_reduce(seed):
+    """Ranks 1-5, all element types, all swizzles, element strides 1-3,
+    origins sweeping from below to above every dimension."""
+    g = synthgen.rng(20000 + seed)
+    c = random_case(g)
+    coords = sweep_coords(g, c, 24)
+    say("case", seed, c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, c.fill)
+    om = oracle.Map(c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, c.fill)
+    assert om.validate() == "OK"
+    sd = to_dev(c.buf)
+    got, m = gpu_load(c, sd, coords)
+    want = om.load(c.buf, coords)
+    np.testing.assert_array_equal(got, want)
+    # store the loaded images into a sentinel buffer: overlapping boxes write
+    # identical values, so the result is unique
+    dst = to_dev(np.full(c.buf.size, 0xA5, dtype=np.uint8))
+    md = encode(dst, c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, c.fill)
+    att.tile_store(md, to_dev(coords), len(coords), to_dev(got), stream())
+    hw = np.full(c.buf.size, 0xA5, dtype=np.uint8)
+    om.store(hw, coords, want)
+    np.testing.assert_array_equal(to_host(dst), hw)
+    # reduce-add of random images (integer types: order-free, bit-exact)
+    if c.dtype not in ("f16", "bf16", "f32", "f64"):
+        imgs = synthgen.random_bytes(seed + 7, got.size).reshape(got.shape)
+        acc = to_dev(c.buf)
+        ma = encode(acc, c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, "zero")
+        att.tile_reduce_add(ma, to_dev(coords), len(coords), to_dev(imgs), stream())
+        hw = c.buf.copy()
+        oracle.Map(c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle).reduce_add(hw, coords, imgs)
+        np.testing.assert_array_equal(to_host(acc)[: c.buf.size], hw)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32", "f64"])
+def test_float_reduce_single_contribution_exact(dtype):
+    """Non-overlapping boxes: one IEEE addition per element, rounded once;
+    bit-exact against the oracle."""
+    es = ESIZE[dtype]
+    L0 = 64 // es
+    dims, strides, box = (4 * L0, 24), (4 * L0 * es + 32,), (L0, 8)
+    foot = strides[0] * dims[1]
+    g = synthgen.rng(31)
+    if dtype == "bf16":
+        dst0 = synthgen.normal_bf16_bits(32, foot // 2).view(np.uint8)
+        imgs = synthgen.normal_bf16_bits(33, (12, L0 * 8)).view(np.uint8)
+    else:
+        npt = {"f16": np.float16, "f32": np.float32, "f64": np.float64}[dtype]
+        dst0 = g.standard_normal(foot // es).astype(npt).view(np.uint8)
+        imgs = (g.standard_normal((12, L0 * 8)) * 4).astype(npt).view(np.uint8)
+    coords = np.array([[L0 * (i % 4), 8 * (i // 4)] for i in range(12)], dtype=np.int32)
+    acc = to_dev(dst0)
+    m = encode(acc, dtype, dims, strides, box)
+    att.tile_reduce_add(m, to_dev(coords), 12, to_dev(imgs), stream())
+    hw = dst0.copy()
+    oracle.Map(dtype, dims, strides, box).reduce_add(hw, coords, imgs)
+    np.testing.assert_array_equal(to_host(acc), hw)
+
+
+# ------------------------------- edge cases ---------------------------------
+
+def test_empty_and_fully_outside():
+    src = synthgen.u16_bits(3, (32, 64))
+    sd = to_dev(src)
+    m = encode(sd, "bf16", (64, 32), (128,), (64, 8), swizzle="128b", fill="nan")
+    att.tile_load(m, 0, 0, 0, stream())        # nbox == 0: no launch
+    coords = np.array([[-64, 0], [64, 0], [0, -8], [0, 32], [-1000, -1000]], dtype=np.int32)
+    out = empty_dev(5 * 1024, 0)
+    att.tile_load(m, to_dev(coords), 5, out, stream())
+    got = to_host(out).view(np.uint16)
+    assert (got == 0x7FC0).all()
+    dst = to_dev(src)
+    att.tile_store(encode(dst, "bf16", (64, 32), (128,), (64, 8), swizzle="128b"), to_dev(coords), 5,
+                   to_dev(np.zeros(5 * 1024, np.uint8)), stream())
+    np.testing.assert_array_equal(to_host(dst).view(np.uint16).reshape(32, 64), src)
+
+
+def test_maximum_box():
+    """Largest box a map may describe (162816 bytes: 32 x 159 x 8 fp32)."""
+    dims, strides, box = (32, 159, 9), (128, 128 * 159), (32, 159, 8)
+    src = synthgen.uniform_f32(5, (9, 159, 32))
+    om = oracle.Map("f32", dims, strides, box, swizzle="128b")
+    assert om.validate() == "OK" and om.box_bytes() == 162816
+    sd = to_dev(src)
+    m = encode(sd, "f32", dims, strides, box, swizzle="128b")
+    coords = np.array([[0, 0, 0], [0, 0, 1], [3, -5, 2]], dtype=np.int32)
+    out = empty_dev(3 * 162816, 0)
+    att.tile_load(m, to_dev(coords), 3, out, stream())
+    np.testing.assert_array_equal(to_host(out).reshape(3, -1), om.load(src, coords))
+
+
+def test_rank1_and_u8_extremes():
+    buf = synthgen.random_bytes(9, 1000 + 16)
+    for box in (16, 256):
+        c = np.array([[-300], [-17], [0], [1], [15], [500], [999], [1000]], dtype=np.int32)
+        om = oracle.Map("u8", (1000,), (), (box,))
+        sd = to_dev(buf)
+        m = encode(sd, "u8", (1000,), (), (box,))
+        out = empty_dev(len(c) * box, 0)
+        att.tile_load(m, to_dev(c), len(c), out, stream())
+        np.testing.assert_array_equal(to_host(out).reshape(len(c), box), om.load(buf, c))

@@ -321,7 +321,10 @@ def _map(**kw):
     (dict(dims=((1 << 32) + 1, 64)), "ERR_DIM"),
     # LDS capacity
     (dict(dims=(256, 256, 8), strides=(512, 131072), box=(64, 256, 8)), "ERR_LDS_CAPACITY"),
-    (dict(dims=(256, 256, 8), strides=(512, 131072), box=(64, 256, 5)), "OK"),
+    (dict(dims=(256, 256, 8), strides=(512, 131072), box=(64, 256, 5)), "ERR_LDS_CAPACITY"),
+    (dict(dims=(256, 256, 8), strides=(512, 131072), box=(64, 256, 4)), "OK"),
+    (dict(dtype="f32", dims=(32, 159, 8), strides=(128, 20352), box=(32, 159, 8)), "OK"),
+    (dict(dtype="f32", dims=(32, 160, 8), strides=(128, 20480), box=(32, 160, 8)), "ERR_LDS_CAPACITY"),
     (dict(dtype="u8", box=(128, 8)), "OK"),
 ])
 def test_validate_constraint_table(kw, want):
