@@ -91,9 +91,10 @@ def lib():
         L.txbar_selftest.argtypes = [tp, _V, _U32, _V, _V, _V]
         L.lds_bank_probe.argtypes = [_I32, _U32, _V, _V]
         L.gemm_bf16.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
+        L.gemm_bf16_ex.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _V]
         for name in ("tmap_encode", "tmap_replace_address", "tmap_query", "tile_load", "tile_store",
                      "tile_reduce_add", "tile_copy", "tile_copy_ex", "txbar_selftest",
-                     "lds_bank_probe", "gemm_bf16"):
+                     "lds_bank_probe", "gemm_bf16", "gemm_bf16_ex"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -195,3 +196,9 @@ def gemm_bf16(A: tmap_t, B: tmap_t, d_C, M: int, N: int, K: int, ldc: int, stage
               stream=0) -> None:
     _check(lib().gemm_bf16(ctypes.byref(A), ctypes.byref(B), _addr(d_C), int(M), int(N), int(K),
                            int(ldc), int(stages), _addr(stream)), "gemm_bf16")
+
+
+def gemm_bf16_ex(A: tmap_t, B: tmap_t, d_C, M: int, N: int, K: int, ldc: int, stages: int = 2,
+                 group_m: int = 0, xcd: int = 1, stream=0) -> None:
+    _check(lib().gemm_bf16_ex(ctypes.byref(A), ctypes.byref(B), _addr(d_C), int(M), int(N), int(K),
+                              int(ldc), int(stages), int(group_m), int(xcd), _addr(stream)), "gemm_bf16_ex")

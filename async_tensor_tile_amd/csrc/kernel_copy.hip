@@ -25,7 +25,14 @@ struct CopyArgs {
     TmapImpl dst;
     uint32_t ntiles;
     uint32_t nt[5];     // tiles per dimension
+    uint32_t chunked;   // 1: workgroup b owns tiles [b*per, b*per + per); 0: tiles b + n*grid
+    uint32_t xcd;       // 1: renumber workgroups so each XCD owns one contiguous range
 };
+
+// Copy variant flags (tile_copy_ex `variant`).
+// Bits 4..5 select how many consecutive boxes share one ring stage (1, 2, 4, 8).
+enum : uint32_t { CV_NT_STORE = 1u, CV_GENERIC = 2u, CV_CHUNKED = 4u, CV_XCD = 8u, CV_NB_SHIFT = 4u };
+constexpr uint32_t kNumXcd = 8;
 
 constexpr uint32_t kCopyWaves = 4;
 
@@ -76,26 +83,19 @@ __device__ __forceinline__ void lds_read_group<8>(const uint32_t (&a)[8], u32x4 
                    "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]) : "memory");
 }
 
-// Wait until at most `pending_groups` of this wave's DMA instructions are in
-// flight.  Loads complete in issue order, so this retires every load issued
-// before the last `pending_groups` of them.
-template <int GPW, int S>
-__device__ __forceinline__ void wait_stage(uint32_t later_stages) {
-    if constexpr (S >= 4) { if (later_stages >= 3) { wait_vmcnt<3 * GPW>(); return; } }
-    if constexpr (S >= 3) { if (later_stages >= 2) { wait_vmcnt<2 * GPW>(); return; } }
-    if constexpr (S >= 2) { if (later_stages >= 1) { wait_vmcnt<GPW>(); return; } }
-    wait_vmcnt<0>();
-}
-
-template <int GPW, int S, bool NT>
-__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a) {
+// One stage holds NB consecutive boxes (each its own dense LDS image).  The
+// wave issues its DMA instructions row-group major, box minor, so that
+// back-to-back requests cover NB neighbouring 128-byte segments of the same
+// rows: with 128-byte-wide boxes that is what keeps HBM pages busy.
+template <int GPW, int S, int NB>
+__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a, uint32_t nt_store) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t lane = lane_id();
     const uint32_t B = a.src.box_bytes;
     const uint32_t sw = a.src.swizzle;
 
-    // Per-lane constants, identical for every tile: where the chunk this lane
+    // Per-lane constants, identical for every box: where the chunk this lane
     // loads comes from, where the chunk it stores goes, and which LDS slot
     // holds the latter.
     uint64_t ld_off[GPW], st_off[GPW];
@@ -113,20 +113,33 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a) 
         rd[j] = lds0 + swz_chunk(p, sw) * 16u;
     }
 
-    const uint32_t T = a.ntiles;
-    const uint32_t first = blockIdx.x;
-    if (first >= T) return;
-    const uint32_t nmine = (T - 1 - first) / gridDim.x + 1;
+    // Units of NB boxes.  Workgroups are dispatched round-robin over the
+    // XCDs; with `xcd` the ones sharing an XCD get neighbouring unit ranges.
+    const uint32_t U = a.ntiles / NB;
+    const uint32_t G = gridDim.x;
+    const uint32_t b = a.xcd ? (blockIdx.x % kNumXcd) * (G / kNumXcd) + blockIdx.x / kNumXcd : blockIdx.x;
+    const uint32_t per = (U + G - 1) / G;
+    const uint32_t first = a.chunked ? b * per : b;
+    const uint32_t step = a.chunked ? 1u : G;
+    if (first >= U) return;
+    const uint32_t nmine = a.chunked ? (U - first < per ? U - first : per) : (U - 1 - first) / G + 1;
 
     auto issue = [&](uint32_t n) {
-        uint64_t so, dof;
-        int32_t c[5];
-        tile_origin(a, first + n * gridDim.x, so, dof, c);
-        uint8_t* stage = smem + (n % S) * B;
-        const uint64_t sb = a.src.base + so;
+        const uint32_t t0 = (first + n * step) * NB;
+        uint8_t* stage = smem + (n % S) * (NB * B);
+        uint64_t sb[NB];
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+            uint64_t so, dof;
+            int32_t c[5];
+            tile_origin(a, t0 + x, so, dof, c);
+            sb[x] = a.src.base + so;
+        }
 #pragma unroll
         for (int j = 0; j < GPW; ++j)
-            dma16((const void*)(uintptr_t)(sb + ld_off[j]), stage + (wave * GPW + j) * 1024u);
+#pragma unroll
+            for (int x = 0; x < NB; ++x)
+                dma16((const void*)(uintptr_t)(sb[x] + ld_off[j]), stage + x * B + (wave * GPW + j) * 1024u);
     };
 
 #pragma unroll
@@ -136,22 +149,26 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a) 
     for (uint32_t n = 0; n < nmine; ++n) {
         if (n + S - 1 < nmine) issue(n + S - 1);
         const uint32_t left = nmine - 1 - n;
-        wait_stage<GPW, S>(left < (uint32_t)(S - 1) ? left : (uint32_t)(S - 1));
-        uint32_t addr[GPW];
-        const uint32_t soff = (n % S) * B;
+        wait_stage<GPW * NB, S - 1>(left < (uint32_t)(S - 1) ? left : (uint32_t)(S - 1));
+        const uint32_t t0 = (first + n * step) * NB;
 #pragma unroll
-        for (int j = 0; j < GPW; ++j) addr[j] = rd[j] + soff;
-        u32x4 v[GPW];
-        lds_read_group<GPW>(addr, v);
-        uint64_t so, dof;
-        int32_t c[5];
-        tile_origin(a, first + n * gridDim.x, so, dof, c);
-        gbyte* db = gptr(a.dst.base + dof);
+        for (int x = 0; x < NB; ++x) {
+            uint32_t addr[GPW];
+            const uint32_t soff = (n % S) * (NB * B) + x * B;
 #pragma unroll
-        for (int j = 0; j < GPW; ++j) {
-            ATT_GLOBAL u32x4* p = (ATT_GLOBAL u32x4*)(db + st_off[j]);
-            if constexpr (NT) __builtin_nontemporal_store(v[j], p);
-            else *p = v[j];
+            for (int j = 0; j < GPW; ++j) addr[j] = rd[j] + soff;
+            u32x4 v[GPW];
+            lds_read_group<GPW>(addr, v);
+            uint64_t so, dof;
+            int32_t c[5];
+            tile_origin(a, t0 + x, so, dof, c);
+            gbyte* db = gptr(a.dst.base + dof);
+#pragma unroll
+            for (int j = 0; j < GPW; ++j) {
+                ATT_GLOBAL u32x4* p = (ATT_GLOBAL u32x4*)(db + st_off[j]);
+                if (nt_store) __builtin_nontemporal_store(v[j], p);
+                else *p = v[j];
+            }
         }
     }
 }
@@ -170,33 +187,51 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_generic(CopyArgs 
     tile_store_issue<false>(a.dst, c, smem, wave, nwaves);
 }
 
-template <int GPW, int S, bool NT>
-static tmap_status launch_ring(const CopyArgs& a, uint32_t grid, hipStream_t st) {
-    const uint32_t lds = (uint32_t)S * a.src.box_bytes;
-    hipError_t e = hipFuncSetAttribute((const void*)k_tile_copy_ring<GPW, S, NT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-    hipLaunchKernelGGL((k_tile_copy_ring<GPW, S, NT>), dim3(grid), dim3(kCopyWaves * 64), lds, st, a);
-    return check_launch("tile_copy");
-}
-
-template <int GPW, bool NT>
-static tmap_status launch_ring_s(const CopyArgs& a, uint32_t stages, uint32_t grid, hipStream_t st) {
-    switch (stages) {
-    case 1: return launch_ring<GPW, 1, NT>(a, grid, st);
-    case 2: return launch_ring<GPW, 2, NT>(a, grid, st);
-    case 3: return launch_ring<GPW, 3, NT>(a, grid, st);
-    default: return launch_ring<GPW, 4, NT>(a, grid, st);
+template <int GPW, int S, int NB>
+static tmap_status launch_ring(const CopyArgs& a, uint32_t grid, uint32_t nt, hipStream_t st) {
+    if constexpr (GPW * NB * (S - 1) > 63) {
+        return TMAP_ERR_UNSUPPORTED;       // more DMA instructions in flight than vmcnt counts
+    } else {
+        const uint32_t lds = (uint32_t)S * NB * a.src.box_bytes;
+        hipError_t e = hipFuncSetAttribute((const void*)k_tile_copy_ring<GPW, S, NB>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+        hipLaunchKernelGGL((k_tile_copy_ring<GPW, S, NB>), dim3(grid), dim3(kCopyWaves * 64), lds, st, a, nt);
+        return check_launch("tile_copy");
     }
 }
 
-template <bool NT>
-static tmap_status launch_ring_g(const CopyArgs& a, uint32_t gpw, uint32_t stages, uint32_t grid, hipStream_t st) {
+template <int GPW, int NB>
+static tmap_status launch_ring_s(const CopyArgs& a, uint32_t stages, uint32_t grid, uint32_t nt, hipStream_t st) {
+    switch (stages) {
+    case 1: return launch_ring<GPW, 1, NB>(a, grid, nt, st);
+    case 2: return launch_ring<GPW, 2, NB>(a, grid, nt, st);
+    case 3: return launch_ring<GPW, 3, NB>(a, grid, nt, st);
+    case 4: return launch_ring<GPW, 4, NB>(a, grid, nt, st);
+    case 6: return launch_ring<GPW, 6, NB>(a, grid, nt, st);
+    case 8: return launch_ring<GPW, 8, NB>(a, grid, nt, st);
+    default: return TMAP_ERR_UNSUPPORTED;
+    }
+}
+
+template <int GPW>
+static tmap_status launch_ring_nb(const CopyArgs& a, uint32_t nb, uint32_t stages, uint32_t grid, uint32_t nt,
+                                  hipStream_t st) {
+    switch (nb) {
+    case 1: return launch_ring_s<GPW, 1>(a, stages, grid, nt, st);
+    case 2: return launch_ring_s<GPW, 2>(a, stages, grid, nt, st);
+    case 4: return launch_ring_s<GPW, 4>(a, stages, grid, nt, st);
+    default: return launch_ring_s<GPW, 8>(a, stages, grid, nt, st);
+    }
+}
+
+static tmap_status launch_ring_g(const CopyArgs& a, uint32_t gpw, uint32_t nb, uint32_t stages, uint32_t grid,
+                                 uint32_t nt, hipStream_t st) {
     switch (gpw) {
-    case 1: return launch_ring_s<1, NT>(a, stages, grid, st);
-    case 2: return launch_ring_s<2, NT>(a, stages, grid, st);
-    case 4: return launch_ring_s<4, NT>(a, stages, grid, st);
-    default: return launch_ring_s<8, NT>(a, stages, grid, st);
+    case 1: return launch_ring_nb<1>(a, nb, stages, grid, nt, st);
+    case 2: return launch_ring_nb<2>(a, nb, stages, grid, nt, st);
+    case 4: return launch_ring_nb<4>(a, nb, stages, grid, nt, st);
+    default: return launch_ring_nb<8>(a, nb, stages, grid, nt, st);
     }
 }
 
@@ -228,7 +263,7 @@ using namespace att;
 extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32_t stages, uint32_t grid,
                                     uint32_t variant, void* stream) {
     if (!src || !dst) return TMAP_ERR_NULL;
-    if (stages < 1 || stages > 4 || variant > 2) return TMAP_ERR_UNSUPPORTED;
+    if (stages < 1 || stages > 8 || variant > 63) return TMAP_ERR_UNSUPPORTED;
     CopyArgs a;
     a.src = load_map(src);
     a.dst = load_map(dst);
@@ -247,6 +282,8 @@ extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32
     }
     if (T == 0 || T > 0x7FFFFFFFull) return TMAP_ERR_UNSUPPORTED;
     a.ntiles = (uint32_t)T;
+    a.chunked = (variant & CV_CHUNKED) ? 1u : 0u;
+    a.xcd = 0u;
     uint32_t limit = 0, cus = 0;
     tmap_status st = device_lds_limit(&limit);
     if (st) return st;
@@ -255,13 +292,17 @@ extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32
     const uint32_t B = a.src.box_bytes;
     const uint32_t groups = B / 1024u;
     const uint32_t gpw = (B % 1024u == 0) ? groups / kCopyWaves : 0u;
-    const bool ring_ok = even && variant != 2 && gpw * kCopyWaves == groups &&
-                         (gpw == 1 || gpw == 2 || gpw == 4 || gpw == 8) && stages * B <= limit;
+    uint32_t nb = 1u << ((variant >> CV_NB_SHIFT) & 3u);
+    if (a.ntiles % nb != 0) nb = 1;
+    const bool ring_ok = even && !(variant & CV_GENERIC) && gpw * kCopyWaves == groups &&
+                         (gpw == 1 || gpw == 2 || gpw == 4 || gpw == 8) && stages * nb * B <= limit &&
+                         gpw * nb * (stages - 1) <= 63 && stages != 5 && stages != 7;
     hipStream_t s = as_stream(stream);
     if (ring_ok) {
-        const uint32_t g = grid ? grid : auto_grid(a.ntiles, cus, stages * B);
-        if (variant == 1) return launch_ring_g<true>(a, gpw, stages, g, s);
-        return launch_ring_g<false>(a, gpw, stages, g, s);
+        const uint32_t units = a.ntiles / nb;
+        const uint32_t g = grid ? grid : auto_grid(units, cus, stages * nb * B);
+        a.xcd = ((variant & CV_XCD) && g % kNumXcd == 0) ? 1u : 0u;
+        return launch_ring_g(a, gpw, nb, stages, g, (variant & CV_NT_STORE) ? 1u : 0u, s);
     }
     const uint32_t lds = round_up(B, 1024u);
     if (lds > limit) return TMAP_ERR_LDS_CAPACITY;
@@ -272,6 +313,17 @@ extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32
     return check_launch("tile_copy");
 }
 
+// Default launch: non-temporal stores, workgroups owning neighbouring boxes,
+// two ring stages' worth of boxes per workgroup so that LDS, not the grid,
+// bounds how many workgroups share a CU.
 extern "C" tmap_status tile_copy(const tmap_t* src, const tmap_t* dst, uint32_t stages, void* stream) {
-    return tile_copy_ex(src, dst, stages, 0u, 0u, stream);
+    if (!src) return TMAP_ERR_NULL;
+    const TmapImpl s = load_map(src);
+    uint64_t T = 1;
+    for (int d = 0; d < 5; ++d) {
+        const uint64_t bx = (uint64_t)s.box_m1[d] + 1u;
+        T *= ((uint64_t)s.dim[d] + bx - 1) / bx;
+    }
+    const uint32_t grid = T >= 2 ? (uint32_t)((T + 1) / 2) : 1u;
+    return tile_copy_ex(src, dst, stages, grid, CV_NT_STORE | CV_CHUNKED, stream);
 }

@@ -126,6 +126,18 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_group) {
     __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_group, 16, 0, 0);
 }
 
+// The same 16-byte copy with a wave-uniform 64-bit base (SGPRs), a per-lane
+// 32-bit offset and the LDS group address in M0, issued as inline asm so the
+// compiler's LDS alias tracking does not see it: the caller orders it against
+// LDS reads with its own vmcnt waits and barriers (the s_nop covers the M0
+// write hazard).
+__device__ __forceinline__ void dma16_sv(uint64_t sbase, uint32_t voff, uint32_t lds_group_addr) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "{m0}"(lds_group_addr)
+                 : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -133,6 +145,30 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Retire the copies of the stage about to be read when `later` stages of
+// PER DMA instructions each were issued after it.  Loads complete in issue
+// order, so vmcnt <= later * PER means that stage has landed in LDS.
+template <int PER, int K>
+__device__ __forceinline__ void wait_stage(uint32_t later) {
+    if constexpr (K > 0) {
+        if (later >= (uint32_t)K) {
+            wait_vmcnt<K * PER>();
+            return;
+        }
+        wait_stage<PER, K - 1>(later);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+// Workgroup barrier that also stops the compiler from moving memory
+// accesses across it (the raw s_barrier builtin alone does not).
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // ds_read_b128 issued as inline asm: the compiler's own LDS-DMA alias
 // tracking would otherwise put vmcnt(0) in front of every LDS read and

@@ -121,6 +121,25 @@ def run_extra(att, torch, stream, reps: int):
     ms = timed(lambda: att.tile_reduce_add(mr, rc.data_ptr(), ex["nbox"], srcs.data_ptr(), stream), reps)
     out["reduce_add_i32_pass"] = {"ms": round(ms, 4),
                                   "GBps_algorithmic": round(ex["nbox"] * 16384 * 3 / ms / 1e6, 1)}
+
+    # bf16 GEMM mainloop, M = N = K = 8192, A row-major, B column-major
+    ex = W.GEMM_8192
+    M, N, K = ex["M"], ex["N"], ex["K"]
+    g = torch.Generator(device="cuda").manual_seed(ex["seed"])
+    Ad = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
+    Bd = torch.randn(N, K, generator=g, device="cuda").to(torch.bfloat16)
+    Cd = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    best = None
+    for bk, sw, stages in ((64, "128b", 2), (32, "64b", 3), (32, "64b", 4)):
+        mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (bk, 256), None, sw)
+        mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (bk, 256), None, sw)
+        ms = timed(lambda: att.gemm_bf16(mA, mB, Cd.data_ptr(), M, N, K, N, stages, stream), max(3, reps // 4))
+        tf = 2.0 * M * N * K / ms / 1e9
+        key = f"gemm_bf16_8192_bk{bk}_s{stages}"
+        out[key] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1), "pct_of_bf16_peak": round(100 * tf / 2500.0, 2)}
+        if best is None or tf > best[0]:
+            best = (tf, key)
+    out["gemm_best"] = best[1]
     return out
 
 
@@ -130,7 +149,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--stages", type=int, default=2)
-    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--variant", type=int, default=-1, help="-1: tile_copy defaults")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--pairs", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -164,7 +183,10 @@ def main():
 
     def step(k):
         _, _, ms_, md_ = pairs[k % len(pairs)]
-        att.tile_copy_ex(ms_, md_, args.stages, args.grid, args.variant, stream)
+        if args.variant < 0:
+            att.tile_copy(ms_, md_, args.stages, stream)
+        else:
+            att.tile_copy_ex(ms_, md_, args.stages, args.grid, args.variant, stream)
 
     for k in range(args.warmup):
         step(k)

@@ -182,12 +182,16 @@ tmap_status tile_reduce_add(const tmap_t* m, const int32_t* d_coords, uint32_t n
  * LDS->global through `dst`, with `stages` LDS buffers per workgroup
  * (producer/consumer ring, [MLC] "TMA in a pipeline").  src and dst must have
  * the same dtype, rank, dims, box and swizzle, all element strides 1, and
- * must not overlap.  stages in [1, 4].  Errors: NULL, UNSUPPORTED (geometry
+ * must not overlap.  stages in [1, 8].  Errors: NULL, UNSUPPORTED (geometry
  * mismatch, stages, element strides), LDS_CAPACITY, HIP. */
 tmap_status tile_copy(const tmap_t* src, const tmap_t* dst, uint32_t stages, void* stream);
 
-/* Same as tile_copy with an explicit persistent grid size (0 = automatic)
- * and launch variant (0 = default); for tuning sweeps. */
+/* Same as tile_copy with an explicit grid size (0 = automatic) and launch
+ * variant bits, for tuning sweeps: 1 non-temporal stores, 2 force the
+ * generic one-workgroup-per-box path, 4 workgroups own contiguous box
+ * ranges (else strided), 8 XCD-aware workgroup numbering, bits 4..5 boxes
+ * per ring stage (1, 2, 4, 8).  tile_copy uses 1|4 with two boxes per
+ * workgroup.  Ring depths 5 and 7 take the generic path. */
 tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32_t stages,
                          uint32_t grid, uint32_t variant, void* stream);
 
@@ -222,11 +226,21 @@ tmap_status lds_bank_probe(int32_t layout, uint32_t iters, int32_t* d_hist, void
  * `stages`-deep LDS ring and consumed by MFMA bf16 with fp32 accumulation.
  * d_C is M x N row-major bf16 (round to nearest even), leading dimension
  * ldc >= N elements.  Ragged M, N, K are handled by the maps' zero fill and a
- * masked epilogue.  stages in [2, 2] on gfx950 (two 64 KiB stages fill the
- * 160 KiB LDS; three do not fit).  Errors: NULL, UNSUPPORTED (map shape,
- * dtype, box, swizzle, stages), HIP. */
+ * masked epilogue.  stages = 2 for the 64-deep K step (two 64 KiB stages
+ * fit the 160 KiB LDS, three do not).  Errors: NULL, UNSUPPORTED (map shape,
+ * dtype, box, swizzle, OOB fill other than zero, stages, ldc < N), HIP.
+ * M == 0 or N == 0 is a no-op. */
 tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
                       uint32_t K, uint32_t ldc, uint32_t stages, void* stream);
+
+/* gemm_bf16 with tuning knobs: `group_m` tile rows per rasterisation group
+ * (0 = 8) and `xcd` (1 = give each XCD a contiguous range of tiles).  A map
+ * with box {32, 256} and TMAP_SWIZZLE_64B selects the 32-deep K step, for
+ * which stages may be 2, 3 or 4; box {64, 256} with TMAP_SWIZZLE_128B takes
+ * stages = 2. */
+tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
+                         uint32_t K, uint32_t ldc, uint32_t stages, uint32_t group_m, uint32_t xcd,
+                         void* stream);
 
 #ifdef __cplusplus
 }
