@@ -34,14 +34,20 @@ def bf16_to_f64(bits):
 
 
 def run_gemm(A_bits, Bt_bits, M, N, K, bk=64, stages=2, group_m=0, xcd=1):
-    """A_bits (M, K) row-major; Bt_bits (N, K) = column-major B.  Returns the
-    bf16 bits of C (M, N)."""
-    Ad = torch.from_numpy(A_bits.view(np.int16).copy()).cuda()
-    Bd = torch.from_numpy(Bt_bits.view(np.int16).copy()).cuda()
+    """A_bits (M, K) row-major; Bt_bits (N, K) = column-major B.  Rows are
+    stored with a leading dimension padded to a multiple of 8 elements (the
+    maps need 16-byte strides).  Returns the bf16 bits of C (M, N)."""
+    ld = (K + 7) // 8 * 8
+    Ap = np.zeros((M, ld), dtype=np.uint16)
+    Ap[:, :K] = A_bits
+    Bp = np.zeros((N, ld), dtype=np.uint16)
+    Bp[:, :K] = Bt_bits
+    Ad = torch.from_numpy(Ap.view(np.int16)).cuda()
+    Bd = torch.from_numpy(Bp.view(np.int16)).cuda()
     Cd = torch.full((M, N), 0x7FFF, dtype=torch.int16, device="cuda")
     sw = "128b" if bk == 64 else "64b"
-    mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (bk, 256), None, sw)
-    mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (bk, 256), None, sw)
+    mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (ld * 2,), (bk, 256), None, sw)
+    mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (ld * 2,), (bk, 256), None, sw)
     att.gemm_bf16_ex(mA, mB, Cd.data_ptr(), M, N, K, N, stages, group_m, xcd, stream())
     torch.cuda.synchronize()
     return Cd.cpu().numpy().view(np.uint16)
