@@ -15,8 +15,9 @@
 // with global_load_lds_dwordx4 (swizzle applied on the source side, as in the
 // loader), waits vmcnt, and one s_barrier publishes the stage.  Fragment
 // reads use the same swizzle: lane l of a 32 x 16 operand reads row l % 32,
-// logical chunk 2*kk + l / 32, at physical chunk (logical ^ (row & 7))
-// (measured conflict-free on gfx950's LDS).
+// logical chunk 2*kk + l / 32, at the physical chunk the map's swizzle gives.
+// With the pages' 8-row key those reads hit every LDS bank twice on gfx950
+// (16 lanes x 16 bytes per clock); the _K256 modes' 16-row key removes that.
 #include <hip/hip_runtime.h>
 
 #include "host_util.hpp"
@@ -57,7 +58,8 @@ __device__ __forceinline__ void gemm_tile_of(const GemmArgs& g, uint32_t b, uint
 // EDGE = false: every box is inside the tensors (M, N multiples of 256, K a
 // multiple of BK), copies use precomputed per-lane offsets.  EDGE = true: any
 // shape; boxes go through the general loader with zero fill at the edges.
-template <int BK, int S, bool EDGE>
+// SWM: the operands' swizzle mode (64B / 128B, or their _K256 forms).
+template <int BK, int S, bool EDGE, int SWM>
 __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16(GemmArgs g) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr uint32_t ROWB = BK * 2;                 // bytes per LDS row (128 or 64)
@@ -65,7 +67,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     constexpr uint32_t STAGE = 2 * BOX;
     constexpr uint32_t GROUPS = BOX / 1024;           // 1 KiB DMA groups per box
     constexpr uint32_t GPW = GROUPS / 4;              // per wave and operand
-    constexpr uint32_t SW = BK == 64 ? 3u : 2u;       // swizzle bits (128B / 64B)
+    constexpr uint32_t SW = SWM & 3;                  // swizzled chunk bits (3 or 2)
+    constexpr uint32_t KSH = (SWM & 4) ? 8u : 7u;     // key: 256- or 128-byte unit
     constexpr uint32_t CPR = ROWB / 16;               // chunks per row
 
     const uint32_t wave = threadIdx.x >> 6;
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (uint32_t j = 0; j < GPW; ++j) {
         const uint32_t p = (wave * GPW + j) * 64u + lane;
-        const uint32_t q = swz_chunk(p, SW);
+        const uint32_t q = swz_chunk(p, SWM);
         const uint32_t row = q / CPR, ch = q % CPR;
         offA[j] = row * (uint32_t)g.A.stride[0] + ch * 16u;
         offB[j] = row * (uint32_t)g.B.stride[0] + ch * 16u;
@@ -149,13 +152,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t row = rowA0 + i * 32u;
-                const uint32_t pc = lc ^ (((row * ROWB) >> 7) & ((1u << SW) - 1u));
+                const uint32_t pc = lc ^ (((row * ROWB) >> KSH) & ((1u << SW) - 1u));
                 a[i] = *reinterpret_cast<const bf16x8*>(sA + row * ROWB + pc * 16u);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t row = rowB0 + j * 32u;
-                const uint32_t pc = lc ^ (((row * ROWB) >> 7) & ((1u << SW) - 1u));
+                const uint32_t pc = lc ^ (((row * ROWB) >> KSH) & ((1u << SW) - 1u));
                 b[j] = *reinterpret_cast<const bf16x8*>(sB + row * ROWB + pc * 16u);
             }
         };
@@ -195,33 +198,38 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         }
 }
 
-template <int BK, int S, bool EDGE>
+template <int BK, int S, bool EDGE, int SWM>
 static tmap_status launch_gemm_t(const GemmArgs& g, hipStream_t st) {
     constexpr uint32_t lds = (uint32_t)S * 2u * kTM * BK * 2u;
     uint32_t limit = 0;
     tmap_status s = device_lds_limit(&limit);
     if (s) return s;
     if (lds > limit) return TMAP_ERR_UNSUPPORTED;
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16<BK, S, EDGE>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16<BK, S, EDGE, SWM>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-    hipLaunchKernelGGL((k_gemm_bf16<BK, S, EDGE>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st, g);
+    hipLaunchKernelGGL((k_gemm_bf16<BK, S, EDGE, SWM>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st, g);
     return check_launch("gemm_bf16");
 }
 
 template <int BK, int S>
-static tmap_status launch_gemm(const GemmArgs& g, hipStream_t st) {
+static tmap_status launch_gemm(const GemmArgs& g, uint32_t swm, hipStream_t st) {
     const bool even = g.M % kTM == 0 && g.N % kTN == 0 && g.K % BK == 0;
-    return even ? launch_gemm_t<BK, S, false>(g, st) : launch_gemm_t<BK, S, true>(g, st);
+    constexpr int BASE = BK == 64 ? TMAP_SWIZZLE_128B : TMAP_SWIZZLE_64B;
+    if (swm & 4u)
+        return even ? launch_gemm_t<BK, S, false, BASE | 4>(g, st) : launch_gemm_t<BK, S, true, BASE | 4>(g, st);
+    return even ? launch_gemm_t<BK, S, false, BASE>(g, st) : launch_gemm_t<BK, S, true, BASE>(g, st);
 }
 
-static tmap_status check_operand(const TmapImpl& t, uint32_t rows, uint32_t K, uint32_t* bk) {
+static tmap_status check_operand(const TmapImpl& t, uint32_t rows, uint32_t K, uint32_t* bk, uint32_t* swm) {
     if (t.dtype != TMAP_BF16 || t.rank != 2 || t.oob != TMAP_OOB_ZERO) return TMAP_ERR_UNSUPPORTED;
     if ((uint64_t)t.dim[0] != K || (uint64_t)t.dim[1] != rows) return TMAP_ERR_UNSUPPORTED;
     if (t.es[0] != 1 || t.es[1] != 1 || (uint32_t)t.box_m1[1] + 1u != (uint32_t)kTM) return TMAP_ERR_UNSUPPORTED;
     const uint32_t b0 = (uint32_t)t.box_m1[0] + 1u;
-    if (!((b0 == 64 && t.swizzle == TMAP_SWIZZLE_128B) || (b0 == 32 && t.swizzle == TMAP_SWIZZLE_64B)))
+    const uint32_t span = t.swizzle & 3u;
+    if (!((b0 == 64 && span == TMAP_SWIZZLE_128B) || (b0 == 32 && span == TMAP_SWIZZLE_64B)))
         return TMAP_ERR_UNSUPPORTED;
+    *swm = t.swizzle;
     if (t.stride[0] >= (1ull << 31) / kTM) return TMAP_ERR_UNSUPPORTED;   // 32-bit in-box offsets
     *bk = b0;
     return TMAP_OK;
@@ -240,12 +248,12 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
     GemmArgs g;
     g.A = load_map(A);
     g.B = load_map(B);
-    uint32_t bka = 0, bkb = 0;
-    tmap_status s = check_operand(g.A, M, K, &bka);
+    uint32_t bka = 0, bkb = 0, swa = 0, swb = 0;
+    tmap_status s = check_operand(g.A, M, K, &bka, &swa);
     if (s) return s;
-    s = check_operand(g.B, N, K, &bkb);
+    s = check_operand(g.B, N, K, &bkb, &swb);
     if (s) return s;
-    if (bka != bkb) return TMAP_ERR_UNSUPPORTED;
+    if (bka != bkb || swa != swb) return TMAP_ERR_UNSUPPORTED;
     g.C = reinterpret_cast<uint64_t>(d_C);
     g.M = M; g.N = N; g.K = K; g.ldc = ldc;
     g.tiles_m = (M + kTM - 1) / kTM;
@@ -255,13 +263,13 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
     g.xcd = (xcd && G % 8u == 0) ? 1u : 0u;
     hipStream_t st = as_stream(stream);
     if (bka == 64) {
-        if (stages == 2) return launch_gemm<64, 2>(g, st);
+        if (stages == 2) return launch_gemm<64, 2>(g, swa, st);
         return TMAP_ERR_UNSUPPORTED;
     }
     switch (stages) {
-    case 2: return launch_gemm<32, 2>(g, st);
-    case 3: return launch_gemm<32, 3>(g, st);
-    case 4: return launch_gemm<32, 4>(g, st);
+    case 2: return launch_gemm<32, 2>(g, swa, st);
+    case 3: return launch_gemm<32, 3>(g, swa, st);
+    case 4: return launch_gemm<32, 4>(g, swa, st);
     default: return TMAP_ERR_UNSUPPORTED;
     }
 }

@@ -127,6 +127,22 @@ __global__ __launch_bounds__(64) void k_lds_bank_probe(int32_t layout, uint32_t 
     for (uint32_t i = lane; i < 256; i += 64) reinterpret_cast<u32x4*>(grid)[i] = u32x4{i, i, i, i};
     __syncthreads();
     uint32_t sink = 0;
+    if (layout >= 2) {
+        // One MFMA 32x32x16 operand fragment from a 32-row x 128-byte box:
+        // lane l reads row l % 32, logical chunk l / 32, at the physical
+        // chunk the swizzle gives (layout 2: 128B, layout 3: 128B_K256).
+        const uint32_t sw = layout == 2 ? TMAP_SWIZZLE_128B : TMAP_SWIZZLE_128B_K256;
+        const uint32_t a = swz_chunk((lane & 31u) * 8u + (lane >> 5), sw) * 16u;
+        const uint32_t la = lds_addr_of(grid) + a;
+        for (uint32_t it = 0; it < iters; ++it) {
+            const u32x4 v = lds_read16(la);
+            wait_lgkm0();
+            sink ^= v.x;
+        }
+        hist[lane] = (int32_t)a;
+        if (sink == 0xFFFFFFFFu) hist[64] = -1;
+        return;
+    }
     for (uint32_t row0 = 0; row0 <= 8; ++row0) {
         for (uint32_t col = 0; col < 16; ++col) {
             const uint32_t a = probe_addr(layout, row0 + (lane & 7u), col);
@@ -220,7 +236,7 @@ extern "C" tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, 
 
 extern "C" tmap_status lds_bank_probe(int32_t layout, uint32_t iters, int32_t* d_hist, void* stream) {
     if (!d_hist) return TMAP_ERR_NULL;
-    if (layout != 0 && layout != 1) return TMAP_ERR_UNSUPPORTED;
+    if (layout < 0 || layout > 3) return TMAP_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(k_lds_bank_probe, dim3(1), dim3(64), 0, as_stream(stream), layout, iters, d_hist);
     return check_launch("lds_bank_probe");
 }

@@ -47,11 +47,12 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, uint32_t magic) {
     return magic ? __umulhi(n, magic) : n;
 }
 
-// Physical <-> logical 16-byte chunk inside a box image.  Chunk bits 0..2
-// (position in a 128-byte unit) are XORed with bits 3..5 (the 128-byte unit
-// index), keeping `sw` of them: 3 for 128B, 2 for 64B, 1 for 32B, 0 for NONE.
+// Physical <-> logical 16-byte chunk inside a box image.  The low (sw & 3)
+// chunk bits (3 for 128B, 2 for 64B, 1 for 32B, 0 for NONE) are XORed with
+// the 128-byte unit index (chunk bits 3..), or with the 256-byte unit index
+// (chunk bits 4..) for the _K256 modes.
 __device__ __forceinline__ uint32_t swz_chunk(uint32_t c, uint32_t sw) {
-    return c ^ ((c >> 3) & ((1u << sw) - 1u));
+    return c ^ ((c >> (3u + ((sw >> 2) & 1u))) & ((1u << (sw & 3u)) - 1u));
 }
 
 // Box coordinates of logical chunk q: k[0] is the first element's index in

@@ -59,7 +59,7 @@ extern "C" tmap_status tmap_encode(tmap_t* out, int32_t dtype, uint32_t rank, vo
     if (rank < 1 || rank > 5) return TMAP_ERR_RANK;
     const int es = esize_of(dtype);
     if (es == 0) return TMAP_ERR_DTYPE;
-    if (swizzle < TMAP_SWIZZLE_NONE || swizzle > TMAP_SWIZZLE_128B) return TMAP_ERR_UNSUPPORTED;
+    if (swizzle < TMAP_SWIZZLE_NONE || swizzle > TMAP_SWIZZLE_128B_K256 || swizzle == 4) return TMAP_ERR_UNSUPPORTED;
     if (oob != TMAP_OOB_ZERO && oob != TMAP_OOB_NAN) return TMAP_ERR_UNSUPPORTED;
     if (!gaddr) return TMAP_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(gaddr) % 16 != 0) return TMAP_ERR_ALIGN;
@@ -82,7 +82,7 @@ extern "C" tmap_status tmap_encode(tmap_t* out, int32_t dtype, uint32_t rank, vo
     }
     const uint32_t row_bytes = L[0] * (uint32_t)es;
     if (row_bytes % 16 != 0) return TMAP_ERR_ESTRIDE;
-    if (swizzle != TMAP_SWIZZLE_NONE && row_bytes != (16u << swizzle)) return TMAP_ERR_SWIZZLE_WIDTH;
+    if (swizzle != TMAP_SWIZZLE_NONE && row_bytes != (16u << (swizzle & 3))) return TMAP_ERR_SWIZZLE_WIDTH;
     if (oob == TMAP_OOB_NAN && !is_float(dtype)) return TMAP_ERR_OOB_FILL_DTYPE;
     uint64_t bytes = (uint64_t)es;
     for (int d = 0; d < 5; ++d) bytes *= L[d];
@@ -141,7 +141,7 @@ extern "C" tmap_status tmap_query(const tmap_t* m, tmap_info_t* info) {
     for (int d = 0; d < 5; ++d) info->lds_extent[d] = t->L[d];
     info->box_bytes = t->box_bytes;
     info->row_bytes = (uint32_t)t->cpr * 16u;
-    info->atom_bytes = t->swizzle ? 8u * (16u << t->swizzle) : 0u;
+    info->atom_bytes = t->swizzle ? ((t->swizzle & 4) ? 16u : 8u) * (16u << (t->swizzle & 3)) : 0u;
     info->base = t->base;
     return TMAP_OK;
 }

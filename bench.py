@@ -122,20 +122,41 @@ def run_extra(att, torch, stream, reps: int):
     out["reduce_add_i32_pass"] = {"ms": round(ms, 4),
                                   "GBps_algorithmic": round(ex["nbox"] * 16384 * 3 / ms / 1e6, 1)}
 
-    # bf16 GEMM mainloop, M = N = K = 8192, A row-major, B column-major
+    out.update(run_gemm(att, torch, stream, max(3, reps // 4)))
+    return out
+
+
+GEMM_VARIANTS = ((64, "128b", 2), (32, "64b", 4), (64, "128b_k256", 2), (32, "64b_k256", 3),
+                 (32, "64b_k256", 4))
+
+
+def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS):
+    """bf16 GEMM mainloop, M = N = K = 8192, A row-major, B column-major,
+    N(0,1) operands; 2*M*N*K flop per launch."""
+    from synthgen import workloads as W
+
     ex = W.GEMM_8192
     M, N, K = ex["M"], ex["N"], ex["K"]
     g = torch.Generator(device="cuda").manual_seed(ex["seed"])
     Ad = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
     Bd = torch.randn(N, K, generator=g, device="cuda").to(torch.bfloat16)
     Cd = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    best = None
-    for bk, sw, stages in ((64, "128b", 2), (32, "64b", 3), (32, "64b", 4)):
+    out, best = {}, None
+    for bk, sw, stages in variants:
         mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (bk, 256), None, sw)
         mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (bk, 256), None, sw)
-        ms = timed(lambda: att.gemm_bf16(mA, mB, Cd.data_ptr(), M, N, K, N, stages, stream), max(3, reps // 4))
+        fn = lambda: att.gemm_bf16(mA, mB, Cd.data_ptr(), M, N, K, N, stages, stream)  # noqa: E731
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
         tf = 2.0 * M * N * K / ms / 1e9
-        key = f"gemm_bf16_8192_bk{bk}_s{stages}"
+        key = f"gemm_bf16_8192_bk{bk}_{sw}_s{stages}"
         out[key] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1), "pct_of_bf16_peak": round(100 * tf / 2500.0, 2)}
         if best is None or tf > best[0]:
             best = (tf, key)
@@ -154,6 +175,12 @@ def main():
     ap.add_argument("--pairs", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true")
+    ap.add_argument("--only", choices=["copy", "gemm"], default="copy",
+                    help="gemm: time only the GEMM mainloop (profiling runs)")
+    ap.add_argument("--gemm-variant", default="all",
+                    help="bk,stages[,k256] e.g. 32,4,k256 (with --only gemm)")
+    ap.add_argument("--ref-copy", action="store_true",
+                    help="also time a plain device-to-device copy of the same bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -171,6 +198,22 @@ def main():
     att.lib()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream().cuda_stream
+    if args.only == "gemm":
+        variants = GEMM_VARIANTS
+        if args.gemm_variant != "all":
+            bk, st, *k = args.gemm_variant.split(",")
+            bk, st = int(bk), int(st)
+            variants = ((bk, ("128b" if bk == 64 else "64b") + ("_k256" if k else ""), st),)
+        res = run_gemm(att, torch, stream, args.steps, variants)
+        best = res[res["gemm_best"]]
+        print(json.dumps({"metric": "bf16 GEMM 8192^3 TFLOP/s", "value": best["TFLOPs"], "unit": "TFLOP/s",
+                          "n_gpus": 1, "steps": args.steps, "higher_is_better": True, "dtype": "bf16",
+                          "data": "synthetic", "config": {"workload": "bf16 GEMM M=N=K=8192"},
+                          "roofline": {"bound": "mfma", "achieved": best["TFLOPs"], "peak": 2500.0,
+                                       "unit": "TFLOP/s", "frac": round(best["TFLOPs"] / 2500.0, 4),
+                                       "traffic": None},
+                          "detail": res}), flush=True)
+        return
     ex = W.COPY_8192
     src_host = torch.from_numpy(synthgen.u16_bits(ex["seed"], (8192, 8192)).view(np.uint8).reshape(-1))
     pairs = []
@@ -203,6 +246,24 @@ def main():
 
     verified = all(torch.equal(s, d) for s, d, _, _ in pairs)
 
+    ref_copy = None
+    if args.ref_copy:
+        def ref_step(k):
+            s_, d_, _, _ = pairs[k % len(pairs)]
+            d_.copy_(s_)
+        for k in range(args.warmup):
+            ref_step(k)
+        torch.cuda.synchronize()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        for k in range(args.steps):
+            ref_step(k)
+        b_.record()
+        torch.cuda.synchronize()
+        rms = a_.elapsed_time(b_) / args.steps
+        ref_copy = {"what": "torch copy_ of the same 128 MiB pairs (plain device copy)",
+                    "GBps": round(BYTES_PER_STEP / rms / 1e6, 1), "ms": round(rms, 5)}
+
     ctr = committed_counters()
     traffic = None
     conflicts = None
@@ -233,6 +294,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if ref_copy:
+        result["reference_copy"] = ref_copy
     if args.extra:
         result["extra"] = run_extra(att, torch, stream, 20)
     if not args.no_cpu_baseline:

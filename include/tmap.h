@@ -56,9 +56,15 @@ typedef enum {
  * logical 16-byte sector c of row r at physical sector c XOR (r % 8) ([MLC]
  * "TMA writes swizzled layout"; atoms of 8 rows, [MLC] "3D TMA").  The pages
  * only name the 32- and 64-byte modes; their bit pattern is this library's
- * reading. */
+ * reading.
+ * The _K256 modes are this library's addition for gfx950, whose LDS serves
+ * ds_read_b128 at 256 bytes per clock: the key is taken from bits
+ * 8..(7+b) (the 256-byte unit index), giving 16-row atoms, so that one
+ * 16-byte column read across 32 rows (an MFMA 32x32 operand fragment) hits
+ * every bank once where the 8-row pattern hits each bank twice. */
 typedef enum {
-    TMAP_SWIZZLE_NONE = 0, TMAP_SWIZZLE_32B = 1, TMAP_SWIZZLE_64B = 2, TMAP_SWIZZLE_128B = 3
+    TMAP_SWIZZLE_NONE = 0, TMAP_SWIZZLE_32B = 1, TMAP_SWIZZLE_64B = 2, TMAP_SWIZZLE_128B = 3,
+    TMAP_SWIZZLE_32B_K256 = 5, TMAP_SWIZZLE_64B_K256 = 6, TMAP_SWIZZLE_128B_K256 = 7
 } tmap_swizzle;
 
 /* Out-of-bounds fill for loads ([H200] section 02 table: zero or NaN).
@@ -99,7 +105,8 @@ typedef struct {
     uint32_t lds_extent[5];  /* ceil(box[i] / estride[i]); 1 beyond rank    */
     uint32_t box_bytes;      /* esize * prod(lds_extent): expect_tx amount  */
     uint32_t row_bytes;      /* lds_extent[0] * esize                       */
-    uint32_t atom_bytes;     /* 8 rows of the swizzle span, 0 for NONE      */
+    uint32_t atom_bytes;     /* one period of the XOR key: 8 rows (16 rows
+                                for _K256) of the span; 0 for NONE          */
     uint64_t base;           /* current global base address                 */
 } tmap_info_t;
 
@@ -216,13 +223,19 @@ tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, uint32_t nt
  * swizzled addresses the device address generator produces.  For row0 in
  * 0..8 and col in 0..15 the kernel writes the hit count of each bank sector
  * ((addr >> 4) & 7) to d_hist[(row0*16 + col)*8 + s], and repeats the reads
- * `iters` times so hardware counters can be sampled.  Errors: NULL, HIP. */
+ * `iters` times so hardware counters can be sampled.
+ * Layouts 2 and 3 instead read one MFMA 32x32x16 operand fragment of a
+ * 32-row x 128-byte box (lane l: row l % 32, logical chunk l / 32) under
+ * TMAP_SWIZZLE_128B (2) or TMAP_SWIZZLE_128B_K256 (3), `iters` times, and
+ * write each lane's physical LDS byte offset to d_hist[l] (64 entries).
+ * Errors: NULL, UNSUPPORTED (layout), HIP. */
 tmap_status lds_bank_probe(int32_t layout, uint32_t iters, int32_t* d_hist, void* stream);
 
 /* Consumer: bf16 GEMM mainloop C = A * B ([MLC] overview and "TMA in a
  * pipeline"; [H200] section 02 result).  A is M x K row-major (map dims
  * {K, M}), B is K x N column-major (map dims {K, N}), both bf16 with box
- * {64, 256} and TMAP_SWIZZLE_128B; tiles are staged by the tile loader into a
+ * {64, 256} and TMAP_SWIZZLE_128B or TMAP_SWIZZLE_128B_K256; tiles are staged
+ * by the tile loader into a
  * `stages`-deep LDS ring and consumed by MFMA bf16 with fp32 accumulation.
  * d_C is M x N row-major bf16 (round to nearest even), leading dimension
  * ldc >= N elements.  Ragged M, N, K are handled by the maps' zero fill and a
@@ -234,9 +247,9 @@ tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, u
                       uint32_t K, uint32_t ldc, uint32_t stages, void* stream);
 
 /* gemm_bf16 with tuning knobs: `group_m` tile rows per rasterisation group
- * (0 = 8) and `xcd` (1 = give each XCD a contiguous range of tiles).  A map
- * with box {32, 256} and TMAP_SWIZZLE_64B selects the 32-deep K step, for
- * which stages may be 2, 3 or 4; box {64, 256} with TMAP_SWIZZLE_128B takes
+ * (0 = 8) and `xcd` (1 = give each XCD a contiguous range of tiles).  Maps
+ * with box {32, 256} and TMAP_SWIZZLE_64B or TMAP_SWIZZLE_64B_K256 select the
+ * 32-deep K step, for which stages may be 2, 3 or 4; box {64, 256} takes
  * stages = 2. */
 tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
                          uint32_t K, uint32_t ldc, uint32_t stages, uint32_t group_m, uint32_t xcd,

@@ -29,7 +29,7 @@ DTYPES = {"u8": 0, "u16": 1, "u32": 2, "i32": 3, "u64": 4, "i64": 5,
           "f16": 6, "bf16": 7, "f32": 8, "f64": 9}
 ESIZE = {"u8": 1, "u16": 2, "u32": 4, "i32": 4, "u64": 8, "i64": 8,
          "f16": 2, "bf16": 2, "f32": 4, "f64": 8}
-SWIZZLES = {"none": 0, "32b": 1, "64b": 2, "128b": 3}
+SWIZZLES = {"none": 0, "32b": 1, "64b": 2, "128b": 3, "32b_k256": 5, "64b_k256": 6, "128b_k256": 7}
 FILLS = {"zero": 0, "nan": 1}
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_RANK", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
           5: "ERR_DIM", 6: "ERR_STRIDE", 7: "ERR_BOX", 8: "ERR_ESTRIDE",

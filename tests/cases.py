@@ -22,12 +22,12 @@ def random_case(g: np.random.Generator, swizzle=None, dtype=None, rank=None):
     c.dtype = dtype or str(g.choice(list(ESIZE)))
     es = ESIZE[c.dtype]
     c.rank = rank or int(g.integers(1, 6))
-    c.swizzle = swizzle or str(g.choice(["none", "32b", "64b", "128b"]))
+    c.swizzle = swizzle or str(g.choice(["none", "32b", "64b", "128b", "32b_k256", "64b_k256", "128b_k256"]))
     c.estride = [int(g.integers(1, 4)) for _ in range(c.rank)]
     if c.swizzle == "none":
         L0 = (16 // es) * int(g.integers(1, 4))
     else:
-        L0 = (16 << {"32b": 1, "64b": 2, "128b": 3}[c.swizzle]) // es
+        L0 = (16 << {"32b": 1, "64b": 2, "128b": 3}[c.swizzle.split("_")[0]]) // es
     box0 = (L0 - 1) * c.estride[0] + int(g.integers(1, c.estride[0] + 1))
     if box0 * es % 16 != 0 or box0 > 256:
         c.estride[0] = 1

@@ -56,6 +56,8 @@ CASES = [
     dict(dtype="f32", dims=(32, 159, 8), strides=(128, 20352), box=(32, 159, 8)),
     dict(dtype="f32", dims=(32, 160, 8), strides=(128, 20480), box=(32, 160, 8)),
     dict(dtype="u8", box=(128, 8)), dict(dtype="f64", box=(16, 8), fill="nan"),
+    dict(swizzle="128b_k256"), dict(swizzle="64b_k256", box=(32, 8)), dict(swizzle="32b_k256", box=(16, 8)),
+    dict(swizzle="64b_k256"), dict(swizzle=4), dict(swizzle=8),
 ]
 
 
@@ -88,7 +90,7 @@ def test_encode_random_agreement():
         strides = [int(g.choice([0, 8, 16, 48, 1 << 40, (1 << 40) - 16, 4096])) for _ in range(rank - 1)]
         box = [int(g.choice([0, 1, 2, 4, 8, 16, 32, 64, 128, 256, 257])) for _ in range(rank)]
         es = [int(g.integers(0, 10)) for _ in range(rank)] if g.random() < 0.5 else None
-        sw = ["none", "32b", "64b", "128b"][int(g.integers(0, 4))]
+        sw = int(g.integers(0, 9))
         fill = ["zero", "nan"][int(g.integers(0, 2))]
         base = BASE + int(g.choice([0, 0, 0, 8]))
         got, want = _both(dtype, dims, strides, box, es, sw, fill, base)
@@ -99,6 +101,8 @@ def test_encode_query_and_replace():
     m = att.tmap_encode("f32", 5, BASE, (260, 129, 33, 7, 3), (1040, 134160, 4427280, 30990960),
                         (32, 32, 8, 2, 1), (1, 2, 1, 1, 1), "128b", "nan")
     q = att.tmap_query(m)
+    assert att.tmap_query(att.tmap_encode("bf16", 2, BASE, (64, 64), (128,), (64, 16), None,
+                                          "128b_k256"))["atom_bytes"] == 2048
     assert q["lds_extent"] == [32, 16, 8, 2, 1]
     assert q["box_bytes"] == 32768 == att.tmap_box_bytes(m)
     assert q["row_bytes"] == 128 and q["atom_bytes"] == 1024 and q["esize"] == 4

@@ -33,7 +33,7 @@ def bf16_to_f64(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def run_gemm(A_bits, Bt_bits, M, N, K, bk=64, stages=2, group_m=0, xcd=1):
+def run_gemm(A_bits, Bt_bits, M, N, K, bk=64, stages=2, group_m=0, xcd=1, k256=False):
     """A_bits (M, K) row-major; Bt_bits (N, K) = column-major B.  Rows are
     stored with a leading dimension padded to a multiple of 8 elements (the
     maps need 16-byte strides).  Returns the bf16 bits of C (M, N)."""
@@ -45,7 +45,7 @@ def run_gemm(A_bits, Bt_bits, M, N, K, bk=64, stages=2, group_m=0, xcd=1):
     Ad = torch.from_numpy(Ap.view(np.int16)).cuda()
     Bd = torch.from_numpy(Bp.view(np.int16)).cuda()
     Cd = torch.full((M, N), 0x7FFF, dtype=torch.int16, device="cuda")
-    sw = "128b" if bk == 64 else "64b"
+    sw = ("128b" if bk == 64 else "64b") + ("_k256" if k256 else "")
     mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (ld * 2,), (bk, 256), None, sw)
     mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (ld * 2,), (bk, 256), None, sw)
     att.gemm_bf16_ex(mA, mB, Cd.data_ptr(), M, N, K, N, stages, group_m, xcd, stream())
@@ -61,15 +61,16 @@ def check_close(got_bits, ref):
     assert not bad.any(), f"{bad.sum()} outputs out of tolerance, worst {err.max()}"
 
 
+@pytest.mark.parametrize("k256", [False, True])
 @pytest.mark.parametrize("bk,stages", [(64, 2), (32, 2), (32, 3), (32, 4)])
-def test_identity_exact(bk, stages):
+def test_identity_exact(bk, stages, k256):
     """A = I: C equals B exactly (one product per output, exact in fp32)."""
     K = N = 512
     M = K
     eye = np.zeros((M, K), dtype=np.uint16)
     eye[np.arange(M), np.arange(K)] = 0x3F80
     Bt = synthgen.normal_bf16_bits(51, (N, K))
-    C = run_gemm(eye, Bt, M, N, K, bk, stages)
+    C = run_gemm(eye, Bt, M, N, K, bk, stages, k256=k256)
     np.testing.assert_array_equal(C, Bt.T)
 
 
@@ -83,26 +84,29 @@ def test_permutation_exact():
     np.testing.assert_array_equal(C, Bt.T[perm])
 
 
-@pytest.mark.parametrize("M,N,K,bk,stages", [
-    (512, 768, 1024, 64, 2), (768, 512, 1024, 32, 3), (512, 512, 2048, 32, 4),
-    (300, 200, 100, 64, 2), (257, 513, 96, 32, 2), (1, 1, 64, 64, 2), (256, 256, 8, 64, 2)])
-def test_against_oracle_full(M, N, K, bk, stages):
-    say("gemm", M, N, K, bk, stages)
+@pytest.mark.parametrize("M,N,K,bk,stages,k256", [
+    (512, 768, 1024, 64, 2, False), (768, 512, 1024, 32, 3, False), (512, 512, 2048, 32, 4, False),
+    (512, 768, 1024, 64, 2, True), (768, 512, 1024, 32, 4, True), (300, 200, 100, 32, 3, True),
+    (300, 200, 100, 64, 2, False), (257, 513, 96, 32, 2, False), (1, 1, 64, 64, 2, False),
+    (256, 256, 8, 64, 2, False)])
+def test_against_oracle_full(M, N, K, bk, stages, k256):
+    say("gemm", M, N, K, bk, stages, k256)
     A = synthgen.normal_bf16_bits(54, (M, K))
     Bt = synthgen.normal_bf16_bits(55, (N, K))
-    C = run_gemm(A, Bt, M, N, K, bk, stages)
+    C = run_gemm(A, Bt, M, N, K, bk, stages, k256=k256)
     rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     ref = oracle.gemm_bf16_sample(A, Bt, K, rows.reshape(-1), cols.reshape(-1)).reshape(M, N)
     check_close(C, ref)
 
 
-def test_8192_sampled():
+@pytest.mark.parametrize("bk,stages,k256", [(64, 2, False), (32, 4, True), (64, 2, True)])
+def test_8192_sampled(bk, stages, k256):
     ex = W.GEMM_8192
     M, N, K = ex["M"], ex["N"], ex["K"]
     say("gemm 8192^3")
     A = synthgen.normal_bf16_bits(ex["seed"] * 1000 + 1, (M, K))
     Bt = synthgen.normal_bf16_bits(ex["seed"] * 1000 + 2, (N, K))
-    C = run_gemm(A, Bt, M, N, K)
+    C = run_gemm(A, Bt, M, N, K, bk, stages, k256=k256)
     rows, cols = synthgen.sample_pairs(ex["seed"] * 1000 + 3, ex["nsample"], M, N)
     ref = oracle.gemm_bf16_sample(A, Bt, K, rows, cols)
     check_close(C[rows, cols], ref)

@@ -103,6 +103,17 @@ def test_bank_sector_probe(table):
                 assert got[row0, col].tolist() == want, (layout, row0, col)
 
 
+@pytest.mark.parametrize("layout,mode", [(2, "128b"), (3, "128b_k256")])
+def test_bank_probe_mfma_fragment_addresses(layout, mode):
+    """The fragment read addresses the device generates equal the oracle's
+    swizzle of (row l % 32, chunk l / 32) in a 128-byte-row box."""
+    h = empty_dev(65 * 4, 0)
+    att.lds_bank_probe(layout, 4, h, stream())
+    got = to_host(h).view(np.int32)[:64]
+    want = [oracle.swizzle((l % 32) * 128 + (l // 32) * 16, mode) for l in range(64)]
+    assert got.tolist() == want
+
+
 def test_txbar_4096_bytes(table):
     """[MLC] waiting for a TMA load: two 2048-byte tiles complete one phase
     with expect_tx(4096); states replayed on the oracle barrier model."""
