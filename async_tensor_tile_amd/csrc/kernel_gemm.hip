@@ -129,48 +129,60 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     const uint32_t rowB0 = wn * 128u + (lane & 31u);
     const uint32_t khalf = lane >> 5;
 
-#pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-        if ((uint32_t)s < nk) issue(s);
-
-    for (uint32_t kt = 0; kt < nk; ++kt) {
-        // This wave's copies for stage kt have landed (later stages may still
-        // be in flight); the barrier then makes every wave's copies visible
-        // and guarantees the stage refilled below is no longer being read.
-        const uint32_t ahead = nk - 1 - kt < (uint32_t)(S - 2) ? nk - 1 - kt : (uint32_t)(S - 2);
-        if constexpr (interior) wait_stage<2 * GPW, S - 2>(ahead);
-        else wait_vmcnt<0>();
-        wait_lgkm0();
-        wg_barrier();
-        if (kt + S - 1 < nk) issue(kt + S - 1);
-
-        const uint8_t* sA = smem + (kt % S) * STAGE;
+    constexpr uint32_t KK = BK / 16;                  // MFMA sub-steps per stage
+    // Fragment reads for sub-step kk of the tile held in ring slot `slot`.
+    auto load_frags = [&](uint32_t slot, uint32_t kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+        const uint8_t* sA = smem + slot * STAGE;
         const uint8_t* sB = sA + BOX;
-        // Fragments of sub-step kk+1 are read while the 16 MFMAs of kk run.
-        auto load_frags = [&](uint32_t kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
-            const uint32_t lc = 2u * kk + khalf;      // logical 16-byte chunk of the row
+        const uint32_t lc = 2u * kk + khalf;          // logical 16-byte chunk of the row
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t row = rowA0 + i * 32u;
-                const uint32_t pc = lc ^ (((row * ROWB) >> KSH) & ((1u << SW) - 1u));
-                a[i] = *reinterpret_cast<const bf16x8*>(sA + row * ROWB + pc * 16u);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t row = rowA0 + i * 32u;
+            const uint32_t pc = lc ^ (((row * ROWB) >> KSH) & ((1u << SW) - 1u));
+            a[i] = *reinterpret_cast<const bf16x8*>(sA + row * ROWB + pc * 16u);
+        }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t row = rowB0 + j * 32u;
-                const uint32_t pc = lc ^ (((row * ROWB) >> KSH) & ((1u << SW) - 1u));
-                b[j] = *reinterpret_cast<const bf16x8*>(sB + row * ROWB + pc * 16u);
-            }
-        };
-        // Scheduling barriers pin the order [reads of kk+1][MFMAs of kk]: the
-        // reads then have the 16 MFMAs (512 matrix-core cycles) to land
-        // before the wait the compiler places ahead of their first use.
-        bf16x8 fa[2][4], fb[2][4];
-        load_frags(0, fa[0], fb[0]);
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t row = rowB0 + j * 32u;
+            const uint32_t pc = lc ^ (((row * ROWB) >> KSH) & ((1u << SW) - 1u));
+            b[j] = *reinterpret_cast<const bf16x8*>(sB + row * ROWB + pc * 16u);
+        }
+    };
+
+    // Prologue: all S ring slots in flight; wait for the first.
 #pragma unroll
-        for (uint32_t kk = 0; kk < BK / 16; ++kk) {
+    for (int s = 0; s < S; ++s)
+        if ((uint32_t)s < nk) issue(s);
+    if constexpr (interior) wait_stage<2 * GPW, S - 1>(nk - 1 < (uint32_t)(S - 1) ? nk - 1 : (uint32_t)(S - 1));
+    else wait_vmcnt<0>();
+    wait_lgkm0();
+    wg_barrier();
+
+    // Main loop.  Fragment registers are double-buffered: the reads for
+    // sub-step kk+1 are issued before the 16 MFMAs of kk (scheduling
+    // barriers pin that order).  During the last sub-step of a tile the wave
+    // has issued every read of that slot, so that is where it waits for the
+    // next tile's copies, joins the workgroup barrier (after which no wave
+    // reads the slot any more), refills the slot with tile kt+S and starts
+    // reading the next tile -- all while the last 16 MFMAs of this tile run.
+    bf16x8 fa[2][4], fb[2][4];
+    load_frags(0, 0, fa[0], fb[0]);
+    for (uint32_t kt = 0; kt < nk; ++kt) {
+        const uint32_t slot = kt % S;
+#pragma unroll
+        for (uint32_t kk = 0; kk < KK; ++kk) {
             const uint32_t cur = kk & 1u;
-            if (kk + 1 < BK / 16) load_frags(kk + 1, fa[cur ^ 1u], fb[cur ^ 1u]);
+            if (kk + 1 < KK) {
+                load_frags(slot, kk + 1, fa[cur ^ 1u], fb[cur ^ 1u]);
+            } else if (kt + 1 < nk) {
+                const uint32_t later = nk - 2 - kt < (uint32_t)(S - 2) ? nk - 2 - kt : (uint32_t)(S - 2);
+                if constexpr (interior) wait_stage<2 * GPW, S - 2>(later);
+                else wait_vmcnt<0>();
+                wait_lgkm0();
+                wg_barrier();
+                if (kt + S < nk) issue(kt + S);
+                load_frags((kt + 1) % S, 0, fa[cur ^ 1u], fb[cur ^ 1u]);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
