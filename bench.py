@@ -175,8 +175,9 @@ def main():
     ap.add_argument("--pairs", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true")
-    ap.add_argument("--only", choices=["copy", "gemm"], default="copy",
-                    help="gemm: time only the GEMM mainloop (profiling runs)")
+    ap.add_argument("--only", choices=["copy", "gemm", "lds-probe"], default="copy",
+                    help="gemm: time only the GEMM mainloop; lds-probe: run the LDS bank probe "
+                         "layouts (profiling runs)")
     ap.add_argument("--gemm-variant", default="all",
                     help="bk,stages[,k256] e.g. 32,4,k256 (with --only gemm)")
     ap.add_argument("--ref-copy", action="store_true",
@@ -198,6 +199,16 @@ def main():
     att.lib()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream().cuda_stream
+    if args.only == "lds-probe":
+        # one dispatch per layout: the pages' grouped / 256-byte-stride sector
+        # reads (0, 1) and an MFMA 32x32 operand fragment under 128B (2) and
+        # 128B_K256 (3), each read 1000 times for the LDS counters
+        h = torch.zeros(9 * 16 * 8, dtype=torch.int32, device="cuda")
+        for layout in range(4):
+            att.lds_bank_probe(layout, 1000, h.data_ptr(), stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"lds_probe_layouts": 4, "iters": 1000}), flush=True)
+        return
     if args.only == "gemm":
         variants = GEMM_VARIANTS
         if args.gemm_variant != "all":
