@@ -39,7 +39,8 @@ struct GemmArgs {
     uint32_t M, N, K, ldc;
     uint32_t tiles_m, tiles_n;
     uint32_t group_m;    // tile rows per rasterisation group
-    uint32_t xcd;        // renumber workgroups per XCD
+    uint32_t xcd;        // 0: plain order, 1: contiguous ranges per XCD, 2: a 2-D block of tiles per XCD
+    uint32_t blk_m, blk_n;   // xcd == 2: tile rows / columns of each XCD's block
 };
 
 // Tile (tm, tn) of workgroup b: groups of `group_m` tile rows are walked
@@ -74,9 +75,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t lane = lane_id();
     const uint32_t G = gridDim.x;
-    const uint32_t bid = g.xcd ? (blockIdx.x % 8u) * (G / 8u) + blockIdx.x / 8u : blockIdx.x;
     uint32_t tm, tn;
-    gemm_tile_of(g, bid, tm, tn);
+    if (g.xcd == 2) {
+        // Workgroups are dispatched round-robin over the 8 XCDs: XCD x owns a
+        // blk_m x blk_n block of C tiles (blocks 2 wide in n), walked in
+        // groups of group_m tile rows, so its L2 serves blk_m A panels and
+        // blk_n B panels instead of whole tile rows.
+        const uint32_t x = blockIdx.x % 8u, local = blockIdx.x / 8u;
+        const uint32_t bm0 = (x >> 1) * g.blk_m, bn0 = (x & 1u) * g.blk_n;
+        const uint32_t gm = g.group_m < g.blk_m ? g.group_m : g.blk_m;
+        const uint32_t per = gm * g.blk_n;
+        const uint32_t grp = local / per, in = local % per;
+        tm = bm0 + grp * gm + in % gm;
+        tn = bn0 + in / gm;
+    } else {
+        const uint32_t bid = g.xcd ? (blockIdx.x % 8u) * (G / 8u) + blockIdx.x / 8u : blockIdx.x;
+        gemm_tile_of(g, bid, tm, tn);
+    }
     const uint32_t m0 = tm * kTM, n0 = tn * kTN;
     const uint32_t nk = (g.K + BK - 1) / BK;
     constexpr bool interior = !EDGE;
@@ -130,23 +145,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     const uint32_t khalf = lane >> 5;
 
     constexpr uint32_t KK = BK / 16;                  // MFMA sub-steps per stage
-    // Fragment reads for sub-step kk of the tile held in ring slot `slot`.
+    // Fragment reads for sub-step kk of the tile held in ring slot `slot`,
+    // addressed with 32-bit LDS offsets (row base and XOR key per fragment
+    // row are loop invariants).
+    typedef __attribute__((address_space(3))) const bf16x8 lds_frag_t;
+    uint32_t rbA[4], kyA[4], rbB[4], kyB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t ra = rowA0 + i * 32u, rb = rowB0 + i * 32u;
+        rbA[i] = lds0 + ra * ROWB;
+        kyA[i] = ((ra * ROWB) >> KSH) & ((1u << SW) - 1u);
+        rbB[i] = lds0 + BOX + rb * ROWB;
+        kyB[i] = ((rb * ROWB) >> KSH) & ((1u << SW) - 1u);
+    }
     auto load_frags = [&](uint32_t slot, uint32_t kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
-        const uint8_t* sA = smem + slot * STAGE;
-        const uint8_t* sB = sA + BOX;
+        const uint32_t so = slot * STAGE;
         const uint32_t lc = 2u * kk + khalf;          // logical 16-byte chunk of the row
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t row = rowA0 + i * 32u;
-            const uint32_t pc = lc ^ (((row * ROWB) >> KSH) & ((1u << SW) - 1u));
-            a[i] = *reinterpret_cast<const bf16x8*>(sA + row * ROWB + pc * 16u);
-        }
+        for (int i = 0; i < 4; ++i)
+            a[i] = *(lds_frag_t*)(uintptr_t)(rbA[i] + so + ((lc ^ kyA[i]) << 4));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t row = rowB0 + j * 32u;
-            const uint32_t pc = lc ^ (((row * ROWB) >> KSH) & ((1u << SW) - 1u));
-            b[j] = *reinterpret_cast<const bf16x8*>(sB + row * ROWB + pc * 16u);
-        }
+        for (int j = 0; j < 4; ++j)
+            b[j] = *(lds_frag_t*)(uintptr_t)(rbB[j] + so + ((lc ^ kyB[j]) << 4));
     };
 
     // Prologue: all S ring slots in flight; wait for the first.
@@ -159,36 +179,64 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     wg_barrier();
 
     // Main loop.  Fragment registers are double-buffered: the reads for
-    // sub-step kk+1 are issued before the 16 MFMAs of kk (scheduling
-    // barriers pin that order).  During the last sub-step of a tile the wave
-    // has issued every read of that slot, so that is where it waits for the
-    // next tile's copies, joins the workgroup barrier (after which no wave
-    // reads the slot any more), refills the slot with tile kt+S and starts
-    // reading the next tile -- all while the last 16 MFMAs of this tile run.
+    // sub-step kk+1 are interleaved with the 16 MFMAs of kk (one read per two
+    // MFMAs; scheduling-group barriers pin the pattern).  During the last
+    // sub-step of a tile the wave has issued every read of that slot: after
+    // the first half of its MFMAs it waits for the next tile's copies, joins
+    // the workgroup barrier (after which no wave reads the slot any more),
+    // refills the slot with tile kt+S, and reads the next tile's first
+    // fragments between the remaining MFMAs.
     bf16x8 fa[2][4], fb[2][4];
     load_frags(0, 0, fa[0], fb[0]);
+    // MFMAs for accumulator rows [i0, i0 + ni) of sub-step buffer `cur`
+    // (constant bounds after unrolling, so acc stays in registers).
+    auto mfma_rows = [&](uint32_t cur, int i0, int ni) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < i0 || i >= i0 + ni) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+        }
+    };
+    // Accumulator updates stay outside runtime branches (only the copy issue
+    // is conditional), so the 256 accumulator registers never meet a join.
     for (uint32_t kt = 0; kt < nk; ++kt) {
-        const uint32_t slot = kt % S;
+        const uint32_t s = kt % S;
 #pragma unroll
         for (uint32_t kk = 0; kk < KK; ++kk) {
             const uint32_t cur = kk & 1u;
-            if (kk + 1 < KK) {
-                load_frags(slot, kk + 1, fa[cur ^ 1u], fb[cur ^ 1u]);
-            } else if (kt + 1 < nk) {
-                const uint32_t later = nk - 2 - kt < (uint32_t)(S - 2) ? nk - 2 - kt : (uint32_t)(S - 2);
-                if constexpr (interior) wait_stage<2 * GPW, S - 2>(later);
-                else wait_vmcnt<0>();
-                wait_lgkm0();
-                wg_barrier();
-                if (kt + S < nk) issue(kt + S);
-                load_frags((kt + 1) % S, 0, fa[cur ^ 1u], fb[cur ^ 1u]);
+            if constexpr (true) {
+                if (kk + 1 < KK) {
+                    load_frags(s, kk + 1, fa[cur ^ 1u], fb[cur ^ 1u]);
+                    mfma_rows(cur, 0, 4);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    continue;
+                }
             }
+            // last sub-step of the tile
+            mfma_rows(cur, 0, 2);
             __builtin_amdgcn_sched_barrier(0);
+            const uint32_t rem = nk - 1 - kt;             // tiles after this one
+            const uint32_t later = rem == 0 ? 0u : (rem - 1 < (uint32_t)(S - 2) ? rem - 1 : (uint32_t)(S - 2));
+            if constexpr (interior) wait_stage<2 * GPW, S - 2>(later);
+            else wait_vmcnt<0>();
+            wait_lgkm0();
+            wg_barrier();
+            if (kt + S < nk) issue(kt + S);
+            __builtin_amdgcn_sched_barrier(0);
+            load_frags((s + 1) % S, 0, fa[cur ^ 1u], fb[cur ^ 1u]);   // unused after the last tile
+            mfma_rows(cur, 2, 2);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -273,6 +321,13 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
     g.group_m = group_m ? group_m : 8u;
     const uint32_t G = g.tiles_m * g.tiles_n;
     g.xcd = (xcd && G % 8u == 0) ? 1u : 0u;
+    g.blk_m = g.blk_n = 0;
+    if (xcd == 2 && g.tiles_m % 4u == 0 && g.tiles_n % 2u == 0) {
+        g.xcd = 2;                     // 4 x 2 arrangement of XCD blocks
+        g.blk_m = g.tiles_m / 4u;
+        g.blk_n = g.tiles_n / 2u;
+        if (g.group_m > g.blk_m || g.blk_m % g.group_m) g.group_m = g.blk_m;
+    }
     hipStream_t st = as_stream(stream);
     if (bka == 64) {
         if (stages == 2) return launch_gemm<64, 2>(g, swa, st);
@@ -282,6 +337,7 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
     case 2: return launch_gemm<32, 2>(g, swa, st);
     case 3: return launch_gemm<32, 3>(g, swa, st);
     case 4: return launch_gemm<32, 4>(g, swa, st);
+    case 5: return launch_gemm<32, 5>(g, swa, st);
     default: return TMAP_ERR_UNSUPPORTED;
     }
 }

@@ -127,7 +127,7 @@ def run_extra(att, torch, stream, reps: int):
 
 
 GEMM_VARIANTS = ((64, "128b", 2), (32, "64b", 4), (64, "128b_k256", 2), (32, "64b_k256", 3),
-                 (32, "64b_k256", 4))
+                 (32, "64b_k256", 4), (32, "64b_k256", 5))
 
 
 def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS):

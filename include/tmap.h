@@ -247,9 +247,11 @@ tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, u
                       uint32_t K, uint32_t ldc, uint32_t stages, void* stream);
 
 /* gemm_bf16 with tuning knobs: `group_m` tile rows per rasterisation group
- * (0 = 8) and `xcd` (1 = give each XCD a contiguous range of tiles).  Maps
+ * (0 = 8) and `xcd` (0 = plain order, 1 = each XCD a contiguous range of
+ * tiles, 2 = each XCD a 2-D block of tiles in a 4 x 2 arrangement when the
+ * tile grid divides).  Maps
  * with box {32, 256} and TMAP_SWIZZLE_64B or TMAP_SWIZZLE_64B_K256 select the
- * 32-deep K step, for which stages may be 2, 3 or 4; box {64, 256} takes
+ * 32-deep K step, for which stages may be 2 to 5; box {64, 256} takes
  * stages = 2. */
 tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
                          uint32_t K, uint32_t ldc, uint32_t stages, uint32_t group_m, uint32_t xcd,
