@@ -20,6 +20,9 @@
 // (16 lanes x 16 bytes per clock); the _K256 modes' 16-row key removes that.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "host_util.hpp"
 #include "tile_device.hpp"
 #include "tmap.h"
@@ -28,6 +31,8 @@ namespace att {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTM = 256, kTN = 256;
 constexpr int kGemmThreads = 256;
@@ -41,7 +46,73 @@ struct GemmArgs {
     uint32_t group_m;    // tile rows per rasterisation group
     uint32_t xcd;        // 0: plain order, 1: contiguous ranges per XCD, 2: a 2-D block of tiles per XCD
     uint32_t blk_m, blk_n;   // xcd == 2: tile rows / columns of each XCD's block
+    uint32_t c_staged;       // 1: C written back through Cm (LDS image + tile store)
+    TmapImpl Cm;             // C map: dims {N, M}, box {64, 256}, 128B_K256 swizzle
 };
+
+// One iteration of the main loop as a fixed sequence of 16*KK MFMA slots
+// (see the kernel): which MFMA each slot runs, which fragment read follows
+// it, and the lgkmcnt the slot must wait for before its MFMA.  Fragment reads
+// are issued as inline asm (so the compiler's LDS-DMA alias tracking adds no
+// vmcnt waits) and complete in issue order, so the wait is exact.
+template <int KK>
+struct GemmSched {
+    static constexpr int SLOTS = 16 * KK;
+    static constexpr int B_END = 8 + 16 * (KK - 1);
+    // MFMA of slot m: accumulator row i, column j, fragment buffer.
+    static constexpr int mi(int m) { return m < 8 ? 2 + m / 4 : (m < B_END ? ((m - 8) % 16) / 4 : (m - B_END) / 4); }
+    static constexpr int mj(int m) { return m < 8 ? m % 4 : (m < B_END ? (m - 8) % 4 : (m - B_END) % 4); }
+    static constexpr int mbuf(int m) { return m < 8 ? 1 : (m < B_END ? ((m - 8) / 16) & 1 : 1); }
+    // Read order inside a group of eight: A0 and B0..B3 first, since the
+    // following MFMAs start with accumulator row 0.
+    static constexpr int order(int p) { return p == 0 ? 0 : (p <= 4 ? 3 + p : p - 4); }
+    // Fragment (0..3 A, 4..7 B) read after slot m's MFMA, or -1; its sub-step
+    // and buffer.
+    static constexpr int rfrag(int m) {
+        return m < 8 ? order(m) : (m < B_END && ((m - 8) % 2) == 0 ? order(((m - 8) % 16) / 2) : -1);
+    }
+    static constexpr int rkk(int m) { return m < 8 ? 0 : (m - 8) / 16 + 1; }
+    static constexpr int rbuf(int m) { return rkk(m) & 1; }
+    static constexpr int reads_before(int m) {
+        int n = 0;
+        for (int x = 0; x < m; ++x) n += rfrag(x) >= 0;
+        return n;
+    }
+    // Issue index (within the iteration) of the read that filled fragment f
+    // of the buffer slot m consumes; -1 if it was read in an earlier
+    // iteration (complete at the barrier).
+    static constexpr int producer(int m, int f) {
+        for (int x = m - 1; x >= 0; --x)
+            if (rfrag(x) == f && rbuf(x) == mbuf(m)) return reads_before(x);
+        return -1;
+    }
+    // lgkmcnt to wait for before slot m's MFMA, or -1 for none.
+    static constexpr int lgkm(int m) {
+        const int pa = producer(m, mi(m)), pb = producer(m, 4 + mj(m));
+        const int p = pa > pb ? pa : pb;
+        return p < 0 ? -1 : reads_before(m) - p - 1;
+    }
+};
+
+// Slot 8 (first MFMA of sub-step 0) needs A0 and B0, the first two of the
+// eight reads issued in slots 0..7.
+static_assert(GemmSched<2>::lgkm(8) == 6 && GemmSched<4>::lgkm(8) == 6, "schedule");
+static_assert(GemmSched<2>::lgkm(0) == -1 && GemmSched<2>::lgkm(31) >= 0, "schedule");
+
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Tile (tm, tn) of workgroup b: groups of `group_m` tile rows are walked
 // column by column so that concurrently running workgroups share A and B
@@ -112,12 +183,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     const uint64_t baseA = g.A.base + (uint64_t)m0 * g.A.stride[0];
     const uint64_t baseB = g.B.base + (uint64_t)n0 * g.B.stride[0];
 
-    auto issue = [&](uint32_t kt) {
-        uint8_t* st = smem + (kt % S) * STAGE;
+    // Whole-tile issue (prologue, and every copy of the general loader).
+    auto issue = [&](uint32_t kt, uint32_t slot) {
+        uint8_t* st = smem + slot * STAGE;
         if constexpr (interior) {
             const uint64_t ka = baseA + (uint64_t)kt * ROWB;
             const uint64_t kb = baseB + (uint64_t)kt * ROWB;
-            const uint32_t la = lds0 + (kt % S) * STAGE + wave_u * GPW * 1024u;
+            const uint32_t la = lds0 + slot * STAGE + wave_u * GPW * 1024u;
 #pragma unroll
             for (uint32_t j = 0; j < GPW; ++j) dma16_sv(ka, offA[j], la + j * 1024u);
 #pragma unroll
@@ -139,128 +211,184 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const uint32_t wm = wave >> 1, wn = wave & 1;
-    // LDS byte offset of this lane's operand row inside a box, and its XOR key.
-    const uint32_t rowA0 = wm * 128u + (lane & 31u);
-    const uint32_t rowB0 = wn * 128u + (lane & 31u);
     const uint32_t khalf = lane >> 5;
+    constexpr uint32_t KK = BK / 16;                  // MFMA sub-steps per stage (even)
+    static_assert(KK % 2 == 0, "fragment buffer parity assumes an even sub-step count");
 
-    constexpr uint32_t KK = BK / 16;                  // MFMA sub-steps per stage
-    // Fragment reads for sub-step kk of the tile held in ring slot `slot`,
-    // addressed with 32-bit LDS offsets (row base and XOR key per fragment
-    // row are loop invariants).
-    typedef __attribute__((address_space(3))) const bf16x8 lds_frag_t;
-    uint32_t rbA[4], kyA[4], rbB[4], kyB[4];
+    // LDS address of fragment f (0..3: A rows wm*128 + f*32 + l%32; 4..7: B)
+    // for sub-step kk, relative to the ring slot: lane l reads logical chunk
+    // 2*kk + l/32 of its row at the physical chunk the swizzle gives.  Loop
+    // invariant, so each read is one add of the slot offset.
+    uint32_t fad[KK][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t ra = rowA0 + i * 32u, rb = rowB0 + i * 32u;
-        rbA[i] = lds0 + ra * ROWB;
-        kyA[i] = ((ra * ROWB) >> KSH) & ((1u << SW) - 1u);
-        rbB[i] = lds0 + BOX + rb * ROWB;
-        kyB[i] = ((rb * ROWB) >> KSH) & ((1u << SW) - 1u);
-    }
-    auto load_frags = [&](uint32_t slot, uint32_t kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
-        const uint32_t so = slot * STAGE;
-        const uint32_t lc = 2u * kk + khalf;          // logical 16-byte chunk of the row
+    for (uint32_t kk = 0; kk < KK; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a[i] = *(lds_frag_t*)(uintptr_t)(rbA[i] + so + ((lc ^ kyA[i]) << 4));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = *(lds_frag_t*)(uintptr_t)(rbB[j] + so + ((lc ^ kyB[j]) << 4));
-    };
-
-    // Prologue: all S ring slots in flight; wait for the first.
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-        if ((uint32_t)s < nk) issue(s);
-    if constexpr (interior) wait_stage<2 * GPW, S - 1>(nk - 1 < (uint32_t)(S - 1) ? nk - 1 : (uint32_t)(S - 1));
-    else wait_vmcnt<0>();
-    wait_lgkm0();
-    wg_barrier();
-
-    // Main loop.  Fragment registers are double-buffered: the reads for
-    // sub-step kk+1 are interleaved with the 16 MFMAs of kk (one read per two
-    // MFMAs; scheduling-group barriers pin the pattern).  During the last
-    // sub-step of a tile the wave has issued every read of that slot: after
-    // the first half of its MFMAs it waits for the next tile's copies, joins
-    // the workgroup barrier (after which no wave reads the slot any more),
-    // refills the slot with tile kt+S, and reads the next tile's first
-    // fragments between the remaining MFMAs.
-    bf16x8 fa[2][4], fb[2][4];
-    load_frags(0, 0, fa[0], fb[0]);
-    // MFMAs for accumulator rows [i0, i0 + ni) of sub-step buffer `cur`
-    // (constant bounds after unrolling, so acc stays in registers).
-    auto mfma_rows = [&](uint32_t cur, int i0, int ni) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i < i0 || i >= i0 + ni) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+        for (int f = 0; f < 8; ++f) {
+            const uint32_t row = (f < 4 ? wm : wn) * 128u + (uint32_t)(f & 3) * 32u + (lane & 31u);
+            const uint32_t rb = row * ROWB;
+            const uint32_t key = (rb >> KSH) & ((1u << SW) - 1u);
+            fad[kk][f] = lds0 + (f < 4 ? 0u : BOX) + rb + (((2u * kk + khalf) ^ key) << 4);
         }
-    };
-    // Accumulator updates stay outside runtime branches (only the copy issue
-    // is conditional), so the 256 accumulator registers never meet a join.
-    for (uint32_t kt = 0; kt < nk; ++kt) {
-        const uint32_t s = kt % S;
+    bf16x8 fr[2][8];                                  // [sub-step parity][A0..A3, B0..B3]
 #pragma unroll
-        for (uint32_t kk = 0; kk < KK; ++kk) {
-            const uint32_t cur = kk & 1u;
-            if constexpr (true) {
-                if (kk + 1 < KK) {
-                    load_frags(s, kk + 1, fa[cur ^ 1u], fb[cur ^ 1u]);
-                    mfma_rows(cur, 0, 4);
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    continue;
-                }
+    for (int f = 0; f < 8; ++f) fr[1][f] = bf16x8{};
+
+    // One iteration runs from one workgroup barrier to the next:
+    //   phase A: accumulator rows 2-3 of the previous tile's last sub-step
+    //            (fragments already in registers), while reading sub-step 0
+    //            of tile t (8 MFMAs, one read each);
+    //   phase B: sub-steps 0 .. KK-2 of tile t, reading the next sub-step
+    //            (16 MFMAs and 8 reads each);
+    //   phase C: rows 0-1 of tile t's last sub-step (8 MFMAs); then wait for
+    //            tile t+1's copies, and the barrier.
+    // The slot of tile t-1 is free from the start of the iteration (every
+    // wave passed the barrier after its last read of it), so tile t+S-1's
+    // copies go there, spread evenly over the first SPAN MFMAs: the CU's
+    // address unit takes 16 cycles per 1 KiB copy, and issued back to back
+    // they would hold the waves' MFMA streams.  Every MFMA slot is pinned by
+    // a scheduling barrier.  Iteration 0's phase A multiplies zero fragments
+    // into zero accumulators (an exact no-op).
+    constexpr int SLOTS = 16 * (int)KK;              // MFMAs per wave and iteration
+    constexpr int NDMA = 2 * (int)GPW;               // copies per wave and tile
+    constexpr int SPAN = S >= 3 ? SLOTS : (SLOTS * 3) / 8;
+    typedef GemmSched<(int)KK> Sch;
+    auto iteration = [&](auto with_copies, uint32_t t, uint32_t slot_t, uint32_t slot_fill, uint32_t later,
+                         bool wait_next) {
+        constexpr bool COPY = decltype(with_copies)::value;
+        const uint32_t so = slot_t * STAGE;
+        const uint64_t ka = baseA + (uint64_t)(t + S - 1) * ROWB;
+        const uint64_t kb = baseB + (uint64_t)(t + S - 1) * ROWB;
+        const uint32_t la = lds0 + slot_fill * STAGE + wave_u * GPW * 1024u;
+        static_for<SLOTS>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            constexpr int W = Sch::lgkm(m);
+            if constexpr (W >= 0) {
+                wait_lgkm<W>();
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // last sub-step of the tile
-            mfma_rows(cur, 0, 2);
+            constexpr int i = Sch::mi(m), j = Sch::mj(m), buf = Sch::mbuf(m);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[buf][4 + j], fr[buf][i], acc[i][j], 0, 0, 0);
+            constexpr int f = Sch::rfrag(m);
+            if constexpr (f >= 0)
+                fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16(fad[Sch::rkk(m)][f] + so));
+            if constexpr (COPY && interior) {
+                static_for<NDMA>([&](auto cc) {
+                    constexpr int c = decltype(cc)::value;
+                    if constexpr ((c * SPAN) / NDMA == m) {
+                        if constexpr (c < (int)GPW) dma16_sv(ka, offA[c], la + (uint32_t)c * 1024u);
+                        else dma16_sv(kb, offB[c - GPW], la + BOX + (uint32_t)(c - GPW) * 1024u);
+                    }
+                });
+            }
             __builtin_amdgcn_sched_barrier(0);
-            const uint32_t rem = nk - 1 - kt;             // tiles after this one
-            const uint32_t later = rem == 0 ? 0u : (rem - 1 < (uint32_t)(S - 2) ? rem - 1 : (uint32_t)(S - 2));
+        });
+        if (wait_next) {
             if constexpr (interior) wait_stage<2 * GPW, S - 2>(later);
             else wait_vmcnt<0>();
             wait_lgkm0();
             wg_barrier();
-            if (kt + S < nk) issue(kt + S);
-            __builtin_amdgcn_sched_barrier(0);
-            load_frags((s + 1) % S, 0, fa[cur ^ 1u], fb[cur ^ 1u]);   // unused after the last tile
-            mfma_rows(cur, 2, 2);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+
+    // Prologue: tiles 0 .. S-2 in flight; wait for tile 0.
+    const uint32_t pro = nk < (uint32_t)(S - 1) ? nk : (uint32_t)(S - 1);
+    for (uint32_t s = 0; s < pro; ++s) issue(s, s);
+    if constexpr (interior) wait_stage<2 * GPW, S - 2>(pro - 1);
+    else wait_vmcnt<0>();
+    wait_lgkm0();
+    wg_barrier();
+
+    // Iterations whose tile t+S-1 exists copy it into the slot of tile t-1.
+    // The general loader issues whole tiles up front and drains before each
+    // barrier.
+    uint32_t slot_t = 0, slot_fill = S - 1;
+    uint32_t t = 0;
+    const uint32_t nfull = nk >= (uint32_t)S ? nk - (uint32_t)S + 1u : 0u;
+    for (; t < nfull; ++t) {
+        if constexpr (!interior) issue(t + S - 1, slot_fill);
+        iteration(std::integral_constant<bool, true>{}, t, slot_t, slot_fill, (uint32_t)(S - 2), true);
+        slot_fill = slot_t;
+        slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
+    }
+    for (; t < nk; ++t) {
+        // Tiles issued after tile t+1: t+2 .. nk-1.
+        const uint32_t later = nk >= t + 2 ? nk - t - 2 : 0u;
+        iteration(std::integral_constant<bool, false>{}, t, slot_t, slot_fill, later, t + 1 < nk);
+        slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
+    }
+    // Rows 2-3 of the last tile's last sub-step.
+    wait_lgkm0();
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        acc[2 + m / 4][m % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[1][4 + m % 4], fr[1][2 + m / 4],
+                                                                       acc[2 + m / 4][m % 4], 0, 0, 0);
     }
 
-    // Epilogue: fp32 -> bf16 (round to nearest even), masked at the M / N edge.
-    // Accumulator register r of lane l holds row (r/4)*8 + (l/32)*4 + r%4 and
-    // column l%32 of its 32 x 32 tile.
+    // Epilogue.  The MFMAs take B as their first operand, so accumulator
+    // (i, j) holds the transposed 32 x 32 tile: register r of lane l is C row
+    // i*32 + l%32 of the wave's block and column j*32 + (r/4)*8 + (l/32)*4 +
+    // r%4, i.e. four consecutive columns per group of four registers (8 bytes
+    // of bf16, converted with round-to-nearest-even).
+    const uint32_t rloc = wm * 128u + (lane & 31u);
+    const uint32_t cloc = wn * 128u + khalf * 4u;
+    if (g.c_staged) {
+        // Registers -> LDS -> global, as the pages' epilogue does: the
+        // workgroup's 256 x 256 tile becomes four 256 x 64 box images of the
+        // C map (128-byte rows, 16-row XOR key: the 8-byte writes of rows r
+        // and r+1..r+15 land in distinct bank groups), then every wave writes
+        // boxes back 16 bytes per lane through the tile store, which clips
+        // at the M / N edges.  The ring is free once every wave has passed
+        // this barrier (all fragment reads completed before the last MFMAs).
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) u32x2 lds_u2_t;
+        wg_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t row = rloc + (uint32_t)i * 32u;
+                    const uint32_t col = cloc + (uint32_t)j * 32u + (uint32_t)q * 8u;
+                    const uint32_t chunk = row * 8u + ((col & 63u) >> 3);
+                    const uint32_t addr = lds0 + (col >> 6) * 32768u +
+                                          (swz_chunk(chunk, TMAP_SWIZZLE_128B_K256) << 4) + (col & 7u) * 2u;
+                    const f32x2 lo = {acc[i][j][4 * q], acc[i][j][4 * q + 1]};
+                    const f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    const u32x2 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                                     __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
+                    *(lds_u2_t*)(uintptr_t)addr = v;
+                }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int32_t cc[5] = {(int32_t)(n0 + (uint32_t)b * 64u), (int32_t)m0, 0, 0, 0};
+            tile_store_issue<false>(g.Cm, cc, smem + b * 32768, wave, 4);
+        }
+        return;
+    }
+    // C not 16-byte aligned: element stores, masked at the M / N edge.
     ATT_GLOBAL uint16_t* C = (ATT_GLOBAL uint16_t*)gptr(g.C);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t col = n0 + wn * 128u + j * 32u + (lane & 31u);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const uint32_t row = m0 + wm * 128u + i * 32u + (r / 4) * 8u + khalf * 4u + (r % 4);
-                if (row < g.M && col < g.N) C[(uint64_t)row * g.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t row = m0 + rloc + (uint32_t)i * 32u;
+                const uint32_t col = n0 + cloc + (uint32_t)j * 32u + (uint32_t)q * 8u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (row < g.M && col + e < g.N)
+                        C[(uint64_t)row * g.ldc + col + e] = f32_to_bf16_rne(acc[i][j][4 * q + e]);
             }
-        }
 }
 
 template <int BK, int S, bool EDGE, int SWM>
 static tmap_status launch_gemm_t(const GemmArgs& g, hipStream_t st) {
-    constexpr uint32_t lds = (uint32_t)S * 2u * kTM * BK * 2u;
+    // The ring, or the 128 KiB C staging image if that is larger.
+    constexpr uint32_t ring = (uint32_t)S * 2u * kTM * BK * 2u;
+    constexpr uint32_t lds = ring > 4u * 32768u ? ring : 4u * 32768u;
     uint32_t limit = 0;
     tmap_status s = device_lds_limit(&limit);
     if (s) return s;
@@ -327,6 +455,18 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
         g.blk_m = g.tiles_m / 4u;
         g.blk_n = g.tiles_n / 2u;
         if (g.group_m > g.blk_m || g.blk_m % g.group_m) g.group_m = g.blk_m;
+    }
+    g.c_staged = 0;
+    if ((reinterpret_cast<uintptr_t>(d_C) & 15u) == 0 && ldc % 8u == 0) {
+        tmap_t cm;
+        const uint64_t cdim[2] = {N, M};
+        const uint64_t cstride[1] = {(uint64_t)ldc * 2u};
+        const uint32_t cbox[2] = {64u, (uint32_t)kTM};
+        if (tmap_encode(&cm, TMAP_BF16, 2, d_C, cdim, cstride, cbox, nullptr, TMAP_SWIZZLE_128B_K256,
+                        TMAP_OOB_ZERO) == TMAP_OK) {
+            g.Cm = load_map(&cm);
+            g.c_staged = 1;
+        }
     }
     hipStream_t st = as_stream(stream);
     if (bka == 64) {

@@ -260,39 +260,40 @@ __device__ __forceinline__ void atomic_add_g(gbyte* dst, T v) {
     __hip_atomic_fetch_add((ATT_GLOBAL T*)dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void reduce_add_element(uint8_t dtype, gbyte* dst, const uint8_t* src) {
+// Element `bits` (the low esize bytes hold it) added into dst.
+__device__ __forceinline__ void reduce_add_element(uint8_t dtype, gbyte* dst, uint64_t bits) {
     switch (dtype) {
     case TMAP_U32: case TMAP_I32:
-        atomic_add_g<uint32_t>(dst, *reinterpret_cast<const uint32_t*>(src));
+        atomic_add_g<uint32_t>(dst, (uint32_t)bits);
         break;
     case TMAP_U64: case TMAP_I64:
-        atomic_add_g<uint64_t>(dst, *reinterpret_cast<const uint64_t*>(src));
+        atomic_add_g<uint64_t>(dst, bits);
         break;
     case TMAP_F32:
-        atomic_add_g<float>(dst, *reinterpret_cast<const float*>(src));
+        atomic_add_g<float>(dst, __builtin_bit_cast(float, (uint32_t)bits));
         break;
     case TMAP_F64:
-        atomic_add_g<double>(dst, *reinterpret_cast<const double*>(src));
+        atomic_add_g<double>(dst, __builtin_bit_cast(double, bits));
         break;
     case TMAP_U8: {
-        const uint32_t v = *src;
+        const uint32_t v = (uint32_t)bits & 0xFFu;
         cas_update_sub(dst, 8, [v](uint32_t cur) { return (cur + v) & 0xFFu; });
         break;
     }
     case TMAP_U16: {
-        const uint32_t v = *reinterpret_cast<const uint16_t*>(src);
+        const uint32_t v = (uint32_t)bits & 0xFFFFu;
         cas_update_sub(dst, 16, [v](uint32_t cur) { return (cur + v) & 0xFFFFu; });
         break;
     }
     case TMAP_BF16: {
-        const float v = bf16_to_f32(*reinterpret_cast<const uint16_t*>(src));
+        const float v = bf16_to_f32((uint16_t)bits);
         cas_update_sub(dst, 16, [v](uint32_t cur) {
             return (uint32_t)f32_to_bf16_rne(bf16_to_f32((uint16_t)cur) + v);
         });
         break;
     }
     case TMAP_F16: {
-        const float v = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(src));
+        const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
         cas_update_sub(dst, 16, [v](uint32_t cur) {
             const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)cur) + v;
             return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
@@ -301,6 +302,17 @@ __device__ __forceinline__ void reduce_add_element(uint8_t dtype, gbyte* dst, co
     }
     default: break;
     }
+}
+
+// The esize bytes at byte offset `off` of a 16-byte chunk (off a multiple of
+// esize), selected with shifts so that no per-lane array is indexed at run
+// time (that would live in scratch memory).
+__device__ __forceinline__ uint64_t chunk_element(const u32x4 v, uint32_t off, uint32_t esize) {
+    const uint32_t w = off >> 2;
+    const uint32_t lo = w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+    if (esize == 8) return ((uint64_t)(w == 0 ? v.y : v.w) << 32) | lo;
+    const uint32_t x = lo >> ((off & 3u) * 8u);
+    return esize == 4 ? x : (esize == 2 ? (x & 0xFFFFu) : (x & 0xFFu));
 }
 
 // Write one box from LDS image `lds` back through the map (inverse swizzle).
@@ -326,21 +338,19 @@ __device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_
             *(ATT_GLOBAL u32x4*)(rowp + L.g0 * m.esize) = v;
             continue;
         }
-        union { u32x4 v; uint8_t b[16]; } u;
-        u.v = v;
         for (int64_t e = 0; e < n_el; ++e) {
             const int64_t g = L.g0 + e * m.es[0];
             if (g < 0 || g >= m.dim[0]) continue;
             gbyte* dst = rowp + g * m.esize;
-            const uint8_t* src = u.b + e * m.esize;
+            const uint64_t bits = chunk_element(v, (uint32_t)e * m.esize, m.esize);
             if (REDUCE) {
-                reduce_add_element(m.dtype, dst, src);
+                reduce_add_element(m.dtype, dst, bits);
             } else {
                 switch (m.esize) {
-                case 1: *dst = *src; break;
-                case 2: *(ATT_GLOBAL uint16_t*)dst = *reinterpret_cast<const uint16_t*>(src); break;
-                case 4: *(ATT_GLOBAL uint32_t*)dst = *reinterpret_cast<const uint32_t*>(src); break;
-                default: *(ATT_GLOBAL uint64_t*)dst = *reinterpret_cast<const uint64_t*>(src); break;
+                case 1: *dst = (uint8_t)bits; break;
+                case 2: *(ATT_GLOBAL uint16_t*)dst = (uint16_t)bits; break;
+                case 4: *(ATT_GLOBAL uint32_t*)dst = (uint32_t)bits; break;
+                default: *(ATT_GLOBAL uint64_t*)dst = bits; break;
                 }
             }
         }

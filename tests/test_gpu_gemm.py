@@ -112,3 +112,29 @@ def test_8192_sampled(bk, stages, k256):
     check_close(C[rows, cols], ref)
     # the unsampled output is finite and was written everywhere
     assert not (C == 0x7FFF).any()
+
+
+@pytest.mark.parametrize("offset,ldc", [(0, 264), (1, 264), (0, 203)])
+def test_c_leading_dimension(offset, ldc):
+    """C written with leading dimension ldc >= N: the LDS-staged tile store
+    (16-byte aligned C, ldc a multiple of 8) and the element-store fallback
+    (offset by one element, or odd ldc) both clip at the M / N edges and leave
+    the padding columns and the bytes around C untouched."""
+    M, N, K = 300, 200, 192
+    say("gemm ldc", offset, ldc)
+    A = synthgen.normal_bf16_bits(56, (M, K))
+    Bt = synthgen.normal_bf16_bits(57, (N, K))
+    Ad = torch.from_numpy(A.view(np.int16)).cuda()
+    Bd = torch.from_numpy(Bt.view(np.int16)).cuda()
+    buf = torch.full((M * ldc + 16,), 0x7FFF, dtype=torch.int16, device="cuda")
+    mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (64, 256), None, "128b_k256")
+    mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (64, 256), None, "128b_k256")
+    att.gemm_bf16(mA, mB, buf.data_ptr() + 2 * offset, M, N, K, ldc, 2, stream())
+    torch.cuda.synchronize()
+    out = buf.cpu().numpy().view(np.uint16)
+    C = out[offset:offset + M * ldc].reshape(M, ldc)
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ref = oracle.gemm_bf16_sample(A, Bt, K, rows.reshape(-1), cols.reshape(-1)).reshape(M, N)
+    check_close(C[:, :N], ref)
+    assert (C[:, N:] == 0x7FFF).all()
+    assert (out[:offset] == 0x7FFF).all() and (out[offset + M * ldc:] == 0x7FFF).all()
