@@ -316,8 +316,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         iteration(std::integral_constant<bool, false>{}, t, slot_t, slot_fill, later, t + 1 < nk);
         slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
     }
-    // Rows 2-3 of the last tile's last sub-step.
+    // Rows 2-3 of the last tile's last sub-step.  The fragments come from
+    // inline-asm reads the compiler believes complete at issue, so nothing
+    // may be scheduled above the wait.
     wait_lgkm0();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         acc[2 + m / 4][m % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[1][4 + m % 4], fr[1][2 + m / 4],
@@ -360,10 +363,42 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
                     *(lds_u2_t*)(uintptr_t)addr = v;
                 }
         __syncthreads();
+        // Box store specialised to the 2-D C map: lane l of wave w handles
+        // logical chunk q = k*256 + w*64 + l of each box (8 rows x 128 bytes
+        // per wave and step, whole cache lines), reads its physical slot
+        // (conflict-free: the key only permutes chunks inside a 128-byte
+        // row), and writes 16 bytes, or element by element where the row
+        // crosses N.  Rows at or past M are skipped.  Every copy has landed
+        // by now, so the reads are ordinary LDS loads whose waits the
+        // compiler places itself.
+        typedef __attribute__((address_space(3))) const u32x4 lds_u4_t;
+        const uint64_t cstride = (uint64_t)g.Cm.stride[0];
+        const uint32_t Mc = (uint32_t)g.Cm.dim[1], Nc = (uint32_t)g.Cm.dim[0];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int32_t cc[5] = {(int32_t)(n0 + (uint32_t)b * 64u), (int32_t)m0, 0, 0, 0};
-            tile_store_issue<false>(g.Cm, cc, smem + b * 32768, wave, 4);
+            u32x4 vs[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t q = (uint32_t)k * 256u + wave * 64u + lane;
+                const uint32_t addr = lds0 + (uint32_t)b * 32768u + (swz_chunk(q, TMAP_SWIZZLE_128B_K256) << 4);
+                vs[k] = *(lds_u4_t*)(uintptr_t)addr;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t q = (uint32_t)k * 256u + wave * 64u + lane;
+                const uint32_t row = m0 + (q >> 3);
+                const uint32_t col = n0 + (uint32_t)b * 64u + (q & 7u) * 8u;
+                const u32x4 v = vs[k];
+                if (row >= Mc || col >= Nc) continue;
+                gbyte* dst = gptr(g.Cm.base + row * cstride + (uint64_t)col * 2u);
+                if (col + 8u <= Nc) {
+                    *(ATT_GLOBAL u32x4*)dst = v;
+                } else {
+#pragma unroll
+                    for (uint32_t e = 0; e < 8; ++e)
+                        if (col + e < Nc) *(ATT_GLOBAL uint16_t*)(dst + 2u * e) = (uint16_t)chunk_element(v, 2u * e, 2u);
+                }
+            }
         }
         return;
     }
