@@ -90,11 +90,12 @@ def lib():
         L.tile_copy_ex.argtypes = [tp, tp, _U32, _U32, _U32, _V]
         L.txbar_selftest.argtypes = [tp, _V, _U32, _V, _V, _V]
         L.lds_bank_probe.argtypes = [_I32, _U32, _V, _V]
+        L.hbm_probe.argtypes = [_I32, _V, _V, ctypes.c_uint64, _V]
         L.gemm_bf16.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
         L.gemm_bf16_ex.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _V]
         for name in ("tmap_encode", "tmap_replace_address", "tmap_query", "tile_load", "tile_store",
                      "tile_reduce_add", "tile_copy", "tile_copy_ex", "txbar_selftest",
-                     "lds_bank_probe", "gemm_bf16", "gemm_bf16_ex"):
+                     "lds_bank_probe", "hbm_probe", "gemm_bf16", "gemm_bf16_ex"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -185,6 +186,12 @@ def tile_copy_ex(src: tmap_t, dst: tmap_t, stages: int = 2, grid: int = 0, varia
 def txbar_selftest(m: tmap_t, d_coords, ntile: int, d_trace, d_lds_image_out, stream=0) -> None:
     _check(lib().txbar_selftest(ctypes.byref(m), _addr(d_coords), int(ntile), _addr(d_trace),
                                 _addr(d_lds_image_out), _addr(stream)), "txbar_selftest")
+
+
+def hbm_probe(kind, d_src, d_dst, nbytes: int, stream=0) -> None:
+    """Streaming HBM probe: kind "read" (0), "write" (1) or "copy" (2)."""
+    k = {"read": 0, "write": 1, "copy": 2}.get(kind, kind)
+    _check(lib().hbm_probe(int(k), _addr(d_src), _addr(d_dst), int(nbytes), _addr(stream)), "hbm_probe")
 
 
 def lds_bank_probe(layout: int, iters: int, d_hist, stream=0) -> None:

@@ -231,6 +231,18 @@ tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, uint32_t nt
  * Errors: NULL, UNSUPPORTED (layout), HIP. */
 tmap_status lds_bank_probe(int32_t layout, uint32_t iters, int32_t* d_hist, void* stream);
 
+/* HBM streaming probe (a measurement aid, not an operation of the pages):
+ * moves `bytes` (a multiple of 16) with plain fully coalesced 16-byte vector
+ * accesses, non-temporal stores, about eight 256-thread workgroups per CU,
+ * so that a benchmark can report what this GPU's memory system delivers to
+ * simple streams beside the tile copy.  kind 0: read d_src only (d_dst is a
+ * sink of at least 4 bytes that may receive one word); kind 1: write d_dst
+ * only (d_src ignored, may be NULL); kind 2: copy d_src -> d_dst.  Device
+ * pointers, 16-byte aligned, caller-owned.  Asynchronous on `stream`.
+ * Errors: NULL, ALIGN, UNSUPPORTED (kind, bytes not a multiple of 16), HIP.
+ * bytes == 0 is a no-op. */
+tmap_status hbm_probe(int32_t kind, const void* d_src, void* d_dst, uint64_t bytes, void* stream);
+
 /* Consumer: bf16 GEMM mainloop C = A * B ([MLC] overview and "TMA in a
  * pipeline"; [H200] section 02 result).  A is M x K row-major (map dims
  * {K, M}), B is K x N column-major (map dims {K, N}), both bf16 with box

@@ -127,3 +127,11 @@ def test_launch_argument_errors_without_gpu():
     with pytest.raises(att.TmapError) as ei:
         att.lds_bank_probe(0, 1, 0)
     assert ei.value.name == "ERR_NULL"
+    # hbm_probe: argument checks come before any HIP call
+    att.hbm_probe("copy", BASE, BASE, 0)
+    for args, name in ((("copy", BASE, BASE, 17), "ERR_UNSUPPORTED"), ((3, BASE, BASE, 16), "ERR_UNSUPPORTED"),
+                       (("copy", 0, BASE, 16), "ERR_NULL"), (("write", 0, 0, 16), "ERR_NULL"),
+                       (("read", BASE, BASE + 8, 16), "ERR_ALIGN")):
+        with pytest.raises(att.TmapError) as ei:
+            att.hbm_probe(*args)
+        assert ei.value.name == name, args
