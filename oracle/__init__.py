@@ -61,6 +61,8 @@ class OrcTxbar(ctypes.Structure):
                 ("pending_bytes", ctypes.c_int64), ("phase", ctypes.c_int32)]
 
 
+REDUCE_OPS = {"add": 0, "min": 1, "max": 2}
+
 _lib = None
 
 
@@ -86,6 +88,7 @@ def lib():
             getattr(L, name).argtypes = [mp, u8p, i32p, u8p]
         for name in ("orc_load_batch", "orc_store_batch", "orc_reduce_add_batch"):
             getattr(L, name).argtypes = [mp, u8p, i32p, ctypes.c_uint32, u8p]
+        L.orc_reduce_minmax_batch.argtypes = [mp, ctypes.c_int, u8p, i32p, ctypes.c_uint32, u8p]
         L.orc_reduce_add_f64_accumulate.argtypes = [mp, P(ctypes.c_double), P(ctypes.c_double),
                                                     i32p, ctypes.c_uint32, u8p]
         tp = P(OrcTxbar)
@@ -187,6 +190,19 @@ class Map:
         assert img.size == c.shape[0] * self.box_bytes()
         lib().orc_reduce_add_batch(ctypes.byref(self.m), _ptr(g, ctypes.c_uint8),
                                    _ptr(c, ctypes.c_int32), c.shape[0], _ptr(img, ctypes.c_uint8))
+
+    def reduce(self, gmem: np.ndarray, coords, images: np.ndarray, op: str = "add") -> None:
+        """Reduce store with op "add", "min" or "max" (boxes in index order)."""
+        if op == "add":
+            self.reduce_add(gmem, coords, images)
+            return
+        assert gmem.flags.c_contiguous
+        c = self._coords(coords)
+        g = gmem.view(np.uint8).reshape(-1)
+        img = np.ascontiguousarray(images).view(np.uint8).reshape(-1)
+        assert img.size == c.shape[0] * self.box_bytes()
+        lib().orc_reduce_minmax_batch(ctypes.byref(self.m), REDUCE_OPS[op], _ptr(g, ctypes.c_uint8),
+                                      _ptr(c, ctypes.c_int32), c.shape[0], _ptr(img, ctypes.c_uint8))
 
     def reduce_add_f64(self, acc: np.ndarray, mag: np.ndarray, coords, images: np.ndarray) -> None:
         """Order-free float64 accumulation of every contribution (in place)."""

@@ -24,6 +24,8 @@
  *   orc_load/store      pinned against an independent NumPy pad-and-slice
  *                       formulation and the worked examples above.
  *   orc_reduce_add      pinned by closed forms (integer wrap, IEEE sums).
+ *   orc_reduce_minmax   pinned by NumPy minimum / maximum / fmin / fmax per
+ *                       type and hand-listed NaN / signed-zero cases.
  *   orc_txbar_*         pinned by [MLC] "waiting for TMA load" 4096-byte trace.
  *   orc_bank_sector_*   pinned by [MLC] "128-byte swizzle grouping" counts.
  *   orc_gemm_*          pinned by exact special cases and a library matmul.
@@ -298,6 +300,90 @@ void orc_reduce_add(const orc_map* m, uint8_t* gmem, const int32_t* coords, cons
     } while (next_k(m, k));
 }
 
+static double element_as_f64(int dtype, const uint8_t* p)
+{
+    switch (dtype) {
+    case ORC_F32: { float v; memcpy(&v, p, 4); return (double)v; }
+    case ORC_F64: { double v; memcpy(&v, p, 8); return v; }
+    case ORC_BF16: { uint16_t v; memcpy(&v, p, 2); return orc_bf16_to_f64(v); }
+    case ORC_F16: { uint16_t v; memcpy(&v, p, 2); return orc_f16_to_f64(v); }
+    default: return 0.0;
+    }
+}
+
+/* ---- min / max reduce ------------------------------------------------------
+ * Readings (the pages name "add, min and the like" without defining them):
+ *   integers compare as their type, signed for I32 / I64, unsigned otherwise;
+ *   floats follow IEEE 754 minNum / maxNum: a NaN operand yields the other
+ *   operand, two NaNs give the type's canonical quiet NaN; -0 is ordered
+ *   below +0; otherwise the chosen operand's bits are kept unchanged
+ *   (subnormals and infinities included).  Under these rules the result does
+ *   not depend on the order in which contributions arrive. */
+static int element_is_nan(int dtype, const uint8_t* p)
+{
+    return is_float(dtype) && isnan(element_as_f64(dtype, p));
+}
+
+/* 1 if a orders strictly below b (both non-NaN floats, or integers). */
+static int element_less(int dtype, const uint8_t* a, const uint8_t* b)
+{
+    switch (dtype) {
+    case ORC_U8: return a[0] < b[0];
+    case ORC_U16: { uint16_t x, y; memcpy(&x, a, 2); memcpy(&y, b, 2); return x < y; }
+    case ORC_U32: { uint32_t x, y; memcpy(&x, a, 4); memcpy(&y, b, 4); return x < y; }
+    case ORC_I32: { int32_t x, y; memcpy(&x, a, 4); memcpy(&y, b, 4); return x < y; }
+    case ORC_U64: { uint64_t x, y; memcpy(&x, a, 8); memcpy(&y, b, 8); return x < y; }
+    case ORC_I64: { int64_t x, y; memcpy(&x, a, 8); memcpy(&y, b, 8); return x < y; }
+    default: {
+        double x = element_as_f64(dtype, a), y = element_as_f64(dtype, b);
+        if (x == 0.0 && y == 0.0) return signbit(x) && !signbit(y);
+        return x < y;
+    }
+    }
+}
+
+static void canonical_nan(int dtype, uint8_t* dst)
+{
+    switch (dtype) {
+    case ORC_F32: { uint32_t v = 0x7FC00000u; memcpy(dst, &v, 4); break; }
+    case ORC_F64: { uint64_t v = 0x7FF8000000000000ull; memcpy(dst, &v, 8); break; }
+    case ORC_BF16: { uint16_t v = 0x7FC0u; memcpy(dst, &v, 2); break; }
+    case ORC_F16: { uint16_t v = 0x7E00u; memcpy(dst, &v, 2); break; }
+    default: break;
+    }
+}
+
+static void minmax_element(int dtype, int op, uint8_t* dst, const uint8_t* src)
+{
+    int es = orc_esize(dtype);
+    int nd = element_is_nan(dtype, dst), ns = element_is_nan(dtype, src);
+    if (nd && ns) { canonical_nan(dtype, dst); return; }
+    if (ns) return;                                   /* keep dst */
+    if (nd) { memcpy(dst, src, (size_t)es); return; }
+    int take_src = op == ORC_RED_MIN ? element_less(dtype, src, dst) : element_less(dtype, dst, src);
+    if (take_src) memcpy(dst, src, (size_t)es);
+}
+
+void orc_reduce_minmax(const orc_map* m, int op, uint8_t* gmem, const int32_t* coords, const uint8_t* lds)
+{
+    int es = orc_esize(m->dtype);
+    uint32_t k[5] = {0, 0, 0, 0, 0};
+    do {
+        uint64_t lin, off;
+        int inb = element_address(m, coords, k, &lin, &off);
+        uint32_t phys = orc_swizzle((uint32_t)(lin * (uint64_t)es), m->swizzle);
+        if (inb) minmax_element(m->dtype, op, gmem + off, lds + phys);
+    } while (next_k(m, k));
+}
+
+void orc_reduce_minmax_batch(const orc_map* m, int op, uint8_t* gmem, const int32_t* coords,
+                             uint32_t nbox, const uint8_t* lds)
+{
+    uint32_t bb = orc_box_bytes(m);
+    for (uint32_t b = 0; b < nbox; ++b)
+        orc_reduce_minmax(m, op, gmem, coords + (size_t)b * (size_t)m->rank, lds + (size_t)b * bb);
+}
+
 void orc_load_batch(const orc_map* m, const uint8_t* gmem, const int32_t* coords,
                     uint32_t nbox, uint8_t* lds)
 {
@@ -320,17 +406,6 @@ void orc_reduce_add_batch(const orc_map* m, uint8_t* gmem, const int32_t* coords
     uint32_t bb = orc_box_bytes(m);
     for (uint32_t b = 0; b < nbox; ++b)
         orc_reduce_add(m, gmem, coords + (size_t)b * (size_t)m->rank, lds + (size_t)b * bb);
-}
-
-static double element_as_f64(int dtype, const uint8_t* p)
-{
-    switch (dtype) {
-    case ORC_F32: { float v; memcpy(&v, p, 4); return (double)v; }
-    case ORC_F64: { double v; memcpy(&v, p, 8); return v; }
-    case ORC_BF16: { uint16_t v; memcpy(&v, p, 2); return orc_bf16_to_f64(v); }
-    case ORC_F16: { uint16_t v; memcpy(&v, p, 2); return orc_f16_to_f64(v); }
-    default: return 0.0;
-    }
 }
 
 void orc_reduce_add_f64_accumulate(const orc_map* m, double* acc, double* mag,

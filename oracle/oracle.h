@@ -84,6 +84,15 @@ void orc_store_batch(const orc_map* m, uint8_t* gmem, const int32_t* coords,
 void orc_reduce_add_batch(const orc_map* m, uint8_t* gmem, const int32_t* coords,
                           uint32_t nbox, const uint8_t* lds);
 
+/* Reduce store with an element-wise operation other than add ([HPC] "TMA
+ * reduce": the write-back may combine with what global memory holds, add,
+ * min and the like).  op: ORC_RED_MIN or ORC_RED_MAX (ORC_RED_ADD is
+ * orc_reduce_add).  Boxes are applied in index order. */
+enum { ORC_RED_ADD = 0, ORC_RED_MIN = 1, ORC_RED_MAX = 2 };
+void orc_reduce_minmax(const orc_map* m, int op, uint8_t* gmem, const int32_t* coords, const uint8_t* lds);
+void orc_reduce_minmax_batch(const orc_map* m, int op, uint8_t* gmem, const int32_t* coords,
+                             uint32_t nbox, const uint8_t* lds);
+
 /* Order-free reference for float reductions.  acc and mag are float64 arrays
  * indexed by (element byte offset from base) / esize; acc must already hold
  * the destination's initial values (and mag their magnitudes).  Every

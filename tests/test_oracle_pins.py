@@ -532,3 +532,165 @@ def test_gemm_sample_identity_and_permutation_exact():
     P[np.arange(K), perm] = 0x3F80
     got = oracle.gemm_bf16_sample(P, Bt, K, rows.reshape(-1), cols.reshape(-1)).reshape(K, 32)
     np.testing.assert_array_equal(got, _bf16_to_np64(Bt).T[perm])
+
+
+# ------------------------------ min / max reduce -----------------------------
+
+_FLOAT_NP = {"f32": np.float32, "f64": np.float64, "f16": np.float16}
+
+
+def _as_f64_values(dtype, bits):
+    """Element values of raw bits as float64 (bf16 through float32)."""
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return bits.view(_FLOAT_NP[dtype]).astype(np.float64)
+
+
+@pytest.mark.parametrize("op", ["min", "max"])
+@pytest.mark.parametrize("dtype", ["u8", "u16", "u32", "i32", "u64", "i64", "f32", "f64", "f16", "bf16"])
+def test_reduce_minmax_single_box_matches_numpy(dtype, op):
+    """One in-bounds box of random bit patterns (floats include NaN, infinities,
+    subnormals and both zeros): integers against NumPy minimum / maximum of the
+    signed or unsigned type, floats against NumPy fmin / fmax (IEEE minNum /
+    maxNum: a NaN operand yields the other one) as values, with two NaNs giving
+    the canonical NaN and -0 ordered below +0."""
+    es = oracle.ESIZE[dtype]
+    dims, strides, box = (64, 12), (64 * es + 16,), (32, 8)
+    if box[0] * es % 16:
+        box = (16, 8)
+    foot = strides[0] * dims[1]
+    dst = synthgen.random_bytes(31 + es, foot)
+    src = synthgen.random_bytes(41 + es, box[0] * box[1] * es)
+    m = oracle.Map(dtype, dims, strides, box, swizzle="none")
+    coords = (8, 3)
+    before = dst.copy()
+    m.reduce(dst, [coords], src, op)
+    v_before, sl = _place(dtype, dims, strides, box, coords, before)
+    v_after, _ = _place(dtype, dims, strides, box, coords, dst)
+    a = np.array(v_before[sl])
+    s = src.view(NP_BITS[es]).reshape(box[1], box[0])
+    got = np.array(v_after[sl])
+    if dtype in ("i32", "i64"):
+        sig = {4: np.int32, 8: np.int64}[es]
+        f = np.minimum if op == "min" else np.maximum
+        np.testing.assert_array_equal(got.view(sig), f(a.view(sig), s.view(sig)))
+    elif dtype in ("u8", "u16", "u32", "u64"):
+        f = np.minimum if op == "min" else np.maximum
+        np.testing.assert_array_equal(got, f(a, s))
+    else:
+        av, sv, gv = _as_f64_values(dtype, a), _as_f64_values(dtype, s), _as_f64_values(dtype, got)
+        f = np.fmin if op == "min" else np.fmax
+        want = f(av, sv)
+        np.testing.assert_array_equal(gv, want)          # NaN == NaN here
+        both_nan = np.isnan(av) & np.isnan(sv)
+        assert (got[both_nan] == NAN_BITS[dtype]).all()
+        assert not np.isnan(gv[~both_nan]).any()
+        # the bits are those of one operand (no canonicalisation of values)
+        assert ((got == a) | (got == s) | both_nan).all()
+    mask = np.ones(foot, dtype=bool)
+    mask_v = np_tensor_view(mask.view(np.uint8), "u8", (dims[0] * es, dims[1]), strides)
+    mask_v[sl[0], coords[0] * es:(coords[0] + box[0]) * es] = False
+    np.testing.assert_array_equal(dst[mask], before[mask])
+
+
+SPECIAL = {
+    # dtype: [(dst bits, src bits, min bits, max bits), ...]
+    "f32": [(0x80000000, 0x00000000, 0x80000000, 0x00000000),      # -0 vs +0
+            (0x00000000, 0x80000000, 0x80000000, 0x00000000),
+            (0x7FC00001, 0x3F800000, 0x3F800000, 0x3F800000),      # NaN vs 1
+            (0x3F800000, 0xFFC00000, 0x3F800000, 0x3F800000),      # 1 vs NaN
+            (0x7FC00001, 0xFFFFFFFF, 0x7FC00000, 0x7FC00000),      # NaN vs NaN
+            (0xFF800000, 0x40400000, 0xFF800000, 0x40400000),      # -inf vs 3
+            (0x00000001, 0x00000000, 0x00000000, 0x00000001),      # smallest subnormal vs +0
+            (0x80000001, 0x00000000, 0x80000001, 0x00000000)],
+    "bf16": [(0x8000, 0x0000, 0x8000, 0x0000), (0x7FC1, 0xBF80, 0xBF80, 0xBF80),
+             (0xFFC0, 0x7F81, 0x7FC0, 0x7FC0), (0x0001, 0x8001, 0x8001, 0x0001)],
+    "f16": [(0x8000, 0x0000, 0x8000, 0x0000), (0x7E01, 0x3C00, 0x3C00, 0x3C00),
+            (0xFE00, 0x7C01, 0x7E00, 0x7E00), (0xFC00, 0x7C00, 0xFC00, 0x7C00)],
+    "f64": [(0x8000000000000000, 0x0, 0x8000000000000000, 0x0),
+            (0x7FF8000000000001, 0x3FF0000000000000, 0x3FF0000000000000, 0x3FF0000000000000),
+            (0x7FF0000000000001, 0xFFF8000000000000, 0x7FF8000000000000, 0x7FF8000000000000)],
+    "i32": [(0xFFFFFFFB, 0x00000003, 0xFFFFFFFB, 0x00000003),      # -5 vs 3 (signed)
+            (0x80000000, 0x7FFFFFFF, 0x80000000, 0x7FFFFFFF)],
+    "u32": [(0xFFFFFFFF, 0x00000001, 0x00000001, 0xFFFFFFFF)],
+    "u8": [(200, 100, 100, 200)],
+    "u16": [(0x8000, 0x7FFF, 0x7FFF, 0x8000)],
+    "i64": [(0xFFFFFFFFFFFFFFFF, 0x1, 0xFFFFFFFFFFFFFFFF, 0x1)],
+    "u64": [(0x8000000000000000, 0x1, 0x1, 0x8000000000000000)],
+}
+
+
+@pytest.mark.parametrize("dtype", sorted(SPECIAL))
+def test_reduce_minmax_special_cases(dtype):
+    """Hand-listed cases of the readings: signed / unsigned compares, -0 < +0,
+    minNum / maxNum NaN handling, canonical NaN from two NaNs, subnormals and
+    infinities kept bit for bit."""
+    es = oracle.ESIZE[dtype]
+    cases = SPECIAL[dtype]
+    n = 16 // es * ((len(cases) * es + 15) // 16)      # whole 16-byte rows
+    nt = NP_BITS[es]
+    for col, op in ((2, "min"), (3, "max")):
+        dst = np.zeros(n, dtype=nt)
+        src = np.zeros(n, dtype=nt)
+        for i, c in enumerate(cases):
+            dst[i], src[i] = c[0], c[1]
+        m = oracle.Map(dtype, (n, 1), (n * es,), (n, 1), swizzle="none")
+        m.reduce(dst, [(0, 0)], src.view(np.uint8), op)
+        for i, c in enumerate(cases):
+            assert int(dst[i]) == c[col], (dtype, op, i, hex(int(dst[i])), hex(c[col]))
+
+
+@pytest.mark.parametrize("op", ["min", "max"])
+@pytest.mark.parametrize("dtype", ["i32", "f32", "bf16"])
+def test_reduce_minmax_overlapping_order_free(dtype, op):
+    """Overlapping boxes: the result is the element-wise min / max over the
+    initial value and every contribution, whatever the box order."""
+    es = oracle.ESIZE[dtype]
+    W_, H_ = 96, 80
+    box = (16, 16)
+    dst0 = synthgen.random_bytes(61, W_ * H_ * es)
+    coords = synthgen.uniform_coords(62, 40, (0, 0), (W_ - 16, H_ - 16))
+    srcs = synthgen.random_bytes(63, 40 * 16 * 16 * es)
+    m = oracle.Map(dtype, (W_, H_), (W_ * es,), box, swizzle="none")
+    d1 = dst0.copy()
+    m.reduce(d1, coords, srcs, op)
+    d2 = dst0.copy()
+    rev = srcs.reshape(40, -1)[::-1].copy().reshape(-1)
+    m.reduce(d2, coords[::-1].copy(), rev, op)
+    np.testing.assert_array_equal(d1, d2)
+    # element-wise over all contributions, computed per element with NumPy
+    nt = NP_BITS[es]
+    grid = dst0.view(nt).reshape(H_, W_)
+    contrib = [[[grid[r, c]] for c in range(W_)] for r in range(H_)]
+    sb = srcs.view(nt).reshape(40, 16, 16)
+    for b in range(40):
+        c0, c1 = coords[b]
+        for r in range(16):
+            for c in range(16):
+                contrib[c1 + r][c0 + c].append(sb[b, r, c])
+    got = d1.view(nt).reshape(H_, W_)
+    for r in range(H_):
+        for c in range(W_):
+            vals = np.array(contrib[r][c], dtype=nt)
+            if len(vals) == 1:                       # no box covers it: untouched
+                assert got[r, c] == vals[0]
+                continue
+            if dtype == "i32":
+                v = vals.view(np.int32)
+                want = (v.min() if op == "min" else v.max())
+                assert got[r, c].view(np.int32) == want
+            else:
+                fv = _as_f64_values(dtype, vals)
+                if np.isnan(fv).all():
+                    assert got[r, c] == NAN_BITS[dtype]
+                    continue
+                f = np.nanmin if op == "min" else np.nanmax
+                w = f(fv)
+                gv = _as_f64_values(dtype, np.array([got[r, c]], dtype=nt))[0]
+                assert gv == w
+                if w == 0.0:
+                    zeros = vals[(fv == 0.0)]
+                    neg = any(int(z) >> (8 * es - 1) for z in zeros)
+                    pos = any(not (int(z) >> (8 * es - 1)) for z in zeros)
+                    want_neg = neg if op == "min" else not pos
+                    assert (int(got[r, c]) >> (8 * es - 1)) == int(want_neg)
