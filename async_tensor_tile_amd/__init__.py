@@ -86,6 +86,7 @@ def lib():
         L.tmap_selftest_divide.restype = ctypes.c_uint64
         for name in ("tile_load", "tile_store", "tile_reduce_add"):
             getattr(L, name).argtypes = [tp, _V, _U32, _V, _V]
+        L.tile_reduce.argtypes = [tp, _I32, _V, _U32, _V, _V]
         L.tile_copy.argtypes = [tp, tp, _U32, _V]
         L.tile_copy_ex.argtypes = [tp, tp, _U32, _U32, _U32, _V]
         L.txbar_selftest.argtypes = [tp, _V, _U32, _V, _V, _V]
@@ -94,7 +95,7 @@ def lib():
         L.gemm_bf16.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
         L.gemm_bf16_ex.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _V]
         for name in ("tmap_encode", "tmap_replace_address", "tmap_query", "tile_load", "tile_store",
-                     "tile_reduce_add", "tile_copy", "tile_copy_ex", "txbar_selftest",
+                     "tile_reduce_add", "tile_reduce", "tile_copy", "tile_copy_ex", "txbar_selftest",
                      "lds_bank_probe", "hbm_probe", "gemm_bf16", "gemm_bf16_ex"):
             getattr(L, name).restype = _I32
         _lib = L
@@ -170,6 +171,18 @@ def tile_store(m: tmap_t, d_coords, nbox: int, d_lds_image_in, stream=0) -> None
 def tile_reduce_add(m: tmap_t, d_coords, nbox: int, d_lds_image_in, stream=0) -> None:
     _check(lib().tile_reduce_add(ctypes.byref(m), _addr(d_coords), int(nbox),
                                  _addr(d_lds_image_in), _addr(stream)), "tile_reduce_add")
+
+
+REDUCE_OPS = {"add": 0, "min": 1, "max": 2}
+
+
+def tile_reduce(m: tmap_t, op, d_coords, nbox: int, d_lds_image_in, stream=0) -> None:
+    """Reduce store with op "add", "min" or "max" (or the TMAP_REDUCE_* value)."""
+    code = REDUCE_OPS.get(op, op) if isinstance(op, str) else int(op)
+    if isinstance(code, str):
+        raise ValueError(f"unknown reduce op {op!r}")
+    _check(lib().tile_reduce(ctypes.byref(m), int(code), _addr(d_coords), int(nbox),
+                             _addr(d_lds_image_in), _addr(stream)), "tile_reduce")
 
 
 def tile_copy(src: tmap_t, dst: tmap_t, stages: int = 2, stream=0) -> None:

@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_generic(CopyArgs 
     wait_vmcnt<0>();
     wait_lgkm0();
     __syncthreads();
-    tile_store_issue<false>(a.dst, c, smem, wave, nwaves);
+    tile_store_issue<ST_STORE>(a.dst, c, smem, wave, nwaves);
 }
 
 template <int GPW, int S, int NB>

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load(TmapImpl m, const i
 }
 
 // Stage the raw image of box b into LDS, then store / reduce it through the map.
-template <bool REDUCE>
+template <int OP>
 __global__ __launch_bounds__(kBatchThreads) void k_tile_store(TmapImpl m, const int32_t* __restrict__ coords,
                                                              const uint8_t* __restrict__ in) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_store(TmapImpl m, const 
     }
     wait_vmcnt<0>();
     __syncthreads();
-    tile_store_issue<REDUCE>(m, c, smem, wave, nwaves);
+    tile_store_issue<OP>(m, c, smem, wave, nwaves);
 }
 
 // Byte-counted barrier self-test: one barrier (arrival count 1) completes
@@ -193,7 +193,7 @@ extern "C" tmap_status tile_load(const tmap_t* m, const int32_t* d_coords, uint3
     return check_launch("tile_load");
 }
 
-template <bool REDUCE>
+template <int OP>
 static tmap_status launch_store(const tmap_t* m, const int32_t* d_coords, uint32_t nbox, const void* d_in,
                                 void* stream, const char* name) {
     if (!m) return TMAP_ERR_NULL;
@@ -201,21 +201,31 @@ static tmap_status launch_store(const tmap_t* m, const int32_t* d_coords, uint32
     if (!d_coords || !d_in) return TMAP_ERR_NULL;
     const TmapImpl t = load_map(m);
     const uint32_t lds = round_up(t.box_bytes, 1024u);
-    tmap_status st = prepare_dynamic_lds((const void*)k_tile_store<REDUCE>, lds);
+    tmap_status st = prepare_dynamic_lds((const void*)k_tile_store<OP>, lds);
     if (st) return st;
-    hipLaunchKernelGGL(k_tile_store<REDUCE>, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), t,
+    hipLaunchKernelGGL(k_tile_store<OP>, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), t,
                        d_coords, static_cast<const uint8_t*>(d_in));
     return check_launch(name);
 }
 
 extern "C" tmap_status tile_store(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
                                   const void* d_lds_image_in, void* stream) {
-    return launch_store<false>(m, d_coords, nbox, d_lds_image_in, stream, "tile_store");
+    return launch_store<ST_STORE>(m, d_coords, nbox, d_lds_image_in, stream, "tile_store");
 }
 
 extern "C" tmap_status tile_reduce_add(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
                                        const void* d_lds_image_in, void* stream) {
-    return launch_store<true>(m, d_coords, nbox, d_lds_image_in, stream, "tile_reduce_add");
+    return launch_store<ST_ADD>(m, d_coords, nbox, d_lds_image_in, stream, "tile_reduce_add");
+}
+
+extern "C" tmap_status tile_reduce(const tmap_t* m, int32_t op, const int32_t* d_coords, uint32_t nbox,
+                                   const void* d_lds_image_in, void* stream) {
+    switch (op) {
+    case TMAP_REDUCE_ADD: return launch_store<ST_ADD>(m, d_coords, nbox, d_lds_image_in, stream, "tile_reduce");
+    case TMAP_REDUCE_MIN: return launch_store<ST_MIN>(m, d_coords, nbox, d_lds_image_in, stream, "tile_reduce");
+    case TMAP_REDUCE_MAX: return launch_store<ST_MAX>(m, d_coords, nbox, d_lds_image_in, stream, "tile_reduce");
+    default: return TMAP_ERR_UNSUPPORTED;
+    }
 }
 
 extern "C" tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, uint32_t ntile,

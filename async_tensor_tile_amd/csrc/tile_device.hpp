@@ -304,6 +304,115 @@ __device__ __forceinline__ void reduce_add_element(uint8_t dtype, gbyte* dst, ui
     }
 }
 
+// What a box store does with each in-bounds element.
+enum : int { ST_STORE = 0, ST_ADD = 1, ST_MIN = 2, ST_MAX = 3 };
+
+// min / max of two floating-point values given as raw bits ([HPC] "TMA
+// reduce" names add and min; the readings): a NaN operand yields the other,
+// two NaNs the canonical quiet NaN, -0 orders below +0, and the winner's
+// bits are returned unchanged.  F is float (f32, or f16 / bf16 widened
+// exactly) or double.
+template <bool MAX, typename F>
+__device__ __forceinline__ bool float_take_new(F cur, F v) {
+    const bool nc = cur != cur, nv = v != v;
+    if (nv) return false;
+    if (nc) return true;
+    const bool v_less = v < cur || (v == cur && v == F(0) && __builtin_signbit(v) && !__builtin_signbit(cur));
+    const bool c_less = cur < v || (v == cur && v == F(0) && __builtin_signbit(cur) && !__builtin_signbit(v));
+    return MAX ? c_less : v_less;
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint8_t dtype, uint32_t h) {
+    return dtype == TMAP_BF16 ? __builtin_bit_cast(float, h << 16)
+                              : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// New bits of a min / max update of `cur` by `v` (both raw, esize bytes).
+template <bool MAX>
+__device__ __forceinline__ uint64_t minmax_bits(uint8_t dtype, uint64_t cur, uint64_t v) {
+    switch (dtype) {
+    case TMAP_F32: {
+        const float a = __builtin_bit_cast(float, (uint32_t)cur), b = __builtin_bit_cast(float, (uint32_t)v);
+        if (a != a && b != b) return 0x7FC00000u;
+        return float_take_new<MAX>(a, b) ? v : cur;
+    }
+    case TMAP_F64: {
+        const double a = __builtin_bit_cast(double, cur), b = __builtin_bit_cast(double, v);
+        if (a != a && b != b) return 0x7FF8000000000000ull;
+        return float_take_new<MAX>(a, b) ? v : cur;
+    }
+    case TMAP_F16: case TMAP_BF16: {
+        const float a = half_bits_to_f32(dtype, (uint32_t)cur), b = half_bits_to_f32(dtype, (uint32_t)v);
+        if (a != a && b != b) return dtype == TMAP_BF16 ? 0x7FC0u : 0x7E00u;
+        return float_take_new<MAX>(a, b) ? v : cur;
+    }
+    case TMAP_U8: case TMAP_U16: case TMAP_U32: case TMAP_U64:
+        return MAX ? (v > cur ? v : cur) : (v < cur ? v : cur);
+    case TMAP_I32: {
+        const int32_t a = (int32_t)(uint32_t)cur, b = (int32_t)(uint32_t)v;
+        return (MAX ? b > a : b < a) ? v : cur;
+    }
+    default: {   // TMAP_I64
+        const int64_t a = (int64_t)cur, b = (int64_t)v;
+        return (MAX ? b > a : b < a) ? v : cur;
+    }
+    }
+}
+
+// Atomic min / max of element `bits` into dst: hardware integer min / max
+// for 32- and 64-bit integers, compare-and-swap otherwise.  A value that
+// would not change memory is not written (min only lowers and max only
+// raises the stored value in the order above, so it never would later).
+template <bool MAX>
+__device__ __forceinline__ void reduce_minmax_element(uint8_t dtype, gbyte* dst, uint64_t bits) {
+    switch (dtype) {
+    case TMAP_I32:
+        if (MAX) __hip_atomic_fetch_max((ATT_GLOBAL int32_t*)dst, (int32_t)(uint32_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else __hip_atomic_fetch_min((ATT_GLOBAL int32_t*)dst, (int32_t)(uint32_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    case TMAP_U32:
+        if (MAX) __hip_atomic_fetch_max((ATT_GLOBAL uint32_t*)dst, (uint32_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else __hip_atomic_fetch_min((ATT_GLOBAL uint32_t*)dst, (uint32_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    case TMAP_I64:
+        if (MAX) __hip_atomic_fetch_max((ATT_GLOBAL int64_t*)dst, (int64_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else __hip_atomic_fetch_min((ATT_GLOBAL int64_t*)dst, (int64_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    case TMAP_U64:
+        if (MAX) __hip_atomic_fetch_max((ATT_GLOBAL uint64_t*)dst, (uint64_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else __hip_atomic_fetch_min((ATT_GLOBAL uint64_t*)dst, (uint64_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    case TMAP_F32: {
+        ATT_GLOBAL uint32_t* w = (ATT_GLOBAL uint32_t*)dst;
+        uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while (true) {
+            const uint32_t nw = (uint32_t)minmax_bits<MAX>(dtype, old, bits);
+            if (nw == old) return;
+            if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+                return;
+        }
+    }
+    case TMAP_F64: {
+        ATT_GLOBAL uint64_t* w = (ATT_GLOBAL uint64_t*)dst;
+        uint64_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while (true) {
+            const uint64_t nw = minmax_bits<MAX>(dtype, old, bits);
+            if (nw == old) return;
+            if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+                return;
+        }
+    }
+    case TMAP_U8:
+        cas_update_sub(dst, 8, [dtype, bits](uint32_t cur) { return (uint32_t)minmax_bits<MAX>(dtype, cur, bits & 0xFFu); });
+        return;
+    default:   // U16, F16, BF16
+        cas_update_sub(dst, 16, [dtype, bits](uint32_t cur) { return (uint32_t)minmax_bits<MAX>(dtype, cur, bits & 0xFFFFu); });
+        return;
+    }
+}
+
 // The esize bytes at byte offset `off` of a 16-byte chunk (off a multiple of
 // esize), selected with shifts so that no per-lane array is indexed at run
 // time (that would live in scratch memory).
@@ -318,8 +427,9 @@ __device__ __forceinline__ uint64_t chunk_element(const u32x4 v, uint32_t off, u
 // Write one box from LDS image `lds` back through the map (inverse swizzle).
 // Lane l of group grp handles logical chunk grp*64 + l so that global writes
 // are in address order; it reads the chunk's physical LDS slot.  Elements
-// outside the tensor are skipped; REDUCE adds atomically instead of storing.
-template <bool REDUCE>
+// outside the tensor are skipped; OP (ST_STORE, ST_ADD, ST_MIN, ST_MAX)
+// stores, or combines atomically with what global memory holds.
+template <int OP>
 __device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_t c[5], const uint8_t* lds,
                                                  uint32_t wave, uint32_t nwaves) {
     const uint32_t lane = lane_id();
@@ -334,7 +444,7 @@ __device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_
         const ChunkLoc L = chunk_locate(m, c, q);
         if (!L.rest_in) continue;
         gbyte* rowp = gptr(m.base + (uint64_t)L.rest_off);
-        if (!REDUCE && fast && L.g0 >= 0 && L.g0 + n_el <= m.dim[0]) {
+        if (OP == ST_STORE && fast && L.g0 >= 0 && L.g0 + n_el <= m.dim[0]) {
             *(ATT_GLOBAL u32x4*)(rowp + L.g0 * m.esize) = v;
             continue;
         }
@@ -343,8 +453,10 @@ __device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_
             if (g < 0 || g >= m.dim[0]) continue;
             gbyte* dst = rowp + g * m.esize;
             const uint64_t bits = chunk_element(v, (uint32_t)e * m.esize, m.esize);
-            if (REDUCE) {
+            if constexpr (OP == ST_ADD) {
                 reduce_add_element(m.dtype, dst, bits);
+            } else if constexpr (OP == ST_MIN || OP == ST_MAX) {
+                reduce_minmax_element<OP == ST_MAX>(m.dtype, dst, bits);
             } else {
                 switch (m.esize) {
                 case 1: *dst = (uint8_t)bits; break;

@@ -122,6 +122,17 @@ def run_extra(att, torch, stream, reps: int):
     ms = timed(lambda: att.tile_reduce_add(mr, rc.data_ptr(), ex["nbox"], srcs.data_ptr(), stream), reps)
     out["reduce_add_i32_pass"] = {"ms": round(ms, 4),
                                   "GBps_algorithmic": round(ex["nbox"] * 16384 * 3 / ms / 1e6, 1)}
+    ms = timed(lambda: att.tile_reduce(mr, "min", rc.data_ptr(), ex["nbox"], srcs.data_ptr(), stream), reps)
+    out["reduce_min_i32_pass"] = {"ms": round(ms, 4),
+                                  "GBps_algorithmic": round(ex["nbox"] * 16384 * 3 / ms / 1e6, 1)}
+    # the pages' reduce example type: bf16 add (compare-and-swap per element)
+    dst16 = torch.from_numpy(synthgen.normal_bf16_bits(ex["seed"], (4096, 4096)).view(np.int16)).cuda()
+    src16 = torch.from_numpy(synthgen.normal_bf16_bits(ex["seed"] * 1000 + 21, (ex["nbox"], 64, 64))
+                             .view(np.int16)).cuda()
+    mb = att.tmap_encode("bf16", 2, dst16.data_ptr(), ex["dims"], (8192,), ex["box"], None, "none")
+    ms = timed(lambda: att.tile_reduce(mb, "add", rc.data_ptr(), ex["nbox"], src16.data_ptr(), stream), reps)
+    out["reduce_add_bf16_pass"] = {"ms": round(ms, 4),
+                                   "GBps_algorithmic": round(ex["nbox"] * 8192 * 3 / ms / 1e6, 1)}
 
     g = run_gemm(att, torch, stream, max(3, reps // 2), variants=(GEMM_DEFAULT,))
     best = g[g["gemm_best"]]

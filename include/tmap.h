@@ -184,6 +184,20 @@ tmap_status tile_store(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
 tmap_status tile_reduce_add(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
                             const void* d_lds_image_in, void* stream);
 
+/* Reduce store with a chosen element-wise operation ([HPC] "TMA reduce":
+ * the write-back combines with what global memory holds, "add, min and the
+ * like").  op TMAP_REDUCE_ADD is tile_reduce_add.  TMAP_REDUCE_MIN / _MAX:
+ * integers compare as their type (signed for I32 / I64, unsigned
+ * otherwise); floating types follow IEEE minNum / maxNum -- a NaN operand
+ * yields the other operand, two NaNs the type's canonical quiet NaN -- with
+ * -0 ordered below +0, and the winning operand's bits are stored unchanged.
+ * Each element update is atomic; min / max results do not depend on the
+ * order of overlapping boxes.  Errors as tile_load, plus UNSUPPORTED for an
+ * unknown op. */
+enum { TMAP_REDUCE_ADD = 0, TMAP_REDUCE_MIN = 1, TMAP_REDUCE_MAX = 2 };
+tmap_status tile_reduce(const tmap_t* m, int32_t op, const int32_t* d_coords, uint32_t nbox,
+                        const void* d_lds_image_in, void* stream);
+
 /* Full-grid round trip: every box of the grid covering `src` (origins at
  * multiples of box[i]) is loaded global->LDS through `src` and stored
  * LDS->global through `dst`, with `stages` LDS buffers per workgroup

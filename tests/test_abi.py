@@ -127,6 +127,14 @@ def test_launch_argument_errors_without_gpu():
     with pytest.raises(att.TmapError) as ei:
         att.lds_bank_probe(0, 1, 0)
     assert ei.value.name == "ERR_NULL"
+    # tile_reduce: unknown op, and NULL pointers, rejected without a HIP call
+    att.tile_reduce(m, "max", 0, 0, 0)
+    with pytest.raises(att.TmapError) as ei:
+        att.tile_reduce(m, 7, BASE, 1, BASE)
+    assert ei.value.name == "ERR_UNSUPPORTED"
+    with pytest.raises(att.TmapError) as ei:
+        att.tile_reduce(m, "min", 0, 2, BASE)
+    assert ei.value.name == "ERR_NULL"
     # hbm_probe: argument checks come before any HIP call
     att.hbm_probe("copy", BASE, BASE, 0)
     for args, name in ((("copy", BASE, BASE, 17), "ERR_UNSUPPORTED"), ((3, BASE, BASE, 16), "ERR_UNSUPPORTED"),

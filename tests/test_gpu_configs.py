@@ -178,3 +178,37 @@ def test_reduce_f32_four_passes_within_tolerance():
     err = np.abs(got - acc)
     assert np.isfinite(got).all()
     assert (err <= 1e-6 * mag).all(), float((err / np.maximum(mag, 1e-300)).max())
+
+
+# ------------------------------ reduce min / max ----------------------------
+
+@pytest.mark.parametrize("op", ["min", "max"])
+@pytest.mark.parametrize("dtype", ["i32", "f32", "bf16", "u16"])
+def test_reduce_minmax_four_passes(dtype, op):
+    """The 4096^2 reduce workload with min / max instead of add: four passes of
+    1024 overlapping 64x64 boxes; integers from the workload's range, floats as
+    random bit patterns (NaNs, infinities, both zeros).  Bit-exact."""
+    ex = W.REDUCE_4096
+    es = {"i32": 4, "f32": 4, "bf16": 2, "u16": 2}[dtype]
+    dims = (4096, 4096)
+    strides = (4096 * es,)
+    box = (64, 64)
+    if dtype == "i32":
+        dst0 = synthgen.int32_range(ex["seed"], (4096, 4096), -(1 << 20), 1 << 20).view(np.uint8).reshape(-1)
+    else:
+        dst0 = synthgen.random_bytes(ex["seed"] * 7 + es, 4096 * 4096 * es)
+    acc = to_dev(dst0)
+    m = att.tmap_encode(dtype, 2, acc.data_ptr(), dims, strides, box, None, "none")
+    om = oracle.Map(dtype, dims, strides, box, swizzle="none")
+    hw = dst0.copy()
+    for p in range(4):
+        say("reduce", op, dtype, "pass", p)
+        coords = synthgen.uniform_coords(ex["seed"] * 1000 + 10 + p, ex["nbox"], (0, 0), (4032, 4032))
+        if dtype == "i32":
+            srcs = synthgen.int32_range(ex["seed"] * 1000 + 20 + p, (ex["nbox"], 64, 64), -(1 << 20), 1 << 20)
+            srcs = srcs.view(np.uint8).reshape(-1)
+        else:
+            srcs = synthgen.random_bytes(ex["seed"] * 1000 + 30 + p, ex["nbox"] * 64 * 64 * es)
+        att.tile_reduce(m, op, to_dev(coords), ex["nbox"], to_dev(srcs), stream())
+        om.reduce(hw, coords, srcs, op)
+    np.testing.assert_array_equal(to_host(acc), hw)

@@ -202,6 +202,16 @@ def test_random_maps_load_store_reduce(seed):
         hw = c.buf.copy()
         oracle.Map(c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle).reduce_add(hw, coords, imgs)
         np.testing.assert_array_equal(to_host(acc)[: c.buf.size], hw)
+    # reduce min / max of random bit patterns (NaNs and signed zeros in the
+    # float types): order-free, bit-exact for every type
+    imgs = synthgen.random_bytes(seed + 11, got.size).reshape(got.shape)
+    for op in ("min", "max"):
+        acc = to_dev(c.buf)
+        ma = encode(acc, c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, "zero")
+        att.tile_reduce(ma, op, to_dev(coords), len(coords), to_dev(imgs), stream())
+        hw = c.buf.copy()
+        oracle.Map(c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle).reduce(hw, coords, imgs, op)
+        np.testing.assert_array_equal(to_host(acc)[: c.buf.size], hw, err_msg=op)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32", "f64"])
