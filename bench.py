@@ -134,7 +134,7 @@ def run_extra(att, torch, stream, reps: int):
     out["reduce_add_bf16_pass"] = {"ms": round(ms, 4),
                                    "GBps_algorithmic": round(ex["nbox"] * 8192 * 3 / ms / 1e6, 1)}
 
-    g = run_gemm(att, torch, stream, max(3, reps // 2), variants=(GEMM_DEFAULT,))
+    g = run_gemm(att, torch, stream, max(3, reps // 2), variants=(GEMM_DEFAULT,), vendor=True)
     best = g[g["gemm_best"]]
     best["roofline"] = {"bound": "mfma", "achieved": best["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(best["TFLOPs"] / BF16_PEAK_TFLOPS, 4), "traffic": None}
@@ -148,7 +148,50 @@ GEMM_DEFAULT = (64, "128b_k256", 2)
 BF16_PEAK_TFLOPS = 2500.0
 
 
-def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS):
+# Tile rasterisations of the GEMM (group_m, xcd): plain row-major tile order,
+# groups of 8 tile rows in dispatch order (neighbouring workgroups land on
+# different XCDs), the same groups with each XCD owning a contiguous range,
+# and each XCD owning a 2-D block of tiles.
+GEMM_RASTERS = ((1, 0), (8, 0), (8, 1), (4, 2), (8, 2))
+
+
+def run_gemm_raster(att, torch, stream, reps: int, rounds: int = 3):
+    """The default GEMM under each rasterisation: median TFLOP/s over
+    `rounds` interleaved rounds.  Under rocprofv3 --pmc the dispatches come
+    round by round in GEMM_RASTERS order, reps + 1 per raster and round."""
+    from synthgen import workloads as W
+
+    ex = W.GEMM_8192
+    M, N, K = ex["M"], ex["N"], ex["K"]
+    g = torch.Generator(device="cuda").manual_seed(ex["seed"])
+    Ad = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
+    Bd = torch.randn(N, K, generator=g, device="cuda").to(torch.bfloat16)
+    Cd = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    bk, sw, stages = GEMM_DEFAULT
+    mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (bk, 256), None, sw)
+    mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (bk, 256), None, sw)
+    times = {r: [] for r in GEMM_RASTERS}
+    for _ in range(rounds):              # rounds interleave the variants against clock drift
+        for gm, xcd in GEMM_RASTERS:
+            fn = lambda: att.gemm_bf16_ex(mA, mB, Cd.data_ptr(), M, N, K, N, stages, gm, xcd, stream)  # noqa: E731
+            fn()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            times[(gm, xcd)].append(s.elapsed_time(e) / reps)
+    out = []
+    for (gm, xcd), t in times.items():
+        ms = sorted(t)[len(t) // 2]
+        out.append({"group_m": gm, "xcd": xcd, "ms_median": round(ms, 4),
+                    "TFLOPs": round(2.0 * M * N * K / ms / 1e9, 1), "ms_all": [round(x, 4) for x in t]})
+    return out
+
+
+def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int = 10, vendor: bool = False):
     """bf16 GEMM mainloop, M = N = K = 8192, A row-major, B column-major,
     N(0,1) operands; 2*M*N*K flop per launch."""
     from synthgen import workloads as W
@@ -164,7 +207,8 @@ def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS):
         mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (bk, 256), None, sw)
         mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (bk, 256), None, sw)
         fn = lambda: att.gemm_bf16(mA, mB, Cd.data_ptr(), M, N, K, N, stages, stream)  # noqa: E731
-        fn()
+        for _ in range(warmup):          # clocks settle under sustained MFMA load
+            fn()
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
@@ -179,6 +223,20 @@ def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS):
         if best is None or tf > best[0]:
             best = (tf, key)
     out["gemm_best"] = best[1]
+    if vendor:
+        # the vendor library on the same operands (torch A @ B^T; context only)
+        Bt = Bd.t()
+        for _ in range(warmup):
+            torch.matmul(Ad, Bt, out=Cd)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            torch.matmul(Ad, Bt, out=Cd)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        out["vendor_gemm_torch_matmul"] = {"ms": round(ms, 4), "TFLOPs": round(2.0 * M * N * K / ms / 1e9, 1)}
     return out
 
 
@@ -225,9 +283,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (rank-5 load, reduce-add pass, GEMM 8192^3)")
-    ap.add_argument("--only", choices=["copy", "gemm", "lds-probe"], default="copy",
-                    help="gemm: time only the GEMM mainloop; lds-probe: run the LDS bank probe "
-                         "layouts (profiling runs)")
+    ap.add_argument("--only", choices=["copy", "gemm", "gemm-raster", "lds-probe"], default="copy",
+                    help="gemm: time only the GEMM mainloop; gemm-raster: the default GEMM under each tile "
+                         "rasterisation; lds-probe: run the LDS bank probe layouts (profiling runs)")
     ap.add_argument("--gemm-variant", default="all",
                     help="bk,stages[,k256] e.g. 32,4,k256 (with --only gemm)")
     ap.add_argument("--ref-copy", action="store_true",
@@ -260,6 +318,11 @@ def main():
             att.lds_bank_probe(layout, 1000, h.data_ptr(), stream)
         torch.cuda.synchronize()
         print(json.dumps({"lds_probe_layouts": 4, "iters": 1000}), flush=True)
+        return
+    if args.only == "gemm-raster":
+        print(json.dumps({"gemm_raster": run_gemm_raster(att, torch, stream, args.steps),
+                          "order": [list(r) for r in GEMM_RASTERS], "rounds": 3,
+                          "dispatches_per_raster_and_round": args.steps + 1}), flush=True)
         return
     if args.only == "gemm":
         variants = GEMM_VARIANTS
