@@ -191,9 +191,13 @@ def run_gemm_raster(att, torch, stream, reps: int, rounds: int = 3):
     return out
 
 
-def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int = 10, vendor: bool = False):
+def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int = 10, vendor: bool = False,
+             rounds: int = 3):
     """bf16 GEMM mainloop, M = N = K = 8192, A row-major, B column-major,
-    N(0,1) operands; 2*M*N*K flop per launch."""
+    N(0,1) operands; 2*M*N*K flop per launch.  Each variant is timed in
+    `rounds` interleaved rounds of `reps` launches (median reported), after
+    `warmup` launches so that clocks have settled under sustained MFMA load.
+    With `vendor`, torch's A @ B^T on the same operands joins the rounds."""
     from synthgen import workloads as W
 
     ex = W.GEMM_8192
@@ -202,73 +206,40 @@ def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int 
     Ad = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
     Bd = torch.randn(N, K, generator=g, device="cuda").to(torch.bfloat16)
     Cd = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    out, best = {}, None
+    fns = {}
+    keep = []
     for bk, sw, stages in variants:
         mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (bk, 256), None, sw)
         mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (bk, 256), None, sw)
-        fn = lambda: att.gemm_bf16(mA, mB, Cd.data_ptr(), M, N, K, N, stages, stream)  # noqa: E731
-        for _ in range(warmup):          # clocks settle under sustained MFMA load
+        keep.append((mA, mB))
+        fns[f"gemm_bf16_8192_bk{bk}_{sw}_s{stages}"] = (
+            lambda mA=mA, mB=mB, stages=stages: att.gemm_bf16(mA, mB, Cd.data_ptr(), M, N, K, N, stages, stream))
+    if vendor:
+        Bt = Bd.t()
+        fns["vendor_gemm_torch_matmul"] = lambda: torch.matmul(Ad, Bt, out=Cd)
+    for fn in fns.values():
+        for _ in range(warmup):
             fn()
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(reps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / reps
+    torch.cuda.synchronize()
+    times = {k: [] for k in fns}
+    for _ in range(rounds):
+        for key, fn in fns.items():
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            times[key].append(s.elapsed_time(e) / reps)
+    out, best = {}, None
+    for key, t in times.items():
+        ms = sorted(t)[len(t) // 2]
         tf = 2.0 * M * N * K / ms / 1e9
-        key = f"gemm_bf16_8192_bk{bk}_{sw}_s{stages}"
         out[key] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1), "pct_of_bf16_peak": round(100 * tf / 2500.0, 2)}
-        if best is None or tf > best[0]:
+        if key.startswith("gemm_") and (best is None or tf > best[0]):
             best = (tf, key)
     out["gemm_best"] = best[1]
-    if vendor:
-        # the vendor library on the same operands (torch A @ B^T; context only)
-        Bt = Bd.t()
-        for _ in range(warmup):
-            torch.matmul(Ad, Bt, out=Cd)
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(reps):
-            torch.matmul(Ad, Bt, out=Cd)
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / reps
-        out["vendor_gemm_torch_matmul"] = {"ms": round(ms, 4), "TFLOPs": round(2.0 * M * N * K / ms / 1e9, 1)}
     return out
-
-
-def hbm_ceiling(att, torch, stream, reps: int = 100):
-    """What plain streaming kernels (the library's hbm_probe: coalesced
-    16-byte loads, non-temporal 16-byte stores) reach on this GPU's HBM with
-    the same 128 MiB working sets, 4 rotating buffers so the last-level cache
-    cannot serve them: read-only, write-only and a linear copy."""
-    n = 8192 * 8192 * 2
-    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255) for _ in range(4)]
-    outs = [torch.empty_like(b) for b in bufs]
-    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-
-    def timed(fn):
-        for k in range(10):
-            fn(k)
-        torch.cuda.synchronize()
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for k in range(reps):
-            fn(k)
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / reps
-
-    r = timed(lambda k: att.hbm_probe("read", bufs[k % 4], sink, n, stream))
-    w = timed(lambda k: att.hbm_probe("write", None, outs[k % 4], n, stream))
-    c = timed(lambda k: att.hbm_probe("copy", bufs[k % 4], outs[k % 4], n, stream))
-    ok = all(torch.equal(a, b) for a, b in zip(bufs, outs))
-    return {"read_only_GBps": round(n / r / 1e6, 1), "write_only_GBps": round(n / w / 1e6, 1),
-            "copy_GBps": round(2 * n / c / 1e6, 1), "copy_verified": ok, "bytes_per_buffer": n,
-            "what": "hbm_probe read / write / copy over 4 rotating 128 MiB buffers"}
 
 
 def main():
