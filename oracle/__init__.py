@@ -63,6 +63,11 @@ class OrcTxbar(ctypes.Structure):
 
 REDUCE_OPS = {"add": 0, "min": 1, "max": 2}
 
+class OrcIm2col(ctypes.Structure):
+    _fields_ = [("t", OrcMap), ("lower", ctypes.c_int32 * 3), ("upper", ctypes.c_int32 * 3),
+                ("channels", ctypes.c_uint32), ("pixels", ctypes.c_uint32)]
+
+
 _lib = None
 
 
@@ -88,6 +93,11 @@ def lib():
             getattr(L, name).argtypes = [mp, u8p, i32p, u8p]
         for name in ("orc_load_batch", "orc_store_batch", "orc_reduce_add_batch"):
             getattr(L, name).argtypes = [mp, u8p, i32p, ctypes.c_uint32, u8p]
+        ip = P(OrcIm2col)
+        L.orc_im2col_validate.argtypes = [ip]
+        L.orc_im2col_box_bytes.argtypes = [ip]
+        L.orc_im2col_box_bytes.restype = ctypes.c_uint32
+        L.orc_im2col_load_batch.argtypes = [ip, u8p, i32p, i32p, ctypes.c_uint32, u8p]
         L.orc_reduce_minmax_batch.argtypes = [mp, ctypes.c_int, u8p, i32p, ctypes.c_uint32, u8p]
         L.orc_reduce_add_f64_accumulate.argtypes = [mp, P(ctypes.c_double), P(ctypes.c_double),
                                                     i32p, ctypes.c_uint32, u8p]
@@ -213,6 +223,58 @@ class Map:
         lib().orc_reduce_add_f64_accumulate(ctypes.byref(self.m), _ptr(acc, ctypes.c_double),
                                             _ptr(mag, ctypes.c_double), _ptr(c, ctypes.c_int32),
                                             c.shape[0], _ptr(img, ctypes.c_uint8))
+
+
+class Im2colMap:
+    """An im2col-mode map: dims (C, W[, H[, D]], N) innermost first, rank 3..5;
+    ``strides`` has rank-1 byte entries; ``lower`` / ``upper`` one entry per
+    spatial dimension; ``estride`` full rank (spatial entries are the
+    convolution strides)."""
+
+    def __init__(self, dtype, dims, strides, lower, upper, channels, pixels, estride=None,
+                 swizzle="none", fill="zero", base_addr=0x1000):
+        rank = len(dims)
+        m = OrcIm2col()
+        t = m.t
+        t.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+        t.rank = rank
+        t.base_addr = base_addr
+        for i, d in enumerate(list(dims)[:5]):
+            t.dim[i] = int(d)
+        for i, st in enumerate(list(strides)[:4]):
+            t.stride[i + 1] = int(st)
+        es = estride if estride is not None else [1] * rank
+        for i, e in enumerate(list(es)[:5]):
+            t.estride[i] = int(e)
+        t.swizzle = SWIZZLES[swizzle] if isinstance(swizzle, str) else int(swizzle)
+        t.fill = FILLS[fill] if isinstance(fill, str) else int(fill)
+        for i, v in enumerate(list(lower)[:3]):
+            m.lower[i] = int(v)
+        for i, v in enumerate(list(upper)[:3]):
+            m.upper[i] = int(v)
+        m.channels = int(channels)
+        m.pixels = int(pixels)
+        self.m = m
+        self.rank = rank
+
+    def validate(self) -> str:
+        return STATUS[lib().orc_im2col_validate(ctypes.byref(self.m))]
+
+    def box_bytes(self) -> int:
+        return lib().orc_im2col_box_bytes(ctypes.byref(self.m))
+
+    def load(self, gmem: np.ndarray, coords, offsets) -> np.ndarray:
+        """LDS images (uint8, nbox x box_bytes); coords nbox x rank, offsets
+        nbox x (rank - 2)."""
+        c = np.ascontiguousarray(np.asarray(coords, dtype=np.int32).reshape(-1, self.rank))
+        o = np.ascontiguousarray(np.asarray(offsets, dtype=np.int32).reshape(-1, self.rank - 2))
+        assert c.shape[0] == o.shape[0]
+        g = np.ascontiguousarray(gmem).view(np.uint8)
+        out = np.zeros((c.shape[0], self.box_bytes()), dtype=np.uint8)
+        lib().orc_im2col_load_batch(ctypes.byref(self.m), _ptr(g.reshape(-1), ctypes.c_uint8),
+                                    _ptr(c, ctypes.c_int32), _ptr(o, ctypes.c_int32), c.shape[0],
+                                    _ptr(out, ctypes.c_uint8))
+        return out
 
 
 def swizzle(offset: int, mode: str) -> int:

@@ -26,6 +26,9 @@
  *   orc_reduce_add      pinned by closed forms (integer wrap, IEEE sums).
  *   orc_reduce_minmax   pinned by NumPy minimum / maximum / fmin / fmax per
  *                       type and hand-listed NaN / signed-zero cases.
+ *   orc_im2col_*        the pages only name im2col encoding: the definition is
+ *                       a reading, pinned against torch's unfold (1-D and
+ *                       2-D convolutions) and a NumPy pad-and-slice 3-D case.
  *   orc_txbar_*         pinned by [MLC] "waiting for TMA load" 4096-byte trace.
  *   orc_bank_sector_*   pinned by [MLC] "128-byte swizzle grouping" counts.
  *   orc_gemm_*          pinned by exact special cases and a library matmul.
@@ -183,6 +186,114 @@ void orc_load(const orc_map* m, const uint8_t* gmem, const int32_t* coords, uint
         if (inb) memcpy(lds + phys, gmem + off, (size_t)es);
         else memcpy(lds + phys, fill, (size_t)es);
     } while (next_k(m, k));
+}
+
+/* ---- im2col mode ------------------------------------------------------------
+ * (see oracle.h for the reading).  Window origins along spatial dimension s
+ * form a grid of n_s positions; a pixel's position is a mixed-radix number
+ * (W digit fastest, image index last) counted from the load's start. */
+
+static int64_t floor_div(int64_t a, int64_t b)
+{
+    int64_t q = a / b;
+    if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+    return q;
+}
+
+static int64_t im2col_positions(const orc_im2col* m, int s)
+{
+    int64_t lo = m->lower[s];
+    int64_t hi = (int64_t)m->t.dim[s + 1] - 1 + (int64_t)m->upper[s];
+    if (hi < lo) return 0;
+    return (hi - lo) / (int64_t)m->t.estride[s + 1] + 1;
+}
+
+int orc_im2col_validate(const orc_im2col* m)
+{
+    if (!m) return ORC_ERR_NULL;
+    const orc_map* t = &m->t;
+    if (t->rank < 3 || t->rank > 5) return ORC_ERR_RANK;
+    int es = orc_esize(t->dtype);
+    if (es == 0) return ORC_ERR_DTYPE;
+    if (t->swizzle < ORC_SW_NONE || t->swizzle > ORC_SW_128B_K256 || t->swizzle == 4) return ORC_ERR_UNSUPPORTED;
+    if (t->fill != ORC_FILL_ZERO && t->fill != ORC_FILL_NAN) return ORC_ERR_UNSUPPORTED;
+    if (t->base_addr == 0) return ORC_ERR_NULL;
+    if (t->base_addr % 16 != 0) return ORC_ERR_ALIGN;
+    for (int d = 0; d < t->rank; ++d)
+        if (t->dim[d] < 1 || t->dim[d] > (1ull << 32)) return ORC_ERR_DIM;
+    for (int d = 1; d < t->rank; ++d)
+        if (t->stride[d] == 0 || t->stride[d] % 16 != 0 || t->stride[d] >= (1ull << 40)) return ORC_ERR_STRIDE;
+    if (m->channels < 1 || m->channels > 256) return ORC_ERR_BOX;
+    if (((uint64_t)m->channels * (uint64_t)es) % 16 != 0) return ORC_ERR_BOX;
+    if (m->pixels < 1 || m->pixels > 1024) return ORC_ERR_BOX;
+    if (t->estride[0] != 1 || t->estride[t->rank - 1] != 1) return ORC_ERR_ESTRIDE;
+    for (int d = 1; d < t->rank - 1; ++d)
+        if (t->estride[d] < 1 || t->estride[d] > 8) return ORC_ERR_ESTRIDE;
+    for (int s = 0; s < t->rank - 2; ++s) {
+        if (m->lower[s] < -32768 || m->lower[s] > 32767) return ORC_ERR_BOX;
+        if (m->upper[s] < -32768 || m->upper[s] > 32767) return ORC_ERR_BOX;
+        if (im2col_positions(m, s) < 1) return ORC_ERR_BOX;
+    }
+    uint32_t row_bytes = m->channels * (uint32_t)es;
+    if (t->swizzle != ORC_SW_NONE && row_bytes != (16u << (t->swizzle & 3))) return ORC_ERR_SWIZZLE_WIDTH;
+    if (t->fill == ORC_FILL_NAN && !is_float(t->dtype)) return ORC_ERR_OOB_FILL_DTYPE;
+    if ((uint64_t)row_bytes * m->pixels > ORC_LDS_CAPACITY) return ORC_ERR_LDS_CAPACITY;
+    return ORC_OK;
+}
+
+uint32_t orc_im2col_box_bytes(const orc_im2col* m)
+{
+    return m->pixels * m->channels * (uint32_t)orc_esize(m->t.dtype);
+}
+
+void orc_im2col_load(const orc_im2col* m, const uint8_t* gmem, const int32_t* coords,
+                     const int32_t* offsets, uint8_t* lds)
+{
+    const orc_map* t = &m->t;
+    int es = orc_esize(t->dtype);
+    int S = t->rank - 2;
+    uint8_t fill[8];
+    fill_bits(t->dtype, t->fill, fill);
+    int64_t npos[3];
+    for (int s = 0; s < S; ++s) npos[s] = im2col_positions(m, s);
+    /* linear index of the start: image index is the most significant digit */
+    int64_t L0 = coords[t->rank - 1];
+    for (int s = S - 1; s >= 0; --s)
+        L0 = L0 * npos[s] + floor_div((int64_t)coords[s + 1] - m->lower[s], (int64_t)t->estride[s + 1]);
+    for (uint32_t p = 0; p < m->pixels; ++p) {
+        int64_t L = L0 + (int64_t)p;
+        int64_t x[3];
+        for (int s = 0; s < S; ++s) {
+            int64_t q = floor_div(L, npos[s]);
+            int64_t digit = L - q * npos[s];
+            x[s] = (int64_t)m->lower[s] + digit * (int64_t)t->estride[s + 1] + (int64_t)offsets[s];
+            L = q;
+        }
+        int64_t img = L;
+        int inb_pix = img >= 0 && (uint64_t)img < t->dim[t->rank - 1];
+        uint64_t pix_off = inb_pix ? (uint64_t)img * t->stride[t->rank - 1] : 0;
+        for (int s = 0; s < S; ++s) {
+            if (x[s] < 0 || (uint64_t)x[s] >= t->dim[s + 1]) inb_pix = 0;
+            else pix_off += (uint64_t)x[s] * t->stride[s + 1];
+        }
+        for (uint32_t k = 0; k < m->channels; ++k) {
+            int64_t ch = (int64_t)coords[0] + (int64_t)k;
+            int inb = inb_pix && ch >= 0 && (uint64_t)ch < t->dim[0];
+            uint32_t phys = orc_swizzle((p * m->channels + k) * (uint32_t)es, t->swizzle);
+            if (inb) memcpy(lds + phys, gmem + pix_off + (uint64_t)ch * (uint64_t)es, (size_t)es);
+            else memcpy(lds + phys, fill, (size_t)es);
+        }
+    }
+}
+
+void orc_im2col_load_batch(const orc_im2col* m, const uint8_t* gmem, const int32_t* coords,
+                           const int32_t* offsets, uint32_t nbox, uint8_t* lds)
+{
+    uint32_t bb = orc_im2col_box_bytes(m);
+    int r = m->t.rank;
+    for (uint32_t b = 0; b < nbox; ++b)
+        orc_im2col_load(m, gmem, coords + (size_t)b * (size_t)r, offsets + (size_t)b * (size_t)(r - 2),
+                        lds + (size_t)b * bb);
 }
 
 /* Store, [HPC] "TMA store": the box's LDS image is written back through the
