@@ -87,6 +87,9 @@ def lib():
         for name in ("tile_load", "tile_store", "tile_reduce_add"):
             getattr(L, name).argtypes = [tp, _V, _U32, _V, _V]
         L.tile_reduce.argtypes = [tp, _I32, _V, _U32, _V, _V]
+        L.tmap_encode_im2col.argtypes = [tp, _I32, _U32, _V, _P(ctypes.c_uint64), _P(ctypes.c_uint64),
+                                         _P(_I32), _P(_I32), _U32, _U32, _P(_U32), _I32, _I32]
+        L.tile_load_im2col.argtypes = [tp, _V, _V, _U32, _V, _V]
         L.tile_copy.argtypes = [tp, tp, _U32, _V]
         L.tile_copy_ex.argtypes = [tp, tp, _U32, _U32, _U32, _V]
         L.txbar_selftest.argtypes = [tp, _V, _U32, _V, _V, _V]
@@ -95,7 +98,7 @@ def lib():
         L.gemm_bf16.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
         L.gemm_bf16_ex.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _V]
         for name in ("tmap_encode", "tmap_replace_address", "tmap_query", "tile_load", "tile_store",
-                     "tile_reduce_add", "tile_reduce", "tile_copy", "tile_copy_ex", "txbar_selftest",
+                     "tile_reduce_add", "tile_reduce", "tmap_encode_im2col", "tile_load_im2col", "tile_copy", "tile_copy_ex", "txbar_selftest",
                      "lds_bank_probe", "hbm_probe", "gemm_bf16", "gemm_bf16_ex"):
             getattr(L, name).restype = _I32
         _lib = L
@@ -142,6 +145,22 @@ def tmap_encode(dtype, rank, gaddr, gdim, gstride, box, estride=None, swizzle="n
     return m
 
 
+def tmap_encode_im2col(dtype, rank, gaddr, gdim, gstride, lower, upper, channels_per_pixel,
+                       pixels_per_column, estride=None, swizzle="none", oob="zero") -> tmap_t:
+    """Encode an im2col-mode map: gdim (C, W[, H[, D]], N) innermost first,
+    lower / upper one corner per spatial dimension.  Raises TmapError."""
+    m = tmap_t()
+    dt = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+    sw = SWIZZLE[swizzle] if isinstance(swizzle, str) else int(swizzle)
+    ob = OOB[oob] if isinstance(oob, str) else int(oob)
+    st = lib().tmap_encode_im2col(ctypes.byref(m), dt, int(rank), _addr(gaddr),
+                                  _arr(ctypes.c_uint64, gdim), _arr(ctypes.c_uint64, gstride),
+                                  _arr(_I32, lower), _arr(_I32, upper), int(channels_per_pixel),
+                                  int(pixels_per_column), _arr(_U32, estride), sw, ob)
+    _check(st, "tmap_encode_im2col")
+    return m
+
+
 def tmap_replace_address(m: tmap_t, gaddr) -> None:
     _check(lib().tmap_replace_address(ctypes.byref(m), _addr(gaddr)), "tmap_replace_address")
 
@@ -161,6 +180,11 @@ def tmap_query(m: tmap_t) -> dict:
 def tile_load(m: tmap_t, d_coords, nbox: int, d_lds_image_out, stream=0) -> None:
     _check(lib().tile_load(ctypes.byref(m), _addr(d_coords), int(nbox), _addr(d_lds_image_out),
                            _addr(stream)), "tile_load")
+
+
+def tile_load_im2col(m: tmap_t, d_coords, d_offsets, nbox: int, d_lds_image_out, stream=0) -> None:
+    _check(lib().tile_load_im2col(ctypes.byref(m), _addr(d_coords), _addr(d_offsets), int(nbox),
+                                  _addr(d_lds_image_out), _addr(stream)), "tile_load_im2col")
 
 
 def tile_store(m: tmap_t, d_coords, nbox: int, d_lds_image_in, stream=0) -> None:

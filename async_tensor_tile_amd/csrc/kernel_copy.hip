@@ -267,6 +267,7 @@ extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32
     CopyArgs a;
     a.src = load_map(src);
     a.dst = load_map(dst);
+    if (is_im2col(a.src) || is_im2col(a.dst)) return TMAP_ERR_UNSUPPORTED;
     if (a.src.dtype != a.dst.dtype || a.src.rank != a.dst.rank || a.src.swizzle != a.dst.swizzle)
         return TMAP_ERR_UNSUPPORTED;
     bool even = true;

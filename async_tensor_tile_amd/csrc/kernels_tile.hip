@@ -48,6 +48,134 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load(TmapImpl m, const i
         *reinterpret_cast<u32x4*>(dst + i * 16u) = *reinterpret_cast<const u32x4*>(smem + i * 16u);
 }
 
+// ---- im2col mode ------------------------------------------------------------
+// Window origins form a mixed-radix number (W digit fastest, image index
+// last); pixel r of a load is the origin r positions after the one its
+// coordinates name (a start between grid points snaps down to the grid).
+
+__device__ __forceinline__ int64_t floor_div64(int64_t a, int64_t b) {
+    int64_t q = a / b;
+    if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+    return q;
+}
+
+// One pixel row: whether the whole pixel (all spatial dims and the image
+// index) lies inside the tensor, and its byte offset without the channel.
+struct PixelLoc {
+    int64_t off;
+    bool in;
+};
+
+__device__ __forceinline__ PixelLoc im2col_pixel(const Im2colImpl& m, int64_t L, const int32_t off[3]) {
+    const int S = m.rank - 2;
+    PixelLoc r;
+    r.off = 0;
+    r.in = true;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        if (s < S) {
+            const int64_t n = (int64_t)m.npos[s];
+            const int64_t q = floor_div64(L, n);
+            const int64_t digit = L - q * n;
+            L = q;
+            const int64_t x = (int64_t)m.lower[s] + digit * (int64_t)m.es[s + 1] + (int64_t)off[s];
+            r.in = r.in && x >= 0 && x < m.dim[s + 1];
+            r.off += x * (int64_t)m.stride[s];
+        }
+    }
+    r.in = r.in && L >= 0 && L < m.dim[m.rank - 1];
+    r.off += L * (int64_t)m.stride[m.rank - 2];
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 im2col_gather_t(const Im2colImpl& m, const PixelLoc& P, int64_t ch0) {
+    constexpr int N = 16 / (int)sizeof(T);
+    union { u32x4 v; T e[N]; } u;
+    const T fillv = *reinterpret_cast<const T*>(g_fill_rows[m.fill_idx]);
+    const ATT_GLOBAL T* row = (const ATT_GLOBAL T*)gptr(m.base + (uint64_t)P.off);
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        const int64_t ch = ch0 + e;
+        const bool in = P.in && ch >= 0 && ch < m.dim[0];
+        u.e[e] = in ? row[ch] : fillv;
+    }
+    return u.v;
+}
+
+__device__ __forceinline__ u32x4 im2col_gather(const Im2colImpl& m, const PixelLoc& P, int64_t ch0) {
+    switch (m.esize) {
+    case 1: return im2col_gather_t<uint8_t>(m, P, ch0);
+    case 2: return im2col_gather_t<uint16_t>(m, P, ch0);
+    case 4: return im2col_gather_t<uint32_t>(m, P, ch0);
+    default: return im2col_gather_t<uint64_t>(m, P, ch0);
+    }
+}
+
+// Load box b of an im2col map into LDS (swizzle on write, byte-counted
+// completion as in the tiled load), then dump the image.  Lane l of group grp
+// fills physical chunk grp*64 + l with logical chunk swz(p): its pixel row and
+// channel block.  Whole in-range, 16-byte aligned chunks and wholly
+// out-of-range chunks (read from the fill row) go through global_load_lds;
+// chunks cut by the channel edge are gathered by their lane.
+__global__ __launch_bounds__(kBatchThreads) void k_tile_load_im2col(Im2colImpl m, const int32_t* __restrict__ coords,
+                                                                   const int32_t* __restrict__ offsets,
+                                                                   uint8_t* __restrict__ out, uint32_t bar_off) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    TxBar* bar = reinterpret_cast<TxBar*>(smem + bar_off);
+    const uint32_t b = blockIdx.x;
+    const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
+    const int R = m.rank, S = R - 2;
+    int32_t c[5] = {0, 0, 0, 0, 0};
+    int32_t off[3] = {0, 0, 0};
+#pragma unroll
+    for (int d = 0; d < 5; ++d)
+        if (d < R) c[d] = coords[(size_t)b * R + d];
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+        if (s < S) off[s] = offsets[(size_t)b * S + s];
+    int64_t L0 = c[R - 1];
+#pragma unroll
+    for (int s = 2; s >= 0; --s)
+        if (s < S)
+            L0 = L0 * (int64_t)m.npos[s] + floor_div64((int64_t)c[s + 1] - m.lower[s], (int64_t)m.es[s + 1]);
+    if (tid == 0) {
+        txbar_init(bar, 1);
+        txbar_arrive_expect_tx(bar, (int32_t)m.box_bytes);
+    }
+    __syncthreads();
+    const uint32_t lane = lane_id();
+    const uint32_t nchunk = m.box_bytes >> 4;
+    const int64_t n_el = 16 / m.esize;
+    const bool aligned = (((int64_t)c[0] * m.esize) & 15) == 0;
+    const void* fill = g_fill_rows[m.fill_idx];
+    uint32_t bytes = 0;
+    for (uint32_t grp = wave; grp * 64u < nchunk; grp += nwaves) {
+        const uint32_t p = grp * 64u + lane;
+        const bool active = p < nchunk;
+        const uint32_t rem = nchunk - grp * 64u;
+        bytes += 16u * (rem < 64u ? rem : 64u);
+        const uint32_t q = active ? swz_chunk(p, m.swizzle) : 0u;
+        const uint32_t row = q / m.cpr;
+        const uint32_t j = q - row * m.cpr;
+        const PixelLoc P = im2col_pixel(m, L0 + (int64_t)row, off);
+        const int64_t ch0 = (int64_t)c[0] + (int64_t)j * n_el;
+        const bool full_in = P.in && ch0 >= 0 && ch0 + n_el <= m.dim[0];
+        const bool full_out = !P.in || ch0 >= m.dim[0] || ch0 + n_el <= 0;
+        const bool partial = !aligned || (!full_in && !full_out);
+        const void* src = full_in ? (const void*)(uintptr_t)(m.base + (uint64_t)P.off + (uint64_t)ch0 * m.esize) : fill;
+        if (active && !partial) dma16(src, smem + grp * 1024u);
+        if (active && partial) *reinterpret_cast<u32x4*>(smem + p * 16u) = im2col_gather(m, P, ch0);
+    }
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    if (lane == 0 && bytes) txbar_complete_tx(bar, (int32_t)bytes);
+    txbar_wait(bar, 0);
+    uint8_t* dst = out + (size_t)b * m.box_bytes;
+    for (uint32_t i = tid; i < nchunk; i += blockDim.x)
+        *reinterpret_cast<u32x4*>(dst + i * 16u) = *reinterpret_cast<const u32x4*>(smem + i * 16u);
+}
+
 // Stage the raw image of box b into LDS, then store / reduce it through the map.
 template <int OP>
 __global__ __launch_bounds__(kBatchThreads) void k_tile_store(TmapImpl m, const int32_t* __restrict__ coords,
@@ -181,9 +309,10 @@ using namespace att;
 extern "C" tmap_status tile_load(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
                                  void* d_lds_image_out, void* stream) {
     if (!m) return TMAP_ERR_NULL;
+    const TmapImpl t = load_map(m);
+    if (is_im2col(t)) return TMAP_ERR_UNSUPPORTED;
     if (nbox == 0) return TMAP_OK;
     if (!d_coords || !d_lds_image_out) return TMAP_ERR_NULL;
-    const TmapImpl t = load_map(m);
     const uint32_t bar_off = round_up(t.box_bytes, 1024u);
     const uint32_t lds = bar_off + 64u;
     tmap_status st = prepare_dynamic_lds((const void*)k_tile_load, lds);
@@ -197,9 +326,10 @@ template <int OP>
 static tmap_status launch_store(const tmap_t* m, const int32_t* d_coords, uint32_t nbox, const void* d_in,
                                 void* stream, const char* name) {
     if (!m) return TMAP_ERR_NULL;
+    const TmapImpl t = load_map(m);
+    if (is_im2col(t)) return TMAP_ERR_UNSUPPORTED;
     if (nbox == 0) return TMAP_OK;
     if (!d_coords || !d_in) return TMAP_ERR_NULL;
-    const TmapImpl t = load_map(m);
     const uint32_t lds = round_up(t.box_bytes, 1024u);
     tmap_status st = prepare_dynamic_lds((const void*)k_tile_store<OP>, lds);
     if (st) return st;
@@ -228,11 +358,29 @@ extern "C" tmap_status tile_reduce(const tmap_t* m, int32_t op, const int32_t* d
     }
 }
 
+extern "C" tmap_status tile_load_im2col(const tmap_t* m, const int32_t* d_coords, const int32_t* d_offsets,
+                                        uint32_t nbox, void* d_lds_image_out, void* stream) {
+    if (!m) return TMAP_ERR_NULL;
+    Im2colImpl t;
+    std::memcpy(&t, m, sizeof(t));
+    if (!(t.oob & OOB_IM2COL_FLAG) || t.rank < 3 || t.rank > 5) return TMAP_ERR_UNSUPPORTED;
+    if (nbox == 0) return TMAP_OK;
+    if (!d_coords || !d_offsets || !d_lds_image_out) return TMAP_ERR_NULL;
+    const uint32_t bar_off = round_up(t.box_bytes, 1024u);
+    const uint32_t lds = bar_off + 64u;
+    tmap_status st = prepare_dynamic_lds((const void*)k_tile_load_im2col, lds);
+    if (st) return st;
+    hipLaunchKernelGGL(k_tile_load_im2col, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), t, d_coords,
+                       d_offsets, static_cast<uint8_t*>(d_lds_image_out), bar_off);
+    return check_launch("tile_load_im2col");
+}
+
 extern "C" tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, uint32_t ntile,
                                       int32_t* d_trace, void* d_lds_image_out, void* stream) {
     if (!m || !d_coords || !d_trace || !d_lds_image_out) return TMAP_ERR_NULL;
     if (ntile < 1 || ntile > 8) return TMAP_ERR_UNSUPPORTED;
     const TmapImpl t = load_map(m);
+    if (is_im2col(t)) return TMAP_ERR_UNSUPPORTED;
     if ((uint64_t)t.box_bytes * ntile > (1u << 30)) return TMAP_ERR_LDS_CAPACITY;
     const uint32_t img_stride = round_up(t.box_bytes, 1024u);
     const uint32_t bar_off = img_stride * ntile;

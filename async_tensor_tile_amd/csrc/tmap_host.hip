@@ -117,6 +117,86 @@ extern "C" tmap_status tmap_encode(tmap_t* out, int32_t dtype, uint32_t rank, vo
     return TMAP_OK;
 }
 
+// Im2col-mode map (see tmap.h for the definition).  Same header checks as the
+// tiled encoder, then the window grid per spatial dimension.
+extern "C" tmap_status tmap_encode_im2col(tmap_t* out, int32_t dtype, uint32_t rank, void* gaddr,
+                                          const uint64_t* gdim, const uint64_t* gstride, const int32_t* lower,
+                                          const int32_t* upper, uint32_t channels, uint32_t pixels,
+                                          const uint32_t* estride, int32_t swizzle, int32_t oob) {
+    if (!out) return TMAP_ERR_NULL;
+    std::memset(out, 0, sizeof(tmap_t));
+    if (!gdim || !gstride || !lower || !upper) return TMAP_ERR_NULL;
+    if (rank < 3 || rank > 5) return TMAP_ERR_RANK;
+    const int es = esize_of(dtype);
+    if (es == 0) return TMAP_ERR_DTYPE;
+    if (swizzle < TMAP_SWIZZLE_NONE || swizzle > TMAP_SWIZZLE_128B_K256 || swizzle == 4) return TMAP_ERR_UNSUPPORTED;
+    if (oob != TMAP_OOB_ZERO && oob != TMAP_OOB_NAN) return TMAP_ERR_UNSUPPORTED;
+    if (!gaddr) return TMAP_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(gaddr) % 16 != 0) return TMAP_ERR_ALIGN;
+    for (uint32_t d = 0; d < rank; ++d)
+        if (gdim[d] < 1 || gdim[d] > (1ull << 32)) return TMAP_ERR_DIM;
+    for (uint32_t d = 1; d < rank; ++d) {
+        const uint64_t st = gstride[d - 1];
+        if (st == 0 || st % 16 != 0 || st >= (1ull << 40)) return TMAP_ERR_STRIDE;
+    }
+    if (channels < 1 || channels > 256 || ((uint64_t)channels * (uint64_t)es) % 16 != 0) return TMAP_ERR_BOX;
+    if (pixels < 1 || pixels > 1024) return TMAP_ERR_BOX;
+    uint32_t esv[5] = {1, 1, 1, 1, 1};
+    for (uint32_t d = 0; d < rank; ++d) esv[d] = estride ? estride[d] : 1u;
+    if (esv[0] != 1 || esv[rank - 1] != 1) return TMAP_ERR_ESTRIDE;
+    for (uint32_t d = 1; d + 1 < rank; ++d)
+        if (esv[d] < 1 || esv[d] > 8) return TMAP_ERR_ESTRIDE;
+    const uint32_t S = rank - 2;
+    uint64_t npos[3] = {1, 1, 1};
+    // the linear window index (image most significant) must fit signed
+    // 64-bit arithmetic
+    unsigned __int128 total = gdim[rank - 1];
+    for (uint32_t sd = 0; sd < S; ++sd) {
+        if (lower[sd] < -32768 || lower[sd] > 32767 || upper[sd] < -32768 || upper[sd] > 32767) return TMAP_ERR_BOX;
+        const int64_t lo = lower[sd];
+        const int64_t hi = (int64_t)gdim[sd + 1] - 1 + (int64_t)upper[sd];
+        if (hi < lo) return TMAP_ERR_BOX;
+        npos[sd] = (uint64_t)((hi - lo) / (int64_t)esv[sd + 1] + 1);
+        total *= npos[sd];
+    }
+    if (total > ((unsigned __int128)1 << 62)) return TMAP_ERR_DIM;
+    const uint32_t row_bytes = channels * (uint32_t)es;
+    if (swizzle != TMAP_SWIZZLE_NONE && row_bytes != (16u << (swizzle & 3))) return TMAP_ERR_SWIZZLE_WIDTH;
+    if (oob == TMAP_OOB_NAN && !is_float(dtype)) return TMAP_ERR_OOB_FILL_DTYPE;
+    if ((uint64_t)row_bytes * pixels > TMAP_LDS_CAPACITY) return TMAP_ERR_LDS_CAPACITY;
+
+    Im2colImpl t;
+    std::memset(&t, 0, sizeof(t));
+    t.base = reinterpret_cast<uint64_t>(gaddr);
+    for (int d = 0; d < 5; ++d) {
+        t.dim[d] = d < (int)rank ? (int64_t)gdim[d] : 1;
+        t.es[d] = (uint8_t)esv[d];
+    }
+    for (int d = 1; d < 5; ++d) t.stride[d - 1] = d < (int)rank ? gstride[d - 1] : 0;
+    for (uint32_t sd = 0; sd < 3; ++sd) {
+        t.lower[sd] = (int16_t)(sd < S ? lower[sd] : 0);
+        t.upper[sd] = (int16_t)(sd < S ? upper[sd] : 0);
+        t.npos[sd] = (uint32_t)npos[sd];
+    }
+    t.rank = (uint8_t)rank;
+    t.dtype = (uint8_t)dtype;
+    t.esize = (uint8_t)es;
+    t.swizzle = (uint8_t)swizzle;
+    t.oob = (uint8_t)(oob | OOB_IM2COL_FLAG);
+    t.fill_idx = FILL_ZERO;
+    if (oob == TMAP_OOB_NAN) {
+        t.fill_idx = dtype == TMAP_F32 ? FILL_NAN_F32
+                   : dtype == TMAP_F16 ? FILL_NAN_F16
+                   : dtype == TMAP_BF16 ? FILL_NAN_BF16 : FILL_NAN_F64;
+    }
+    t.cpr = (uint16_t)(row_bytes / 16);
+    t.box_bytes = row_bytes * pixels;
+    t.channels = (uint16_t)channels;
+    t.pixels = (uint16_t)pixels;
+    std::memcpy(out, &t, sizeof(t));
+    return TMAP_OK;
+}
+
 extern "C" tmap_status tmap_replace_address(tmap_t* m, void* gaddr) {
     if (!m || !gaddr) return TMAP_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(gaddr) % 16 != 0) return TMAP_ERR_ALIGN;
@@ -137,8 +217,16 @@ extern "C" tmap_status tmap_query(const tmap_t* m, tmap_info_t* info) {
     info->rank = t->rank;
     info->esize = t->esize;
     info->swizzle = t->swizzle;
-    info->oob = t->oob;
-    for (int d = 0; d < 5; ++d) info->lds_extent[d] = t->L[d];
+    info->oob = t->oob & (uint8_t)~OOB_IM2COL_FLAG;
+    if (is_im2col(*t)) {
+        Im2colImpl im;
+        std::memcpy(&im, m, sizeof(im));
+        info->lds_extent[0] = im.channels;
+        info->lds_extent[1] = im.pixels;
+        for (int d = 2; d < 5; ++d) info->lds_extent[d] = 1;
+    } else {
+        for (int d = 0; d < 5; ++d) info->lds_extent[d] = t->L[d];
+    }
     info->box_bytes = t->box_bytes;
     info->row_bytes = (uint32_t)t->cpr * 16u;
     info->atom_bytes = t->swizzle ? ((t->swizzle & 4) ? 16u : 8u) * (16u << (t->swizzle & 3)) : 0u;

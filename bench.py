@@ -134,6 +134,26 @@ def run_extra(att, torch, stream, reps: int):
     out["reduce_add_bf16_pass"] = {"ms": round(ms, 4),
                                    "GBps_algorithmic": round(ex["nbox"] * 8192 * 3 / ms / 1e6, 1)}
 
+    # im2col: bf16 NHWC 8 x 56 x 56 x 64, 3 x 3 window, padding 1 -- every tap
+    # over every window in 128-pixel boxes of all 64 channels (128B swizzle)
+    N_, H_, W_, C_, P_ = 8, 56, 56, 64, 128
+    xi = torch.from_numpy(synthgen.normal_bf16_bits(77, (N_, H_, W_, C_)).view(np.int16)).cuda()
+    mi = att.tmap_encode_im2col("bf16", 4, xi.data_ptr(), (C_, W_, H_, N_), (C_ * 2, W_ * C_ * 2, H_ * W_ * C_ * 2),
+                                (-1, -1), (-1, -1), C_, P_, None, "128b")
+    co, of = [], []
+    for L0 in range(0, N_ * H_ * W_, P_):
+        for i in range(3):
+            for j in range(3):
+                co.append((0, -1 + L0 % W_, -1 + (L0 // W_) % H_, L0 // (W_ * H_)))
+                of.append((j, i))
+    cod = torch.from_numpy(np.asarray(co, dtype=np.int32)).cuda()
+    ofd = torch.from_numpy(np.asarray(of, dtype=np.int32)).cuda()
+    imgs = torch.empty(len(co) * P_ * C_ * 2, dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: att.tile_load_im2col(mi, cod.data_ptr(), ofd.data_ptr(), len(co), imgs.data_ptr(), stream),
+               reps)
+    out["im2col_conv3x3_bf16"] = {"ms": round(ms, 4), "boxes": len(co),
+                                  "GBps_lds_image_written": round(len(co) * P_ * C_ * 2 / ms / 1e6, 1)}
+
     g = run_gemm(att, torch, stream, max(3, reps // 2), variants=(GEMM_DEFAULT,), vendor=True)
     best = g[g["gemm_best"]]
     best["roofline"] = {"bound": "mfma", "achieved": best["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

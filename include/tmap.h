@@ -157,6 +157,46 @@ const char* tmap_last_error(void);
 
 /* ---- launches (asynchronous, stream-ordered) ------------------------------ */
 
+/* Im2col-mode tensor map ([HPC] closing paragraph: im2col encoding exists,
+ * with its own swizzle parameter; the pages define nothing further, so the
+ * following is this library's reading).  The tensor is channel-innermost:
+ * gdim = (C, W[, H[, D]], N), rank 3..5, byte strides as for tmap_encode.
+ * Along spatial dimension s (gdim[s+1]) window origins form the grid
+ * lower[s], lower[s] + es, ... up to gdim[s+1] - 1 + upper[s] (lower counted
+ * from the start and upper from the end of the dimension; es = estride[s+1],
+ * the convolution stride).  One load (tile_load_im2col) reads
+ * pixels_per_column consecutive window origins -- W fastest, then H, D and
+ * the image index -- starting at the origin named by its coordinates, and
+ * for each origin channels_per_pixel channels from the channel coordinate
+ * on, at the origin plus the load's per-dimension offsets (the filter tap).
+ * Elements outside the tensor take the OOB fill.  The LDS image is
+ * pixels_per_column rows of channels_per_pixel elements, swizzled like a
+ * tiled box.  Limits: channels_per_pixel 1..256 with channels * esize a
+ * multiple of 16 (equal to the swizzle span when swizzled),
+ * pixels_per_column 1..1024, corners in [-32768, 32767] with a non-empty
+ * grid, estride 1 on C and N and 1..8 on spatial dimensions (NULL = all 1),
+ * at most 2^62 windows in total.  Errors as tmap_encode (ERR_BOX for the
+ * pixel / channel / corner limits, ERR_DIM for the window count).  The
+ * result is a tmap_t usable only with tile_load_im2col (tiled entry points
+ * return ERR_UNSUPPORTED for it); tmap_query reports lds_extent =
+ * {channels, pixels, 1, 1, 1}. */
+tmap_status tmap_encode_im2col(tmap_t* out, int32_t dtype, uint32_t rank, void* gaddr,
+                               const uint64_t* gdim, const uint64_t* gstride_bytes,
+                               const int32_t* lower, const int32_t* upper,
+                               uint32_t channels_per_pixel, uint32_t pixels_per_column,
+                               const uint32_t* estride, int32_t swizzle, int32_t oob);
+
+/* Load nbox im2col boxes and dump each raw LDS image (swizzle included) to
+ * d_lds_image_out + b * tmap_box_bytes(m).  Box b's coordinates are
+ * d_coords[b*rank ..] = (channel, spatial origin..., image) and its
+ * filter-tap offsets d_offsets[b*(rank-2) ..] (int32, one per spatial
+ * dimension, W first); any values are legal (elements outside the tensor
+ * take the fill).  Completion inside the kernel is byte-counted.  Errors:
+ * NULL, UNSUPPORTED (not an im2col map), LDS_CAPACITY, HIP.  nbox == 0 is a
+ * no-op. */
+tmap_status tile_load_im2col(const tmap_t* m, const int32_t* d_coords, const int32_t* d_offsets,
+                             uint32_t nbox, void* d_lds_image_out, void* stream);
+
 /* Load nbox boxes global->LDS and dump each box's raw LDS image.
  * [MLC] "one thread describes the whole tile", "TMA writes swizzled layout";
  * [HPC] single-tile load.  Box b starts at d_coords[b*rank .. b*rank+rank-1]

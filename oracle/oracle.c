@@ -229,11 +229,15 @@ int orc_im2col_validate(const orc_im2col* m)
     if (t->estride[0] != 1 || t->estride[t->rank - 1] != 1) return ORC_ERR_ESTRIDE;
     for (int d = 1; d < t->rank - 1; ++d)
         if (t->estride[d] < 1 || t->estride[d] > 8) return ORC_ERR_ESTRIDE;
+    double windows = (double)t->dim[t->rank - 1];
     for (int s = 0; s < t->rank - 2; ++s) {
         if (m->lower[s] < -32768 || m->lower[s] > 32767) return ORC_ERR_BOX;
         if (m->upper[s] < -32768 || m->upper[s] > 32767) return ORC_ERR_BOX;
         if (im2col_positions(m, s) < 1) return ORC_ERR_BOX;
+        windows *= (double)im2col_positions(m, s);
     }
+    /* a limit of this library: every window has a signed 64-bit linear index */
+    if (windows > 4611686018427387904.0) return ORC_ERR_DIM;   /* 2^62 */
     uint32_t row_bytes = m->channels * (uint32_t)es;
     if (t->swizzle != ORC_SW_NONE && row_bytes != (16u << (t->swizzle & 3))) return ORC_ERR_SWIZZLE_WIDTH;
     if (t->fill == ORC_FILL_NAN && !is_float(t->dtype)) return ORC_ERR_OOB_FILL_DTYPE;

@@ -143,3 +143,69 @@ def test_launch_argument_errors_without_gpu():
         with pytest.raises(att.TmapError) as ei:
             att.hbm_probe(*args)
         assert ei.value.name == name, args
+
+
+# ------------------------------- im2col maps ---------------------------------
+
+IM2COL_CASES = [
+    dict(), dict(channels=6), dict(channels=0), dict(channels=260), dict(pixels=0), dict(pixels=1025),
+    dict(estride=(2, 2, 2, 1)), dict(estride=(1, 9, 2, 1)), dict(estride=(1, 2, 2, 2)),
+    dict(upper=(-12, -1)), dict(lower=(40000, 0)), dict(swizzle="128b"), dict(channels=32, swizzle="128b"),
+    dict(channels=16, swizzle="64b_k256"), dict(dtype="i32", fill="nan"), dict(dtype="bf16", channels=64, fill="nan"),
+    dict(channels=256, pixels=1024), dict(strides=(24, 352, 3168)), dict(strides=(32, 0, 3168)),
+    dict(dims=(8, 11), strides=(32,), lower=(), upper=(), estride=(1, 1)),
+    dict(dims=(8, 11, 2), strides=(32, 352), lower=(-2,), upper=(1,), estride=(1, 3, 1)),
+    dict(dims=(8, 5, 5, 5, 2), strides=(32, 160, 800, 4000), lower=(0, -1, 0), upper=(0, 0, -4),
+         estride=(1, 1, 2, 1, 1)),
+    dict(dims=(8, 1 << 32, 1 << 32, 1 << 32, 4), strides=(32, 1 << 35, 1 << 36, 1 << 37), lower=(0, 0, 0),
+         upper=(0, 0, 0), estride=(1, 1, 1, 1, 1)),
+    dict(dims=(0, 11, 9, 2)), dict(base=BASE + 8),
+]
+
+
+def _im2col_args(**kw):
+    a = dict(dtype="f32", dims=(8, 11, 9, 2), strides=(32, 352, 3168), lower=(-1, -1), upper=(-1, -1),
+             channels=8, pixels=16, estride=(1, 2, 2, 1), swizzle="none", fill="zero", base=BASE)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("case", range(len(IM2COL_CASES)))
+def test_im2col_encode_agrees_with_oracle(case):
+    """The library's im2col encoder accepts and rejects exactly what the
+    oracle's validator does, with the same status."""
+    a = _im2col_args(**IM2COL_CASES[case])
+    om = oracle.Im2colMap(a["dtype"], a["dims"], a["strides"], a["lower"], a["upper"], a["channels"],
+                          a["pixels"], a["estride"], a["swizzle"], a["fill"], base_addr=a["base"])
+    want = om.validate()
+    try:
+        m = att.tmap_encode_im2col(a["dtype"], len(a["dims"]), a["base"], a["dims"], a["strides"], a["lower"],
+                                   a["upper"], a["channels"], a["pixels"], a["estride"], a["swizzle"], a["fill"])
+        got = "OK"
+    except att.TmapError as e:
+        got = e.name
+    assert got == want
+    if got == "OK":
+        q = att.tmap_query(m)
+        assert q["box_bytes"] == om.box_bytes()
+        assert q["lds_extent"] == [a["channels"], a["pixels"], 1, 1, 1]
+
+
+def test_im2col_map_rejected_by_tiled_entry_points():
+    m = att.tmap_encode_im2col("bf16", 4, BASE, (64, 8, 8, 2), (128, 1024, 8192), (-1, -1), (-1, -1), 64, 32,
+                               None, "128b")
+    t = att.tmap_encode("bf16", 2, BASE, (64, 64), (128,), (64, 16), None, "128b")
+    for call in (lambda: att.tile_load(m, BASE, 1, BASE), lambda: att.tile_store(m, BASE, 1, BASE),
+                 lambda: att.tile_reduce(m, "add", BASE, 1, BASE), lambda: att.tile_copy(m, m, 2),
+                 lambda: att.gemm_bf16(m, m, BASE, 256, 256, 64, 256, 2)):
+        with pytest.raises(att.TmapError) as ei:
+            call()
+        assert ei.value.name == "ERR_UNSUPPORTED"
+    # and a tiled map is not an im2col map
+    with pytest.raises(att.TmapError) as ei:
+        att.tile_load_im2col(t, BASE, BASE, 1, BASE)
+    assert ei.value.name == "ERR_UNSUPPORTED"
+    att.tile_load_im2col(m, 0, 0, 0, 0)          # nbox == 0: no-op
+    with pytest.raises(att.TmapError) as ei:
+        att.tile_load_im2col(m, BASE, 0, 1, BASE)
+    assert ei.value.name == "ERR_NULL"
