@@ -96,7 +96,7 @@ def lib():
         L.lds_bank_probe.argtypes = [_I32, _U32, _V, _V]
         L.hbm_probe.argtypes = [_I32, _V, _V, ctypes.c_uint64, _V]
         L.gemm_bf16.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
-        L.gemm_bf16_ex.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _V]
+        L.gemm_bf16_ex.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _V]
         for name in ("tmap_encode", "tmap_replace_address", "tmap_query", "tile_load", "tile_store",
                      "tile_reduce_add", "tile_reduce", "tmap_encode_im2col", "tile_load_im2col", "tile_copy", "tile_copy_ex", "txbar_selftest",
                      "lds_bank_probe", "hbm_probe", "gemm_bf16", "gemm_bf16_ex"):
@@ -243,6 +243,8 @@ def gemm_bf16(A: tmap_t, B: tmap_t, d_C, M: int, N: int, K: int, ldc: int, stage
 
 
 def gemm_bf16_ex(A: tmap_t, B: tmap_t, d_C, M: int, N: int, K: int, ldc: int, stages: int = 2,
-                 group_m: int = 0, xcd: int = 1, stream=0) -> None:
+                 group_m: int = 0, xcd: int = 1, stream=0, mfma: int = 0) -> None:
+    """mfma: 0 default, 16 (16x16x32 tiles) or 32 (32x32x16 tiles)."""
     _check(lib().gemm_bf16_ex(ctypes.byref(A), ctypes.byref(B), _addr(d_C), int(M), int(N), int(K),
-                              int(ldc), int(stages), int(group_m), int(xcd), _addr(stream)), "gemm_bf16_ex")
+                              int(ldc), int(stages), int(group_m), int(xcd), int(mfma), _addr(stream)),
+           "gemm_bf16_ex")

@@ -32,6 +32,7 @@ namespace att {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTM = 256, kTN = 256;
@@ -50,28 +51,40 @@ struct GemmArgs {
     TmapImpl Cm;             // C map: dims {N, M}, box {64, 256}, 128B_K256 swizzle
 };
 
-// One iteration of the main loop as a fixed sequence of 16*KK MFMA slots
-// (see the kernel): which MFMA each slot runs, which fragment read follows
-// it, and the lgkmcnt the slot must wait for before its MFMA.  Fragment reads
-// are issued as inline asm (so the compiler's LDS-DMA alias tracking adds no
-// vmcnt waits) and complete in issue order, so the wait is exact.
-template <int KK>
+// One iteration of the main loop as a fixed sequence of MFMA slots (see the
+// kernel): which MFMA each slot runs, which fragment read follows it, and the
+// lgkmcnt the slot must wait for before its MFMA.  A wave's C block is NI x
+// NJ MFMA tiles; one sub-step (one MFMA K extent) needs NI A and NJ B
+// fragments and runs SUB = NI * NJ MFMAs; an iteration covers KK sub-steps.
+// Fragment reads are issued as inline asm (so the compiler's LDS-DMA alias
+// tracking adds no vmcnt waits) and complete in issue order, so the wait is
+// exact (clamped to the counter's 4 bits, which only waits longer).
+template <int NI, int NJ, int KK>
 struct GemmSched {
-    static constexpr int SLOTS = 16 * KK;
-    static constexpr int B_END = 8 + 16 * (KK - 1);
+    static constexpr int SUB = NI * NJ;
+    static constexpr int HALF = SUB / 2;              // rows NI/2.. of the last sub-step
+    static constexpr int NF = NI + NJ;                // fragments per sub-step
+    static constexpr int RA = HALF / NF;              // read spacing while finishing the previous tile
+    static constexpr int RB = SUB / NF;               // read spacing inside a sub-step
+    static constexpr int SLOTS = SUB * KK;
+    static constexpr int B_END = HALF + SUB * (KK - 1);
+    static_assert(RA >= 1 && RB >= 1 && HALF % NF == 0 && SUB % NF == 0, "read spacing");
     // MFMA of slot m: accumulator row i, column j, fragment buffer.
-    static constexpr int mi(int m) { return m < 8 ? 2 + m / 4 : (m < B_END ? ((m - 8) % 16) / 4 : (m - B_END) / 4); }
-    static constexpr int mj(int m) { return m < 8 ? m % 4 : (m < B_END ? (m - 8) % 4 : (m - B_END) % 4); }
-    static constexpr int mbuf(int m) { return m < 8 ? 1 : (m < B_END ? ((m - 8) / 16) & 1 : 1); }
-    // Read order inside a group of eight: A0 and B0..B3 first, since the
-    // following MFMAs start with accumulator row 0.
-    static constexpr int order(int p) { return p == 0 ? 0 : (p <= 4 ? 3 + p : p - 4); }
-    // Fragment (0..3 A, 4..7 B) read after slot m's MFMA, or -1; its sub-step
-    // and buffer.
-    static constexpr int rfrag(int m) {
-        return m < 8 ? order(m) : (m < B_END && ((m - 8) % 2) == 0 ? order(((m - 8) % 16) / 2) : -1);
+    static constexpr int mi(int m) {
+        return m < HALF ? NI / 2 + m / NJ : (m < B_END ? ((m - HALF) % SUB) / NJ : (m - B_END) / NJ);
     }
-    static constexpr int rkk(int m) { return m < 8 ? 0 : (m - 8) / 16 + 1; }
+    static constexpr int mj(int m) { return m < HALF ? m % NJ : (m < B_END ? (m - HALF) % NJ : (m - B_END) % NJ); }
+    static constexpr int mbuf(int m) { return m < HALF ? 1 : (m < B_END ? ((m - HALF) / SUB) & 1 : 1); }
+    // Read order inside a sub-step: A0 and B0..B(NJ-1) first, since the
+    // following MFMAs start with accumulator row 0; fragment ids 0..NI-1 are
+    // A rows, NI.. B columns.
+    static constexpr int order(int p) { return p == 0 ? 0 : (p <= NJ ? NI + p - 1 : p - NJ); }
+    // Fragment read after slot m's MFMA, or -1; its sub-step and buffer.
+    static constexpr int rfrag(int m) {
+        return m < HALF ? (m % RA == 0 ? order(m / RA) : -1)
+                        : (m < B_END && ((m - HALF) % RB) == 0 ? order(((m - HALF) % SUB) / RB) : -1);
+    }
+    static constexpr int rkk(int m) { return m < HALF ? 0 : (m - HALF) / SUB + 1; }
     static constexpr int rbuf(int m) { return rkk(m) & 1; }
     static constexpr int reads_before(int m) {
         int n = 0;
@@ -88,16 +101,18 @@ struct GemmSched {
     }
     // lgkmcnt to wait for before slot m's MFMA, or -1 for none.
     static constexpr int lgkm(int m) {
-        const int pa = producer(m, mi(m)), pb = producer(m, 4 + mj(m));
+        const int pa = producer(m, mi(m)), pb = producer(m, NI + mj(m));
         const int p = pa > pb ? pa : pb;
-        return p < 0 ? -1 : reads_before(m) - p - 1;
+        const int w = p < 0 ? -1 : reads_before(m) - p - 1;
+        return w > 15 ? 15 : w;
     }
 };
 
-// Slot 8 (first MFMA of sub-step 0) needs A0 and B0, the first two of the
-// eight reads issued in slots 0..7.
-static_assert(GemmSched<2>::lgkm(8) == 6 && GemmSched<4>::lgkm(8) == 6, "schedule");
-static_assert(GemmSched<2>::lgkm(0) == -1 && GemmSched<2>::lgkm(31) >= 0, "schedule");
+// Slot HALF (first MFMA of sub-step 0) needs A0 and B0, the first two of the
+// NF reads issued while the previous tile finishes.
+static_assert(GemmSched<4, 4, 2>::lgkm(8) == 6 && GemmSched<4, 4, 4>::lgkm(8) == 6, "schedule");
+static_assert(GemmSched<4, 4, 2>::lgkm(0) == -1 && GemmSched<4, 4, 2>::lgkm(31) >= 0, "schedule");
+static_assert(GemmSched<8, 8, 2>::lgkm(32) == 14 && GemmSched<8, 8, 2>::SLOTS == 128, "schedule");
 
 template <int N>
 __device__ __forceinline__ void wait_lgkm() {
@@ -131,7 +146,11 @@ __device__ __forceinline__ void gemm_tile_of(const GemmArgs& g, uint32_t b, uint
 // multiple of BK), copies use precomputed per-lane offsets.  EDGE = true: any
 // shape; boxes go through the general loader with zero fill at the edges.
 // SWM: the operands' swizzle mode (64B / 128B, or their _K256 forms).
-template <int BK, int S, bool EDGE, int SWM>
+// MI: the MFMA shape, 32 (v_mfma_f32_32x32x16_bf16, 4 x 4 tiles per wave) or
+// 16 (v_mfma_f32_16x16x32_bf16, 8 x 8 tiles).  Both run 1024 flop per clock
+// per SIMD; the 16 x 16 form moves less accumulator and operand register
+// data per flop, which under the chip's power limit holds a higher clock.
+template <int BK, int S, bool EDGE, int SWM, int MI>
 __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16(GemmArgs g) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr uint32_t ROWB = BK * 2;                 // bytes per LDS row (128 or 64)
@@ -142,6 +161,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     constexpr uint32_t SW = SWM & 3;                  // swizzled chunk bits (3 or 2)
     constexpr uint32_t KSH = (SWM & 4) ? 8u : 7u;     // key: 256- or 128-byte unit
     constexpr uint32_t CPR = ROWB / 16;               // chunks per row
+    static_assert(MI == 32 || MI == 16, "MFMA shape");
+    constexpr int NI = 128 / MI, NJ = 128 / MI;       // MFMA tiles per wave block (rows, columns)
+    constexpr int NF = NI + NJ;                       // fragments per sub-step
+    constexpr uint32_t KMI = MI == 32 ? 16u : 32u;    // K extent of one MFMA
+    typedef std::conditional_t<MI == 32, f32x16, f32x4> AccT;
 
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t lane = lane_id();
@@ -202,44 +226,54 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         }
     };
 
-    f32x16 acc[4][4];
+    AccT acc[NI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int j = 0; j < NJ; ++j) acc[i][j] = AccT{};
 
     const uint32_t wm = wave >> 1, wn = wave & 1;
-    const uint32_t khalf = lane >> 5;
-    constexpr uint32_t KK = BK / 16;                  // MFMA sub-steps per stage (even)
+    const uint32_t khalf = lane / (uint32_t)MI;      // which 8-element K chunk of the sub-step
+    constexpr uint32_t KK = BK / KMI;                 // MFMA sub-steps per stage (even)
     static_assert(KK % 2 == 0, "fragment buffer parity assumes an even sub-step count");
 
-    // LDS address of fragment f (0..3: A rows wm*128 + f*32 + l%32; 4..7: B)
-    // for sub-step kk, relative to the ring slot: lane l reads logical chunk
-    // 2*kk + l/32 of its row at the physical chunk the swizzle gives.  Loop
-    // invariant, so each read is one add of the slot offset.
-    uint32_t fad[KK][8];
+    // LDS address of fragment f (0..NI-1: A rows wm*128 + f*MI + l%MI; NI..:
+    // B) for sub-step kk, relative to the ring slot: lane l reads logical chunk
+    // (KMI/8)*kk + l/MI of its row at the physical chunk the swizzle gives.
+    // Loop invariant, so each read is one add of the slot offset.
+    uint32_t fad[KK][NF];
 #pragma unroll
     for (uint32_t kk = 0; kk < KK; ++kk)
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            const uint32_t row = (f < 4 ? wm : wn) * 128u + (uint32_t)(f & 3) * 32u + (lane & 31u);
+        for (int f = 0; f < NF; ++f) {
+            const uint32_t row = (f < NI ? wm : wn) * 128u + (uint32_t)(f % NI) * (uint32_t)MI + (lane % (uint32_t)MI);
             const uint32_t rb = row * ROWB;
             const uint32_t key = (rb >> KSH) & ((1u << SW) - 1u);
-            fad[kk][f] = lds0 + (f < 4 ? 0u : BOX) + rb + (((2u * kk + khalf) ^ key) << 4);
+            fad[kk][f] = lds0 + (f < NI ? 0u : BOX) + rb + ((((KMI / 8u) * kk + khalf) ^ key) << 4);
         }
-    bf16x8 fr[2][8];                                  // [sub-step parity][A0..A3, B0..B3]
+    bf16x8 fr[2][NF];                                 // [sub-step parity][A rows, B columns]
 #pragma unroll
-    for (int f = 0; f < 8; ++f) fr[1][f] = bf16x8{};
+    for (int f = 0; f < NF; ++f) fr[1][f] = bf16x8{};
+    if constexpr (MI == 16) asm volatile("s_nop 7" ::: "memory");   // accumulator writes before the first MFMA
+
+    // One MFMA: B as the first operand, so each accumulator holds the
+    // transposed tile (consecutive C columns per lane).  The 16 x 16 form is
+    // inline asm with the accumulator tied to the destination: the builtin
+    // lets the register allocator split them and copy accumulators around.
+    auto mfma = [&](AccT& c, const bf16x8& b, const bf16x8& a) {
+        if constexpr (MI == 32) {
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+        } else {
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+        }
+    };
 
     // One iteration runs from one workgroup barrier to the next:
-    //   phase A: accumulator rows 2-3 of the previous tile's last sub-step
+    //   phase A: accumulator rows NI/2.. of the previous tile's last sub-step
     //            (fragments already in registers), while reading sub-step 0
-    //            of tile t (8 MFMAs, one read each);
-    //   phase B: sub-steps 0 .. KK-2 of tile t, reading the next sub-step
-    //            (16 MFMAs and 8 reads each);
-    //   phase C: rows 0-1 of tile t's last sub-step (8 MFMAs); then wait for
+    //            of tile t;
+    //   phase B: sub-steps 0 .. KK-2 of tile t, reading the next sub-step;
+    //   phase C: rows 0 .. NI/2-1 of tile t's last sub-step; then wait for
     //            tile t+1's copies, and the barrier.
     // The slot of tile t-1 is free from the start of the iteration (every
     // wave passed the barrier after its last read of it), so tile t+S-1's
@@ -248,10 +282,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     // they would hold the waves' MFMA streams.  Every MFMA slot is pinned by
     // a scheduling barrier.  Iteration 0's phase A multiplies zero fragments
     // into zero accumulators (an exact no-op).
-    constexpr int SLOTS = 16 * (int)KK;              // MFMAs per wave and iteration
+    typedef GemmSched<NI, NJ, (int)KK> Sch;
+    constexpr int SLOTS = Sch::SLOTS;                // MFMAs per wave and iteration
     constexpr int NDMA = 2 * (int)GPW;               // copies per wave and tile
     constexpr int SPAN = S >= 3 ? SLOTS : (SLOTS * 3) / 8;
-    typedef GemmSched<(int)KK> Sch;
     auto iteration = [&](auto with_copies, uint32_t t, uint32_t slot_t, uint32_t slot_fill, uint32_t later,
                          bool wait_next) {
         constexpr bool COPY = decltype(with_copies)::value;
@@ -267,7 +301,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
                 __builtin_amdgcn_sched_barrier(0);
             }
             constexpr int i = Sch::mi(m), j = Sch::mj(m), buf = Sch::mbuf(m);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[buf][4 + j], fr[buf][i], acc[i][j], 0, 0, 0);
+            mfma(acc[i][j], fr[buf][NI + j], fr[buf][i]);
             constexpr int f = Sch::rfrag(m);
             if constexpr (f >= 0)
                 fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16(fad[Sch::rkk(m)][f] + so));
@@ -316,23 +350,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         iteration(std::integral_constant<bool, false>{}, t, slot_t, slot_fill, later, t + 1 < nk);
         slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
     }
-    // Rows 2-3 of the last tile's last sub-step.  The fragments come from
+    // Rows NI/2.. of the last tile's last sub-step.  The fragments come from
     // inline-asm reads the compiler believes complete at issue, so nothing
     // may be scheduled above the wait.
     wait_lgkm0();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        acc[2 + m / 4][m % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[1][4 + m % 4], fr[1][2 + m / 4],
-                                                                       acc[2 + m / 4][m % 4], 0, 0, 0);
-    }
+    for (int m = 0; m < Sch::HALF; ++m) mfma(acc[NI / 2 + m / NJ][m % NJ], fr[1][NI + m % NJ], fr[1][NI / 2 + m / NJ]);
+    // the asm MFMAs' results are read below without the compiler knowing
+    // their latency: cover it (a 16 x 16 x 32 MFMA takes 8 passes)
+    if constexpr (MI == 16) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     // Epilogue.  The MFMAs take B as their first operand, so accumulator
-    // (i, j) holds the transposed 32 x 32 tile: register r of lane l is C row
-    // i*32 + l%32 of the wave's block and column j*32 + (r/4)*8 + (l/32)*4 +
-    // r%4, i.e. four consecutive columns per group of four registers (8 bytes
-    // of bf16, converted with round-to-nearest-even).
-    const uint32_t rloc = wm * 128u + (lane & 31u);
+    // (i, j) holds the transposed MI x MI tile: register 4q + r of lane l is C
+    // row i*MI + l%MI of the wave's block and column j*MI + q*8 + (l/MI)*4 + r,
+    // i.e. four consecutive columns per group of four registers (8 bytes of
+    // bf16, converted with round-to-nearest-even); MI*MI/256 groups per tile.
+    constexpr int NQ = MI * MI / 256;
+    const uint32_t rloc = wm * 128u + (lane % (uint32_t)MI);
     const uint32_t cloc = wn * 128u + khalf * 4u;
     if (g.c_staged) {
         // Registers -> LDS -> global, as the pages' epilogue does: the
@@ -346,13 +381,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         typedef __attribute__((address_space(3))) u32x2 lds_u2_t;
         wg_barrier();
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t row = rloc + (uint32_t)i * 32u;
-                    const uint32_t col = cloc + (uint32_t)j * 32u + (uint32_t)q * 8u;
+                for (int q = 0; q < NQ; ++q) {
+                    const uint32_t row = rloc + (uint32_t)i * (uint32_t)MI;
+                    const uint32_t col = cloc + (uint32_t)j * (uint32_t)MI + (uint32_t)q * 8u;
                     const uint32_t chunk = row * 8u + ((col & 63u) >> 3);
                     const uint32_t addr = lds0 + (col >> 6) * 32768u +
                                           (swz_chunk(chunk, TMAP_SWIZZLE_128B_K256) << 4) + (col & 7u) * 2u;
@@ -405,13 +440,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     // C not 16-byte aligned: element stores, masked at the M / N edge.
     ATT_GLOBAL uint16_t* C = (ATT_GLOBAL uint16_t*)gptr(g.C);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t row = m0 + rloc + (uint32_t)i * 32u;
-                const uint32_t col = n0 + cloc + (uint32_t)j * 32u + (uint32_t)q * 8u;
+            for (int q = 0; q < NQ; ++q) {
+                const uint32_t row = m0 + rloc + (uint32_t)i * (uint32_t)MI;
+                const uint32_t col = n0 + cloc + (uint32_t)j * (uint32_t)MI + (uint32_t)q * 8u;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     if (row < g.M && col + e < g.N)
@@ -419,7 +454,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
             }
 }
 
-template <int BK, int S, bool EDGE, int SWM>
+template <int BK, int S, bool EDGE, int SWM, int MI>
 static tmap_status launch_gemm_t(const GemmArgs& g, hipStream_t st) {
     // The ring, or the 128 KiB C staging image if that is larger.
     constexpr uint32_t ring = (uint32_t)S * 2u * kTM * BK * 2u;
@@ -428,20 +463,33 @@ static tmap_status launch_gemm_t(const GemmArgs& g, hipStream_t st) {
     tmap_status s = device_lds_limit(&limit);
     if (s) return s;
     if (lds > limit) return TMAP_ERR_UNSUPPORTED;
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16<BK, S, EDGE, SWM>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16<BK, S, EDGE, SWM, MI>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-    hipLaunchKernelGGL((k_gemm_bf16<BK, S, EDGE, SWM>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st, g);
+    hipLaunchKernelGGL((k_gemm_bf16<BK, S, EDGE, SWM, MI>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st,
+                       g);
     return check_launch("gemm_bf16");
 }
 
-template <int BK, int S>
-static tmap_status launch_gemm(const GemmArgs& g, uint32_t swm, hipStream_t st) {
+template <int BK, int S, int MI>
+static tmap_status launch_gemm_mi(const GemmArgs& g, uint32_t swm, hipStream_t st) {
     const bool even = g.M % kTM == 0 && g.N % kTN == 0 && g.K % BK == 0;
     constexpr int BASE = BK == 64 ? TMAP_SWIZZLE_128B : TMAP_SWIZZLE_64B;
     if (swm & 4u)
-        return even ? launch_gemm_t<BK, S, false, BASE | 4>(g, st) : launch_gemm_t<BK, S, true, BASE | 4>(g, st);
-    return even ? launch_gemm_t<BK, S, false, BASE>(g, st) : launch_gemm_t<BK, S, true, BASE>(g, st);
+        return even ? launch_gemm_t<BK, S, false, BASE | 4, MI>(g, st) : launch_gemm_t<BK, S, true, BASE | 4, MI>(g, st);
+    return even ? launch_gemm_t<BK, S, false, BASE, MI>(g, st) : launch_gemm_t<BK, S, true, BASE, MI>(g, st);
+}
+
+// The 16 x 16 x 32 form needs an even number of 32-deep sub-steps per stage,
+// so it serves the 64-deep K step; the 32-deep step always uses 32 x 32 x 16.
+template <int BK, int S>
+static tmap_status launch_gemm(const GemmArgs& g, uint32_t swm, uint32_t mfma, hipStream_t st) {
+    if constexpr (BK == 64) {
+        if (mfma != 32) return launch_gemm_mi<BK, S, 16>(g, swm, st);
+    } else {
+        if (mfma == 16) return TMAP_ERR_UNSUPPORTED;
+    }
+    return launch_gemm_mi<BK, S, 32>(g, swm, st);
 }
 
 static tmap_status check_operand(const TmapImpl& t, uint32_t rows, uint32_t K, uint32_t* bk, uint32_t* swm) {
@@ -464,7 +512,8 @@ using namespace att;
 
 extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
                                     uint32_t K, uint32_t ldc, uint32_t stages, uint32_t group_m, uint32_t xcd,
-                                    void* stream) {
+                                    uint32_t mfma, void* stream) {
+    if (mfma != 0 && mfma != 16 && mfma != 32) return TMAP_ERR_UNSUPPORTED;
     if (!A || !B || !d_C) return TMAP_ERR_NULL;
     if (M == 0 || N == 0) return TMAP_OK;
     if (K == 0 || ldc < N || (reinterpret_cast<uintptr_t>(d_C) & 1u)) return TMAP_ERR_UNSUPPORTED;
@@ -505,19 +554,19 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
     }
     hipStream_t st = as_stream(stream);
     if (bka == 64) {
-        if (stages == 2) return launch_gemm<64, 2>(g, swa, st);
+        if (stages == 2) return launch_gemm<64, 2>(g, swa, mfma, st);
         return TMAP_ERR_UNSUPPORTED;
     }
     switch (stages) {
-    case 2: return launch_gemm<32, 2>(g, swa, st);
-    case 3: return launch_gemm<32, 3>(g, swa, st);
-    case 4: return launch_gemm<32, 4>(g, swa, st);
-    case 5: return launch_gemm<32, 5>(g, swa, st);
+    case 2: return launch_gemm<32, 2>(g, swa, mfma, st);
+    case 3: return launch_gemm<32, 3>(g, swa, mfma, st);
+    case 4: return launch_gemm<32, 4>(g, swa, mfma, st);
+    case 5: return launch_gemm<32, 5>(g, swa, mfma, st);
     default: return TMAP_ERR_UNSUPPORTED;
     }
 }
 
 extern "C" tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N, uint32_t K,
                                  uint32_t ldc, uint32_t stages, void* stream) {
-    return gemm_bf16_ex(A, B, d_C, M, N, K, ldc, stages, 0u, 1u, stream);
+    return gemm_bf16_ex(A, B, d_C, M, N, K, ldc, stages, 0u, 1u, 0u, stream);
 }

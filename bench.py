@@ -162,9 +162,10 @@ def run_extra(att, torch, stream, reps: int):
     return out
 
 
-GEMM_VARIANTS = ((64, "128b", 2), (32, "64b", 4), (64, "128b_k256", 2), (32, "64b_k256", 3),
-                 (32, "64b_k256", 4), (32, "64b_k256", 5))
-GEMM_DEFAULT = (64, "128b_k256", 2)
+# (K step, operand swizzle, ring stages, MFMA shape: 16 = 16x16x32, 32 = 32x32x16)
+GEMM_VARIANTS = ((64, "128b_k256", 2, 16), (64, "128b_k256", 2, 32), (64, "128b", 2, 16), (32, "64b_k256", 4, 32),
+                 (32, "64b_k256", 3, 32), (32, "64b", 4, 32))
+GEMM_DEFAULT = (64, "128b_k256", 2, 16)
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -187,7 +188,7 @@ def run_gemm_raster(att, torch, stream, reps: int, rounds: int = 3):
     Ad = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
     Bd = torch.randn(N, K, generator=g, device="cuda").to(torch.bfloat16)
     Cd = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    bk, sw, stages = GEMM_DEFAULT
+    bk, sw, stages, _ = GEMM_DEFAULT
     mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (bk, 256), None, sw)
     mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (bk, 256), None, sw)
     times = {r: [] for r in GEMM_RASTERS}
@@ -228,12 +229,13 @@ def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int 
     Cd = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     fns = {}
     keep = []
-    for bk, sw, stages in variants:
+    for bk, sw, stages, mi in variants:
         mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (bk, 256), None, sw)
         mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (bk, 256), None, sw)
         keep.append((mA, mB))
-        fns[f"gemm_bf16_8192_bk{bk}_{sw}_s{stages}"] = (
-            lambda mA=mA, mB=mB, stages=stages: att.gemm_bf16(mA, mB, Cd.data_ptr(), M, N, K, N, stages, stream))
+        fns[f"gemm_bf16_8192_bk{bk}_{sw}_s{stages}_mfma{mi}"] = (
+            lambda mA=mA, mB=mB, stages=stages, mi=mi: att.gemm_bf16_ex(mA, mB, Cd.data_ptr(), M, N, K, N, stages,
+                                                                        0, 1, stream, mi))
     if vendor:
         Bt = Bd.t()
         fns["vendor_gemm_torch_matmul"] = lambda: torch.matmul(Ad, Bt, out=Cd)
@@ -278,7 +280,7 @@ def main():
                     help="gemm: time only the GEMM mainloop; gemm-raster: the default GEMM under each tile "
                          "rasterisation; lds-probe: run the LDS bank probe layouts (profiling runs)")
     ap.add_argument("--gemm-variant", default="all",
-                    help="bk,stages[,k256] e.g. 32,4,k256 (with --only gemm)")
+                    help="bk,stages[,k256][,mfma] e.g. 32,4,k256 or 64,2,k256,32 (with --only gemm)")
     ap.add_argument("--ref-copy", action="store_true",
                     help="also time a plain device-to-device copy of the same bytes")
     ap.add_argument("--ceiling", action="store_true",
@@ -318,9 +320,12 @@ def main():
     if args.only == "gemm":
         variants = GEMM_VARIANTS
         if args.gemm_variant != "all":
-            bk, st, *k = args.gemm_variant.split(",")
+            bk, st, *rest = args.gemm_variant.split(",")
             bk, st = int(bk), int(st)
-            variants = ((bk, ("128b" if bk == 64 else "64b") + ("_k256" if k else ""), st),)
+            k256 = "k256" in rest
+            mi = [int(x) for x in rest if x.isdigit()]
+            mi = mi[0] if mi else (16 if bk == 64 else 32)
+            variants = ((bk, ("128b" if bk == 64 else "64b") + ("_k256" if k256 else ""), st, mi),)
         res = run_gemm(att, torch, stream, args.steps, variants)
         best = res[res["gemm_best"]]
         print(json.dumps({"metric": "bf16 GEMM 8192^3 TFLOP/s", "value": best["TFLOPs"], "unit": "TFLOP/s",

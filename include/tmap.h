@@ -318,10 +318,12 @@ tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, u
  * tile grid divides).  Maps
  * with box {32, 256} and TMAP_SWIZZLE_64B or TMAP_SWIZZLE_64B_K256 select the
  * 32-deep K step, for which stages may be 2 to 5; box {64, 256} takes
- * stages = 2. */
+ * stages = 2.  `mfma` picks the matrix instruction: 16 (16x16x32 tiles, the
+ * default for the 64-deep step), 32 (32x32x16 tiles, the only form for the
+ * 32-deep step) or 0 for the default; others return ERR_UNSUPPORTED. */
 tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
                          uint32_t K, uint32_t ldc, uint32_t stages, uint32_t group_m, uint32_t xcd,
-                         void* stream);
+                         uint32_t mfma, void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def bf16_to_f64(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def run_gemm(A_bits, Bt_bits, M, N, K, bk=64, stages=2, group_m=0, xcd=1, k256=False):
+def run_gemm(A_bits, Bt_bits, M, N, K, bk=64, stages=2, group_m=0, xcd=1, k256=False, mfma=0):
     """A_bits (M, K) row-major; Bt_bits (N, K) = column-major B.  Rows are
     stored with a leading dimension padded to a multiple of 8 elements (the
     maps need 16-byte strides).  Returns the bf16 bits of C (M, N)."""
@@ -48,7 +48,7 @@ def run_gemm(A_bits, Bt_bits, M, N, K, bk=64, stages=2, group_m=0, xcd=1, k256=F
     sw = ("128b" if bk == 64 else "64b") + ("_k256" if k256 else "")
     mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (ld * 2,), (bk, 256), None, sw)
     mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (ld * 2,), (bk, 256), None, sw)
-    att.gemm_bf16_ex(mA, mB, Cd.data_ptr(), M, N, K, N, stages, group_m, xcd, stream())
+    att.gemm_bf16_ex(mA, mB, Cd.data_ptr(), M, N, K, N, stages, group_m, xcd, stream(), mfma)
     torch.cuda.synchronize()
     return Cd.cpu().numpy().view(np.uint16)
 
@@ -62,16 +62,27 @@ def check_close(got_bits, ref):
 
 
 @pytest.mark.parametrize("k256", [False, True])
-@pytest.mark.parametrize("bk,stages", [(64, 2), (32, 2), (32, 3), (32, 4)])
-def test_identity_exact(bk, stages, k256):
+@pytest.mark.parametrize("bk,stages,mfma", [(64, 2, 16), (64, 2, 32), (32, 2, 32), (32, 3, 32), (32, 4, 32)])
+def test_identity_exact(bk, stages, mfma, k256):
     """A = I: C equals B exactly (one product per output, exact in fp32)."""
     K = N = 512
     M = K
     eye = np.zeros((M, K), dtype=np.uint16)
     eye[np.arange(M), np.arange(K)] = 0x3F80
     Bt = synthgen.normal_bf16_bits(51, (N, K))
-    C = run_gemm(eye, Bt, M, N, K, bk, stages, k256=k256)
+    C = run_gemm(eye, Bt, M, N, K, bk, stages, k256=k256, mfma=mfma)
     np.testing.assert_array_equal(C, Bt.T)
+
+
+def test_mfma_shape_argument():
+    """mfma 16 needs the 64-deep K step; unknown shapes are rejected."""
+    A = np.zeros((256, 64), dtype=np.uint16)
+    with pytest.raises(att.TmapError) as ei:
+        run_gemm(A, A, 256, 256, 64, 32, 2, mfma=16)
+    assert ei.value.name == "ERR_UNSUPPORTED"
+    with pytest.raises(att.TmapError) as ei:
+        run_gemm(A, A, 256, 256, 64, 64, 2, mfma=8)
+    assert ei.value.name == "ERR_UNSUPPORTED"
 
 
 def test_permutation_exact():
@@ -84,29 +95,31 @@ def test_permutation_exact():
     np.testing.assert_array_equal(C, Bt.T[perm])
 
 
-@pytest.mark.parametrize("M,N,K,bk,stages,k256", [
-    (512, 768, 1024, 64, 2, False), (768, 512, 1024, 32, 3, False), (512, 512, 2048, 32, 4, False),
-    (512, 768, 1024, 64, 2, True), (768, 512, 1024, 32, 4, True), (300, 200, 100, 32, 3, True),
-    (300, 200, 100, 64, 2, False), (257, 513, 96, 32, 2, False), (1, 1, 64, 64, 2, False),
-    (256, 256, 8, 64, 2, False)])
-def test_against_oracle_full(M, N, K, bk, stages, k256):
-    say("gemm", M, N, K, bk, stages, k256)
+@pytest.mark.parametrize("M,N,K,bk,stages,k256,mfma", [
+    (512, 768, 1024, 64, 2, False, 0), (768, 512, 1024, 32, 3, False, 0), (512, 512, 2048, 32, 4, False, 0),
+    (512, 768, 1024, 64, 2, True, 0), (768, 512, 1024, 32, 4, True, 0), (300, 200, 100, 32, 3, True, 0),
+    (300, 200, 100, 64, 2, False, 0), (257, 513, 96, 32, 2, False, 0), (1, 1, 64, 64, 2, False, 0),
+    (256, 256, 8, 64, 2, False, 0), (512, 768, 1024, 64, 2, True, 32), (300, 200, 100, 64, 2, True, 32),
+    (257, 513, 96, 64, 2, True, 16), (1, 1, 64, 64, 2, True, 16)])
+def test_against_oracle_full(M, N, K, bk, stages, k256, mfma):
+    say("gemm", M, N, K, bk, stages, k256, mfma)
     A = synthgen.normal_bf16_bits(54, (M, K))
     Bt = synthgen.normal_bf16_bits(55, (N, K))
-    C = run_gemm(A, Bt, M, N, K, bk, stages, k256=k256)
+    C = run_gemm(A, Bt, M, N, K, bk, stages, k256=k256, mfma=mfma)
     rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     ref = oracle.gemm_bf16_sample(A, Bt, K, rows.reshape(-1), cols.reshape(-1)).reshape(M, N)
     check_close(C, ref)
 
 
-@pytest.mark.parametrize("bk,stages,k256", [(64, 2, False), (32, 4, True), (64, 2, True)])
-def test_8192_sampled(bk, stages, k256):
+@pytest.mark.parametrize("bk,stages,k256,mfma", [(64, 2, False, 0), (32, 4, True, 0), (64, 2, True, 16),
+                                                 (64, 2, True, 32)])
+def test_8192_sampled(bk, stages, k256, mfma):
     ex = W.GEMM_8192
     M, N, K = ex["M"], ex["N"], ex["K"]
-    say("gemm 8192^3")
+    say("gemm 8192^3", bk, stages, k256, mfma)
     A = synthgen.normal_bf16_bits(ex["seed"] * 1000 + 1, (M, K))
     Bt = synthgen.normal_bf16_bits(ex["seed"] * 1000 + 2, (N, K))
-    C = run_gemm(A, Bt, M, N, K, bk, stages, k256=k256)
+    C = run_gemm(A, Bt, M, N, K, bk, stages, k256=k256, mfma=mfma)
     rows, cols = synthgen.sample_pairs(ex["seed"] * 1000 + 3, ex["nsample"], M, N)
     ref = oracle.gemm_bf16_sample(A, Bt, K, rows, cols)
     check_close(C[rows, cols], ref)
