@@ -56,13 +56,15 @@ struct GemmArgs {
 // lgkmcnt the slot must wait for before its MFMA.  A wave's C block is NI x
 // NJ MFMA tiles; one sub-step (one MFMA K extent) needs NI A and NJ B
 // fragments and runs SUB = NI * NJ MFMAs; an iteration covers KK sub-steps.
+// The last AR accumulator rows of the previous tile's last sub-step run at
+// the start of the next iteration, under the reads of its first sub-step.
 // Fragment reads are issued as inline asm (so the compiler's LDS-DMA alias
 // tracking adds no vmcnt waits) and complete in issue order, so the wait is
 // exact (clamped to the counter's 4 bits, which only waits longer).
-template <int NI, int NJ, int KK>
+template <int NI, int NJ, int KK, int AR = NI / 2>
 struct GemmSched {
     static constexpr int SUB = NI * NJ;
-    static constexpr int HALF = SUB / 2;              // rows NI/2.. of the last sub-step
+    static constexpr int HALF = AR * NJ;              // slots of rows NI-AR.. of the last sub-step
     static constexpr int NF = NI + NJ;                // fragments per sub-step
     static constexpr int RA = HALF / NF;              // read spacing while finishing the previous tile
     static constexpr int RB = SUB / NF;               // read spacing inside a sub-step
@@ -71,7 +73,7 @@ struct GemmSched {
     static_assert(RA >= 1 && RB >= 1 && HALF % NF == 0 && SUB % NF == 0, "read spacing");
     // MFMA of slot m: accumulator row i, column j, fragment buffer.
     static constexpr int mi(int m) {
-        return m < HALF ? NI / 2 + m / NJ : (m < B_END ? ((m - HALF) % SUB) / NJ : (m - B_END) / NJ);
+        return m < HALF ? NI - AR + m / NJ : (m < B_END ? ((m - HALF) % SUB) / NJ : (m - B_END) / NJ);
     }
     static constexpr int mj(int m) { return m < HALF ? m % NJ : (m < B_END ? (m - HALF) % NJ : (m - B_END) % NJ); }
     static constexpr int mbuf(int m) { return m < HALF ? 1 : (m < B_END ? ((m - HALF) / SUB) & 1 : 1); }
@@ -113,6 +115,8 @@ struct GemmSched {
 static_assert(GemmSched<4, 4, 2>::lgkm(8) == 6 && GemmSched<4, 4, 4>::lgkm(8) == 6, "schedule");
 static_assert(GemmSched<4, 4, 2>::lgkm(0) == -1 && GemmSched<4, 4, 2>::lgkm(31) >= 0, "schedule");
 static_assert(GemmSched<8, 8, 2>::lgkm(32) == 14 && GemmSched<8, 8, 2>::SLOTS == 128, "schedule");
+static_assert(GemmSched<8, 8, 2, 6>::mi(0) == 2 && GemmSched<8, 8, 2, 6>::mi(47) == 7 && GemmSched<8, 8, 2, 6>::mi(127) == 1,
+              "schedule");
 
 template <int N>
 __device__ __forceinline__ void wait_lgkm() {
@@ -155,7 +159,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr uint32_t ROWB = BK * 2;                 // bytes per LDS row (128 or 64)
     constexpr uint32_t BOX = kTM * ROWB;              // bytes per operand box
-    constexpr uint32_t STAGE = 2 * BOX;
+    // Ring layout: the S A-box slots first, then the S B-box slots, so that
+    // slot s of either operand is s * BOX from slot 0 (with two slots that
+    // offset fits a ds_read immediate).
+    constexpr uint32_t BREG = (uint32_t)S * BOX;
     constexpr uint32_t GROUPS = BOX / 1024;           // 1 KiB DMA groups per box
     constexpr uint32_t GPW = GROUPS / 4;              // per wave and operand
     constexpr uint32_t SW = SWM & 3;                  // swizzled chunk bits (3 or 2)
@@ -209,20 +216,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
 
     // Whole-tile issue (prologue, and every copy of the general loader).
     auto issue = [&](uint32_t kt, uint32_t slot) {
-        uint8_t* st = smem + slot * STAGE;
         if constexpr (interior) {
             const uint64_t ka = baseA + (uint64_t)kt * ROWB;
             const uint64_t kb = baseB + (uint64_t)kt * ROWB;
-            const uint32_t la = lds0 + slot * STAGE + wave_u * GPW * 1024u;
+            const uint32_t la = lds0 + slot * BOX + wave_u * GPW * 1024u;
 #pragma unroll
             for (uint32_t j = 0; j < GPW; ++j) dma16_sv(ka, offA[j], la + j * 1024u);
 #pragma unroll
-            for (uint32_t j = 0; j < GPW; ++j) dma16_sv(kb, offB[j], la + BOX + j * 1024u);
+            for (uint32_t j = 0; j < GPW; ++j) dma16_sv(kb, offB[j], la + BREG + j * 1024u);
         } else {
             const int32_t ca[5] = {(int32_t)(kt * BK), (int32_t)m0, 0, 0, 0};
             const int32_t cb[5] = {(int32_t)(kt * BK), (int32_t)n0, 0, 0, 0};
-            tile_load_issue(g.A, ca, st, wave, 4);
-            tile_load_issue(g.B, cb, st + BOX, wave, 4);
+            tile_load_issue(g.A, ca, smem + slot * BOX, wave, 4);
+            tile_load_issue(g.B, cb, smem + BREG + slot * BOX, wave, 4);
         }
     };
 
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
             const uint32_t row = (f < NI ? wm : wn) * 128u + (uint32_t)(f % NI) * (uint32_t)MI + (lane % (uint32_t)MI);
             const uint32_t rb = row * ROWB;
             const uint32_t key = (rb >> KSH) & ((1u << SW) - 1u);
-            fad[kk][f] = lds0 + (f < NI ? 0u : BOX) + rb + ((((KMI / 8u) * kk + khalf) ^ key) << 4);
+            fad[kk][f] = lds0 + (f < NI ? 0u : BREG) + rb + ((((KMI / 8u) * kk + khalf) ^ key) << 4);
         }
     bf16x8 fr[2][NF];                                 // [sub-step parity][A rows, B columns]
 #pragma unroll
@@ -269,11 +275,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     };
 
     // One iteration runs from one workgroup barrier to the next:
-    //   phase A: accumulator rows NI/2.. of the previous tile's last sub-step
-    //            (fragments already in registers), while reading sub-step 0
-    //            of tile t;
+    //   phase A: accumulator rows NI-AR.. of the previous tile's last
+    //            sub-step (fragments already in registers), while reading
+    //            sub-step 0 of tile t;
     //   phase B: sub-steps 0 .. KK-2 of tile t, reading the next sub-step;
-    //   phase C: rows 0 .. NI/2-1 of tile t's last sub-step; then wait for
+    //   phase C: rows 0 .. NI-AR-1 of tile t's last sub-step; then wait for
     //            tile t+1's copies, and the barrier.
     // The slot of tile t-1 is free from the start of the iteration (every
     // wave passed the barrier after its last read of it), so tile t+S-1's
@@ -282,17 +288,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     // they would hold the waves' MFMA streams.  Every MFMA slot is pinned by
     // a scheduling barrier.  Iteration 0's phase A multiplies zero fragments
     // into zero accumulators (an exact no-op).
-    typedef GemmSched<NI, NJ, (int)KK> Sch;
+    constexpr int AR = MI == 16 ? 4 : 2;             // rows carried into the next iteration
+    typedef GemmSched<NI, NJ, (int)KK, AR> Sch;
     constexpr int SLOTS = Sch::SLOTS;                // MFMAs per wave and iteration
     constexpr int NDMA = 2 * (int)GPW;               // copies per wave and tile
     constexpr int SPAN = S >= 3 ? SLOTS : (SLOTS * 3) / 8;
-    auto iteration = [&](auto with_copies, uint32_t t, uint32_t slot_t, uint32_t slot_fill, uint32_t later,
-                         bool wait_next) {
+    // slot_c: the slot of tile t as a compile-time constant (two-slot ring:
+    // the fragment reads carry it as an immediate offset, no per-read add),
+    // or -1 to add slot_t at run time.
+    auto iteration = [&](auto with_copies, auto slot_c, uint32_t t, uint32_t slot_t, uint32_t slot_fill,
+                         uint32_t later, bool wait_next) {
         constexpr bool COPY = decltype(with_copies)::value;
-        const uint32_t so = slot_t * STAGE;
+        constexpr int SC = decltype(slot_c)::value;
+        const uint32_t so = slot_t * BOX;
         const uint64_t ka = baseA + (uint64_t)(t + S - 1) * ROWB;
         const uint64_t kb = baseB + (uint64_t)(t + S - 1) * ROWB;
-        const uint32_t la = lds0 + slot_fill * STAGE + wave_u * GPW * 1024u;
+        const uint32_t la = lds0 + slot_fill * BOX + wave_u * GPW * 1024u;
         static_for<SLOTS>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
             constexpr int W = Sch::lgkm(m);
@@ -303,14 +314,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
             constexpr int i = Sch::mi(m), j = Sch::mj(m), buf = Sch::mbuf(m);
             mfma(acc[i][j], fr[buf][NI + j], fr[buf][i]);
             constexpr int f = Sch::rfrag(m);
-            if constexpr (f >= 0)
-                fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16(fad[Sch::rkk(m)][f] + so));
+            if constexpr (f >= 0) {
+                if constexpr (SC >= 0)
+                    fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16_off<(uint32_t)SC * BOX>(fad[Sch::rkk(m)][f]));
+                else
+                    fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16(fad[Sch::rkk(m)][f] + so));
+            }
             if constexpr (COPY && interior) {
                 static_for<NDMA>([&](auto cc) {
                     constexpr int c = decltype(cc)::value;
                     if constexpr ((c * SPAN) / NDMA == m) {
                         if constexpr (c < (int)GPW) dma16_sv(ka, offA[c], la + (uint32_t)c * 1024u);
-                        else dma16_sv(kb, offB[c - GPW], la + BOX + (uint32_t)(c - GPW) * 1024u);
+                        else dma16_sv(kb, offB[c - GPW], la + BREG + (uint32_t)(c - GPW) * 1024u);
                     }
                 });
             }
@@ -338,25 +353,42 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     uint32_t slot_t = 0, slot_fill = S - 1;
     uint32_t t = 0;
     const uint32_t nfull = nk >= (uint32_t)S ? nk - (uint32_t)S + 1u : 0u;
-    for (; t < nfull; ++t) {
-        if constexpr (!interior) issue(t + S - 1, slot_fill);
-        iteration(std::integral_constant<bool, true>{}, t, slot_t, slot_fill, (uint32_t)(S - 2), true);
-        slot_fill = slot_t;
-        slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
+    typedef std::integral_constant<bool, true> with_c;
+    typedef std::integral_constant<bool, false> without_c;
+    typedef std::integral_constant<int, -1> slot_rt;
+    if constexpr (S == 2 && interior) {
+        // tile t sits in slot t % 2: unroll by two so each body knows its slot
+        for (; t + 2 <= nfull; t += 2) {
+            iteration(with_c{}, std::integral_constant<int, 0>{}, t, 0u, 1u, 0u, true);
+            iteration(with_c{}, std::integral_constant<int, 1>{}, t + 1, 1u, 0u, 0u, true);
+        }
+        if (t < nfull) {
+            iteration(with_c{}, std::integral_constant<int, 0>{}, t, 0u, 1u, 0u, true);
+            ++t;
+        }
+        slot_t = t & 1u;
+        slot_fill = slot_t ^ 1u;
+    } else {
+        for (; t < nfull; ++t) {
+            if constexpr (!interior) issue(t + S - 1, slot_fill);
+            iteration(with_c{}, slot_rt{}, t, slot_t, slot_fill, (uint32_t)(S - 2), true);
+            slot_fill = slot_t;
+            slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
+        }
     }
     for (; t < nk; ++t) {
         // Tiles issued after tile t+1: t+2 .. nk-1.
         const uint32_t later = nk >= t + 2 ? nk - t - 2 : 0u;
-        iteration(std::integral_constant<bool, false>{}, t, slot_t, slot_fill, later, t + 1 < nk);
+        iteration(without_c{}, slot_rt{}, t, slot_t, slot_fill, later, t + 1 < nk);
         slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
     }
-    // Rows NI/2.. of the last tile's last sub-step.  The fragments come from
+    // Rows NI-AR.. of the last tile's last sub-step.  The fragments come from
     // inline-asm reads the compiler believes complete at issue, so nothing
     // may be scheduled above the wait.
     wait_lgkm0();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m < Sch::HALF; ++m) mfma(acc[NI / 2 + m / NJ][m % NJ], fr[1][NI + m % NJ], fr[1][NI / 2 + m / NJ]);
+    for (int m = 0; m < Sch::HALF; ++m) mfma(acc[NI - AR + m / NJ][m % NJ], fr[1][NI + m % NJ], fr[1][NI - AR + m / NJ]);
     // the asm MFMAs' results are read below without the compiler knowing
     // their latency: cover it (a 16 x 16 x 32 MFMA takes 8 passes)
     if constexpr (MI == 16) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");

@@ -180,6 +180,16 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t lds_addr) {
     return v;
 }
 
+// The same read with a compile-time byte offset in the instruction's
+// immediate field (no address arithmetic at the call site).
+template <uint32_t OFF>
+__device__ __forceinline__ u32x4 lds_read16_off(uint32_t lds_addr) {
+    static_assert(OFF < 65536u, "ds_read offset field is 16 bits");
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "n"(OFF) : "memory");
+    return v;
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }

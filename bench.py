@@ -326,7 +326,7 @@ def main():
             mi = [int(x) for x in rest if x.isdigit()]
             mi = mi[0] if mi else (16 if bk == 64 else 32)
             variants = ((bk, ("128b" if bk == 64 else "64b") + ("_k256" if k256 else ""), st, mi),)
-        res = run_gemm(att, torch, stream, args.steps, variants)
+        res = run_gemm(att, torch, stream, args.steps, variants, vendor=True)
         best = res[res["gemm_best"]]
         print(json.dumps({"metric": "bf16 GEMM 8192^3 TFLOP/s", "value": best["TFLOPs"], "unit": "TFLOP/s",
                           "n_gpus": 1, "steps": args.steps, "higher_is_better": True, "dtype": "bf16",
