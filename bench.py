@@ -264,6 +264,37 @@ def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int 
     return out
 
 
+def hbm_ceiling(att, torch, stream, reps: int = 100):
+    """What plain streaming kernels (the library's hbm_probe: coalesced
+    16-byte loads, non-temporal 16-byte stores) reach on this GPU's HBM with
+    the same 128 MiB working sets, 4 rotating buffers so the last-level cache
+    cannot serve them: read-only, write-only and a linear copy."""
+    n = 8192 * 8192 * 2
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255) for _ in range(4)]
+    outs = [torch.empty_like(b) for b in bufs]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        for k in range(10):
+            fn(k)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for k in range(reps):
+            fn(k)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    r = timed(lambda k: att.hbm_probe("read", bufs[k % 4], sink, n, stream))
+    w = timed(lambda k: att.hbm_probe("write", None, outs[k % 4], n, stream))
+    c = timed(lambda k: att.hbm_probe("copy", bufs[k % 4], outs[k % 4], n, stream))
+    ok = all(torch.equal(a, b) for a, b in zip(bufs, outs))
+    return {"read_only_GBps": round(n / r / 1e6, 1), "write_only_GBps": round(n / w / 1e6, 1),
+            "copy_GBps": round(2 * n / c / 1e6, 1), "copy_verified": ok, "bytes_per_buffer": n,
+            "what": "hbm_probe read / write / copy over 4 rotating 128 MiB buffers"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
