@@ -61,6 +61,32 @@ struct GemmArgs {
 // Fragment reads are issued as inline asm (so the compiler's LDS-DMA alias
 // tracking adds no vmcnt waits) and complete in issue order, so the wait is
 // exact (clamped to the counter's 4 bits, which only waits longer).
+// The 16 x 16 MFMAs here are inline asm, so the compiler does not know their
+// latency: code it generates next to them (accumulator copies at control-
+// flow joins, spills, the epilogue's reads) could read a result that has not
+// landed, or write an accumulator a queued MFMA still reads.  Issued MFMAs
+// queue behind each other for well over a hundred cycles, so the drain is
+// 32 x 8 wait states; it runs once per tile, after the last MFMA.
+// acc_fence() then hands every accumulator through an empty asm statement
+// ordered after the drain, so that no compiler copy of a final value can be
+// placed before it; at the start it pins the zeroed accumulators in AGPRs
+// before the first MFMA.
+template <typename AccT, int NI, int NJ>
+__device__ __forceinline__ void acc_fence(AccT (&acc)[NI][NJ]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
+__device__ __forceinline__ void mfma_drain() {
+    asm volatile(
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 template <int NI, int NJ, int KK, int AR = NI / 2>
 struct GemmSched {
     static constexpr int SUB = NI * NJ;
@@ -146,43 +172,14 @@ __device__ __forceinline__ void gemm_tile_of(const GemmArgs& g, uint32_t b, uint
     tn = in / rows;
 }
 
-// EDGE = false: every box is inside the tensors (M, N multiples of 256, K a
-// multiple of BK), copies use precomputed per-lane offsets.  EDGE = true: any
-// shape; boxes go through the general loader with zero fill at the edges.
-// SWM: the operands' swizzle mode (64B / 128B, or their _K256 forms).
-// MI: the MFMA shape, 32 (v_mfma_f32_32x32x16_bf16, 4 x 4 tiles per wave) or
-// 16 (v_mfma_f32_16x16x32_bf16, 8 x 8 tiles).  Both run 1024 flop per clock
-// per SIMD; the 16 x 16 form moves less accumulator and operand register
-// data per flop, which under the chip's power limit holds a higher clock.
-template <int BK, int S, bool EDGE, int SWM, int MI>
-__global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16(GemmArgs g) {
-    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    constexpr uint32_t ROWB = BK * 2;                 // bytes per LDS row (128 or 64)
-    constexpr uint32_t BOX = kTM * ROWB;              // bytes per operand box
-    // Ring layout: the S A-box slots first, then the S B-box slots, so that
-    // slot s of either operand is s * BOX from slot 0 (with two slots that
-    // offset fits a ds_read immediate).
-    constexpr uint32_t BREG = (uint32_t)S * BOX;
-    constexpr uint32_t GROUPS = BOX / 1024;           // 1 KiB DMA groups per box
-    constexpr uint32_t GPW = GROUPS / 4;              // per wave and operand
-    constexpr uint32_t SW = SWM & 3;                  // swizzled chunk bits (3 or 2)
-    constexpr uint32_t KSH = (SWM & 4) ? 8u : 7u;     // key: 256- or 128-byte unit
-    constexpr uint32_t CPR = ROWB / 16;               // chunks per row
-    static_assert(MI == 32 || MI == 16, "MFMA shape");
-    constexpr int NI = 128 / MI, NJ = 128 / MI;       // MFMA tiles per wave block (rows, columns)
-    constexpr int NF = NI + NJ;                       // fragments per sub-step
-    constexpr uint32_t KMI = MI == 32 ? 16u : 32u;    // K extent of one MFMA
-    typedef std::conditional_t<MI == 32, f32x16, f32x4> AccT;
-
-    const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t lane = lane_id();
+// C tile of this workgroup.  Workgroups are dispatched round-robin over the
+// 8 XCDs; xcd == 1 renumbers them so that each XCD owns a contiguous range of
+// the grouped order, xcd == 2 gives XCD x a blk_m x blk_n block of C tiles
+// (blocks 2 wide in n), walked in groups of group_m tile rows, so its L2
+// serves blk_m A panels and blk_n B panels instead of whole tile rows.
+__device__ __forceinline__ void gemm_block_tile(const GemmArgs& g, uint32_t& tm, uint32_t& tn) {
     const uint32_t G = gridDim.x;
-    uint32_t tm, tn;
     if (g.xcd == 2) {
-        // Workgroups are dispatched round-robin over the 8 XCDs: XCD x owns a
-        // blk_m x blk_n block of C tiles (blocks 2 wide in n), walked in
-        // groups of group_m tile rows, so its L2 serves blk_m A panels and
-        // blk_n B panels instead of whole tile rows.
         const uint32_t x = blockIdx.x % 8u, local = blockIdx.x / 8u;
         const uint32_t bm0 = (x >> 1) * g.blk_m, bn0 = (x & 1u) * g.blk_n;
         const uint32_t gm = g.group_m < g.blk_m ? g.group_m : g.blk_m;
@@ -194,213 +191,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         const uint32_t bid = g.xcd ? (blockIdx.x % 8u) * (G / 8u) + blockIdx.x / 8u : blockIdx.x;
         gemm_tile_of(g, bid, tm, tn);
     }
-    const uint32_t m0 = tm * kTM, n0 = tn * kTN;
-    const uint32_t nk = (g.K + BK - 1) / BK;
-    constexpr bool interior = !EDGE;
+}
 
-    // Per-lane source offsets inside a box (same for every K step): lane l of
-    // group j fills physical chunk p = j*64 + l with logical chunk swz(p).
-    const uint32_t lds0 = lds_addr_of(smem);
-    const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
-    uint32_t offA[GPW], offB[GPW];
-#pragma unroll
-    for (uint32_t j = 0; j < GPW; ++j) {
-        const uint32_t p = (wave * GPW + j) * 64u + lane;
-        const uint32_t q = swz_chunk(p, SWM);
-        const uint32_t row = q / CPR, ch = q % CPR;
-        offA[j] = row * (uint32_t)g.A.stride[0] + ch * 16u;
-        offB[j] = row * (uint32_t)g.B.stride[0] + ch * 16u;
-    }
-    const uint64_t baseA = g.A.base + (uint64_t)m0 * g.A.stride[0];
-    const uint64_t baseB = g.B.base + (uint64_t)n0 * g.B.stride[0];
-
-    // Whole-tile issue (prologue, and every copy of the general loader).
-    auto issue = [&](uint32_t kt, uint32_t slot) {
-        if constexpr (interior) {
-            const uint64_t ka = baseA + (uint64_t)kt * ROWB;
-            const uint64_t kb = baseB + (uint64_t)kt * ROWB;
-            const uint32_t la = lds0 + slot * BOX + wave_u * GPW * 1024u;
-#pragma unroll
-            for (uint32_t j = 0; j < GPW; ++j) dma16_sv(ka, offA[j], la + j * 1024u);
-#pragma unroll
-            for (uint32_t j = 0; j < GPW; ++j) dma16_sv(kb, offB[j], la + BREG + j * 1024u);
-        } else {
-            const int32_t ca[5] = {(int32_t)(kt * BK), (int32_t)m0, 0, 0, 0};
-            const int32_t cb[5] = {(int32_t)(kt * BK), (int32_t)n0, 0, 0, 0};
-            tile_load_issue(g.A, ca, smem + slot * BOX, wave, 4);
-            tile_load_issue(g.B, cb, smem + BREG + slot * BOX, wave, 4);
-        }
-    };
-
-    AccT acc[NI][NJ];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = AccT{};
-
-    const uint32_t wm = wave >> 1, wn = wave & 1;
-    const uint32_t khalf = lane / (uint32_t)MI;      // which 8-element K chunk of the sub-step
-    constexpr uint32_t KK = BK / KMI;                 // MFMA sub-steps per stage (even)
-    static_assert(KK % 2 == 0, "fragment buffer parity assumes an even sub-step count");
-
-    // LDS address of fragment f (0..NI-1: A rows wm*128 + f*MI + l%MI; NI..:
-    // B) for sub-step kk, relative to the ring slot: lane l reads logical chunk
-    // (KMI/8)*kk + l/MI of its row at the physical chunk the swizzle gives.
-    // Loop invariant, so each read is one add of the slot offset.
-    uint32_t fad[KK][NF];
-#pragma unroll
-    for (uint32_t kk = 0; kk < KK; ++kk)
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            const uint32_t row = (f < NI ? wm : wn) * 128u + (uint32_t)(f % NI) * (uint32_t)MI + (lane % (uint32_t)MI);
-            const uint32_t rb = row * ROWB;
-            const uint32_t key = (rb >> KSH) & ((1u << SW) - 1u);
-            fad[kk][f] = lds0 + (f < NI ? 0u : BREG) + rb + ((((KMI / 8u) * kk + khalf) ^ key) << 4);
-        }
-    bf16x8 fr[2][NF];                                 // [sub-step parity][A rows, B columns]
-#pragma unroll
-    for (int f = 0; f < NF; ++f) fr[1][f] = bf16x8{};
-    if constexpr (MI == 16) asm volatile("s_nop 7" ::: "memory");   // accumulator writes before the first MFMA
-
-    // One MFMA: B as the first operand, so each accumulator holds the
-    // transposed tile (consecutive C columns per lane).  The 16 x 16 form is
-    // inline asm with the accumulator tied to the destination: the builtin
-    // lets the register allocator split them and copy accumulators around.
-    auto mfma = [&](AccT& c, const bf16x8& b, const bf16x8& a) {
-        if constexpr (MI == 32) {
-            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
-        } else {
-            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
-        }
-    };
-
-    // One iteration runs from one workgroup barrier to the next:
-    //   phase A: accumulator rows NI-AR.. of the previous tile's last
-    //            sub-step (fragments already in registers), while reading
-    //            sub-step 0 of tile t;
-    //   phase B: sub-steps 0 .. KK-2 of tile t, reading the next sub-step;
-    //   phase C: rows 0 .. NI-AR-1 of tile t's last sub-step; then wait for
-    //            tile t+1's copies, and the barrier.
-    // The slot of tile t-1 is free from the start of the iteration (every
-    // wave passed the barrier after its last read of it), so tile t+S-1's
-    // copies go there, spread evenly over the first SPAN MFMAs: the CU's
-    // address unit takes 16 cycles per 1 KiB copy, and issued back to back
-    // they would hold the waves' MFMA streams.  Every MFMA slot is pinned by
-    // a scheduling barrier.  Iteration 0's phase A multiplies zero fragments
-    // into zero accumulators (an exact no-op).
-    constexpr int AR = MI == 16 ? 4 : 2;             // rows carried into the next iteration
-    typedef GemmSched<NI, NJ, (int)KK, AR> Sch;
-    constexpr int SLOTS = Sch::SLOTS;                // MFMAs per wave and iteration
-    constexpr int NDMA = 2 * (int)GPW;               // copies per wave and tile
-    constexpr int SPAN = S >= 3 ? SLOTS : (SLOTS * 3) / 8;
-    // slot_c: the slot of tile t as a compile-time constant (two-slot ring:
-    // the fragment reads carry it as an immediate offset, no per-read add),
-    // or -1 to add slot_t at run time.
-    auto iteration = [&](auto with_copies, auto slot_c, uint32_t t, uint32_t slot_t, uint32_t slot_fill,
-                         uint32_t later, bool wait_next) {
-        constexpr bool COPY = decltype(with_copies)::value;
-        constexpr int SC = decltype(slot_c)::value;
-        const uint32_t so = slot_t * BOX;
-        const uint64_t ka = baseA + (uint64_t)(t + S - 1) * ROWB;
-        const uint64_t kb = baseB + (uint64_t)(t + S - 1) * ROWB;
-        const uint32_t la = lds0 + slot_fill * BOX + wave_u * GPW * 1024u;
-        static_for<SLOTS>([&](auto mc) {
-            constexpr int m = decltype(mc)::value;
-            constexpr int W = Sch::lgkm(m);
-            if constexpr (W >= 0) {
-                wait_lgkm<W>();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            constexpr int i = Sch::mi(m), j = Sch::mj(m), buf = Sch::mbuf(m);
-            mfma(acc[i][j], fr[buf][NI + j], fr[buf][i]);
-            constexpr int f = Sch::rfrag(m);
-            if constexpr (f >= 0) {
-                if constexpr (SC >= 0)
-                    fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16_off<(uint32_t)SC * BOX>(fad[Sch::rkk(m)][f]));
-                else
-                    fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16(fad[Sch::rkk(m)][f] + so));
-            }
-            if constexpr (COPY && interior) {
-                static_for<NDMA>([&](auto cc) {
-                    constexpr int c = decltype(cc)::value;
-                    if constexpr ((c * SPAN) / NDMA == m) {
-                        if constexpr (c < (int)GPW) dma16_sv(ka, offA[c], la + (uint32_t)c * 1024u);
-                        else dma16_sv(kb, offB[c - GPW], la + BREG + (uint32_t)(c - GPW) * 1024u);
-                    }
-                });
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        if (wait_next) {
-            if constexpr (interior) wait_stage<2 * GPW, S - 2>(later);
-            else wait_vmcnt<0>();
-            wait_lgkm0();
-            wg_barrier();
-        }
-    };
-
-    // Prologue: tiles 0 .. S-2 in flight; wait for tile 0.
-    const uint32_t pro = nk < (uint32_t)(S - 1) ? nk : (uint32_t)(S - 1);
-    for (uint32_t s = 0; s < pro; ++s) issue(s, s);
-    if constexpr (interior) wait_stage<2 * GPW, S - 2>(pro - 1);
-    else wait_vmcnt<0>();
-    wait_lgkm0();
-    wg_barrier();
-
-    // Iterations whose tile t+S-1 exists copy it into the slot of tile t-1.
-    // The general loader issues whole tiles up front and drains before each
-    // barrier.
-    uint32_t slot_t = 0, slot_fill = S - 1;
-    uint32_t t = 0;
-    const uint32_t nfull = nk >= (uint32_t)S ? nk - (uint32_t)S + 1u : 0u;
-    typedef std::integral_constant<bool, true> with_c;
-    typedef std::integral_constant<bool, false> without_c;
-    typedef std::integral_constant<int, -1> slot_rt;
-    if constexpr (S == 2 && interior) {
-        // tile t sits in slot t % 2: unroll by two so each body knows its slot
-        for (; t + 2 <= nfull; t += 2) {
-            iteration(with_c{}, std::integral_constant<int, 0>{}, t, 0u, 1u, 0u, true);
-            iteration(with_c{}, std::integral_constant<int, 1>{}, t + 1, 1u, 0u, 0u, true);
-        }
-        if (t < nfull) {
-            iteration(with_c{}, std::integral_constant<int, 0>{}, t, 0u, 1u, 0u, true);
-            ++t;
-        }
-        slot_t = t & 1u;
-        slot_fill = slot_t ^ 1u;
-    } else {
-        for (; t < nfull; ++t) {
-            if constexpr (!interior) issue(t + S - 1, slot_fill);
-            iteration(with_c{}, slot_rt{}, t, slot_t, slot_fill, (uint32_t)(S - 2), true);
-            slot_fill = slot_t;
-            slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
-        }
-    }
-    for (; t < nk; ++t) {
-        // Tiles issued after tile t+1: t+2 .. nk-1.
-        const uint32_t later = nk >= t + 2 ? nk - t - 2 : 0u;
-        iteration(without_c{}, slot_rt{}, t, slot_t, slot_fill, later, t + 1 < nk);
-        slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
-    }
-    // Rows NI-AR.. of the last tile's last sub-step.  The fragments come from
-    // inline-asm reads the compiler believes complete at issue, so nothing
-    // may be scheduled above the wait.
-    wait_lgkm0();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < Sch::HALF; ++m) mfma(acc[NI - AR + m / NJ][m % NJ], fr[1][NI + m % NJ], fr[1][NI - AR + m / NJ]);
-    // the asm MFMAs' results are read below without the compiler knowing
-    // their latency: cover it (a 16 x 16 x 32 MFMA takes 8 passes)
-    if constexpr (MI == 16) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-
+// Epilogue of a workgroup's 256 x 256 C tile from the accumulators of its
+// four waves (2 x 2 blocks of 128 x 128, NI x NJ tiles of MI x MI each).
+template <int MI, typename AccT, int NI, int NJ>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI][NJ], uint32_t lds0, uint32_t wave,
+                                              uint32_t lane, uint32_t m0, uint32_t n0) {
     // Epilogue.  The MFMAs take B as their first operand, so accumulator
     // (i, j) holds the transposed MI x MI tile: register 4q + r of lane l is C
     // row i*MI + l%MI of the wave's block and column j*MI + q*8 + (l/MI)*4 + r,
     // i.e. four consecutive columns per group of four registers (8 bytes of
     // bf16, converted with round-to-nearest-even); MI*MI/256 groups per tile.
     constexpr int NQ = MI * MI / 256;
+    const uint32_t wm = wave >> 1, wn = wave & 1;
     const uint32_t rloc = wm * 128u + (lane % (uint32_t)MI);
-    const uint32_t cloc = wn * 128u + khalf * 4u;
+    const uint32_t cloc = wn * 128u + (lane / (uint32_t)MI) * 4u;
     if (g.c_staged) {
         // Registers -> LDS -> global, as the pages' epilogue does: the
         // workgroup's 256 x 256 tile becomes four 256 x 64 box images of the
@@ -484,6 +290,423 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
                     if (row < g.M && col + e < g.N)
                         C[(uint64_t)row * g.ldc + col + e] = f32_to_bf16_rne(acc[i][j][4 * q + e]);
             }
+}
+
+// EDGE = false: every box is inside the tensors (M, N multiples of 256, K a
+// multiple of BK), copies use precomputed per-lane offsets.  EDGE = true: any
+// shape; boxes go through the general loader with zero fill at the edges.
+// SWM: the operands' swizzle mode (64B / 128B, or their _K256 forms).
+// MI: the MFMA shape, 32 (v_mfma_f32_32x32x16_bf16, 4 x 4 tiles per wave) or
+// 16 (v_mfma_f32_16x16x32_bf16, 8 x 8 tiles).  Both run 1024 flop per clock
+// per SIMD; the 16 x 16 form moves less accumulator and operand register
+// data per flop, which under the chip's power limit holds a higher clock.
+template <int BK, int S, bool EDGE, int SWM, int MI>
+__global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    constexpr uint32_t ROWB = BK * 2;                 // bytes per LDS row (128 or 64)
+    constexpr uint32_t BOX = kTM * ROWB;              // bytes per operand box
+    // Ring layout: the S A-box slots first, then the S B-box slots, so that
+    // slot s of either operand is s * BOX from slot 0 (with two slots that
+    // offset fits a ds_read immediate).
+    constexpr uint32_t BREG = (uint32_t)S * BOX;
+    constexpr uint32_t GROUPS = BOX / 1024;           // 1 KiB DMA groups per box
+    constexpr uint32_t GPW = GROUPS / 4;              // per wave and operand
+    constexpr uint32_t SW = SWM & 3;                  // swizzled chunk bits (3 or 2)
+    constexpr uint32_t KSH = (SWM & 4) ? 8u : 7u;     // key: 256- or 128-byte unit
+    constexpr uint32_t CPR = ROWB / 16;               // chunks per row
+    static_assert(MI == 32 || MI == 16, "MFMA shape");
+    constexpr int NI = 128 / MI, NJ = 128 / MI;       // MFMA tiles per wave block (rows, columns)
+    constexpr int NF = NI + NJ;                       // fragments per sub-step
+    constexpr uint32_t KMI = MI == 32 ? 16u : 32u;    // K extent of one MFMA
+    typedef std::conditional_t<MI == 32, f32x16, f32x4> AccT;
+
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t lane = lane_id();
+    uint32_t tm, tn;
+    gemm_block_tile(g, tm, tn);
+    const uint32_t m0 = tm * kTM, n0 = tn * kTN;
+    const uint32_t nk = (g.K + BK - 1) / BK;
+    constexpr bool interior = !EDGE;
+
+    // Per-lane source offsets inside a box (same for every K step): lane l of
+    // group j fills physical chunk p = j*64 + l with logical chunk swz(p).
+    const uint32_t lds0 = lds_addr_of(smem);
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t offA[GPW], offB[GPW];
+#pragma unroll
+    for (uint32_t j = 0; j < GPW; ++j) {
+        const uint32_t p = (wave * GPW + j) * 64u + lane;
+        const uint32_t q = swz_chunk(p, SWM);
+        const uint32_t row = q / CPR, ch = q % CPR;
+        offA[j] = row * (uint32_t)g.A.stride[0] + ch * 16u;
+        offB[j] = row * (uint32_t)g.B.stride[0] + ch * 16u;
+    }
+    const uint64_t baseA = g.A.base + (uint64_t)m0 * g.A.stride[0];
+    const uint64_t baseB = g.B.base + (uint64_t)n0 * g.B.stride[0];
+
+    // Whole-tile issue (prologue, and every copy of the general loader).
+    auto issue = [&](uint32_t kt, uint32_t slot) {
+        if constexpr (interior) {
+            const uint64_t ka = baseA + (uint64_t)kt * ROWB;
+            const uint64_t kb = baseB + (uint64_t)kt * ROWB;
+            const uint32_t la = lds0 + slot * BOX + wave_u * GPW * 1024u;
+#pragma unroll
+            for (uint32_t j = 0; j < GPW; ++j) dma16_sv(ka, offA[j], la + j * 1024u);
+#pragma unroll
+            for (uint32_t j = 0; j < GPW; ++j) dma16_sv(kb, offB[j], la + BREG + j * 1024u);
+        } else {
+            const int32_t ca[5] = {(int32_t)(kt * BK), (int32_t)m0, 0, 0, 0};
+            const int32_t cb[5] = {(int32_t)(kt * BK), (int32_t)n0, 0, 0, 0};
+            tile_load_issue(g.A, ca, smem + slot * BOX, wave, 4);
+            tile_load_issue(g.B, cb, smem + BREG + slot * BOX, wave, 4);
+        }
+    };
+
+    AccT acc[NI][NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = AccT{};
+
+    const uint32_t wm = wave >> 1, wn = wave & 1;
+    const uint32_t khalf = lane / (uint32_t)MI;      // which 8-element K chunk of the sub-step
+    constexpr uint32_t KK = BK / KMI;                 // MFMA sub-steps per stage (even)
+    static_assert(KK % 2 == 0, "fragment buffer parity assumes an even sub-step count");
+
+    // LDS address of fragment f (0..NI-1: A rows wm*128 + f*MI + l%MI; NI..:
+    // B) for sub-step kk, relative to the ring slot: lane l reads logical chunk
+    // (KMI/8)*kk + l/MI of its row at the physical chunk the swizzle gives.
+    // Loop invariant, so each read is one add of the slot offset.
+    uint32_t fad[KK][NF];
+#pragma unroll
+    for (uint32_t kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const uint32_t row = (f < NI ? wm : wn) * 128u + (uint32_t)(f % NI) * (uint32_t)MI + (lane % (uint32_t)MI);
+            const uint32_t rb = row * ROWB;
+            const uint32_t key = (rb >> KSH) & ((1u << SW) - 1u);
+            fad[kk][f] = lds0 + (f < NI ? 0u : BREG) + rb + ((((KMI / 8u) * kk + khalf) ^ key) << 4);
+        }
+    bf16x8 fr[2][NF];                                 // [sub-step parity][A rows, B columns]
+#pragma unroll
+    for (int f = 0; f < NF; ++f) fr[1][f] = bf16x8{};
+    if constexpr (MI == 16) {
+        acc_fence(acc);                               // accumulator writes before the first MFMA
+        asm volatile("s_nop 7" ::: "memory");
+    }
+
+    // One MFMA: B as the first operand, so each accumulator holds the
+    // transposed tile (consecutive C columns per lane).  The 16 x 16 form is
+    // inline asm with the accumulator tied to the destination: the builtin
+    // lets the register allocator split them and copy accumulators around.
+    auto mfma = [&](AccT& c, const bf16x8& b, const bf16x8& a) {
+        if constexpr (MI == 32) {
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+        } else {
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+        }
+    };
+
+    // One iteration runs from one workgroup barrier to the next:
+    //   phase A: accumulator rows NI-AR.. of the previous tile's last
+    //            sub-step (fragments already in registers), while reading
+    //            sub-step 0 of tile t;
+    //   phase B: sub-steps 0 .. KK-2 of tile t, reading the next sub-step;
+    //   phase C: rows 0 .. NI-AR-1 of tile t's last sub-step; then wait for
+    //            tile t+1's copies, and the barrier.
+    // The slot of tile t-1 is free from the start of the iteration (every
+    // wave passed the barrier after its last read of it), so tile t+S-1's
+    // copies go there, spread evenly over the first SPAN MFMAs: the CU's
+    // address unit takes 16 cycles per 1 KiB copy, and issued back to back
+    // they would hold the waves' MFMA streams.  Every MFMA slot is pinned by
+    // a scheduling barrier.  Iteration 0's phase A multiplies zero fragments
+    // into zero accumulators (an exact no-op).
+    constexpr int AR = MI == 16 ? 4 : 2;             // rows carried into the next iteration
+    typedef GemmSched<NI, NJ, (int)KK, AR> Sch;
+    constexpr int SLOTS = Sch::SLOTS;                // MFMAs per wave and iteration
+    constexpr int NDMA = 2 * (int)GPW;               // copies per wave and tile
+    constexpr int SPAN = S >= 3 ? SLOTS : (SLOTS * 3) / 8;
+    // slot_c: the slot of tile t as a compile-time constant (two-slot ring:
+    // the fragment reads carry it as an immediate offset, no per-read add),
+    // or -1 to add slot_t at run time.
+    auto iteration = [&](auto with_copies, auto slot_c, uint32_t t, uint32_t slot_t, uint32_t slot_fill,
+                         uint32_t later, bool wait_next) {
+        constexpr bool COPY = decltype(with_copies)::value;
+        constexpr int SC = decltype(slot_c)::value;
+        const uint32_t so = slot_t * BOX;
+        const uint64_t ka = baseA + (uint64_t)(t + S - 1) * ROWB;
+        const uint64_t kb = baseB + (uint64_t)(t + S - 1) * ROWB;
+        const uint32_t la = lds0 + slot_fill * BOX + wave_u * GPW * 1024u;
+        static_for<SLOTS>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            constexpr int W = Sch::lgkm(m);
+            if constexpr (W >= 0) {
+                wait_lgkm<W>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            constexpr int i = Sch::mi(m), j = Sch::mj(m), buf = Sch::mbuf(m);
+            mfma(acc[i][j], fr[buf][NI + j], fr[buf][i]);
+            constexpr int f = Sch::rfrag(m);
+            if constexpr (f >= 0) {
+                if constexpr (SC >= 0)
+                    fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16_off<(uint32_t)SC * BOX>(fad[Sch::rkk(m)][f]));
+                else
+                    fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16(fad[Sch::rkk(m)][f] + so));
+            }
+            if constexpr (COPY && interior) {
+                static_for<NDMA>([&](auto cc) {
+                    constexpr int c = decltype(cc)::value;
+                    if constexpr ((c * SPAN) / NDMA == m) {
+                        if constexpr (c < (int)GPW) dma16_sv(ka, offA[c], la + (uint32_t)c * 1024u);
+                        else dma16_sv(kb, offB[c - GPW], la + BREG + (uint32_t)(c - GPW) * 1024u);
+                    }
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if (wait_next) {
+            if constexpr (interior) wait_stage<2 * GPW, S - 2>(later);
+            else wait_vmcnt<0>();
+            wait_lgkm0();
+            wg_barrier();
+        } else {
+            // Last tile: rows NI-AR.. of its last sub-step, inside the
+            // iteration (the accumulators still sit where its MFMAs left
+            // them; the fragments come from asm reads the compiler believes
+            // complete at issue, hence the wait before any MFMA), then let
+            // every MFMA retire before code outside the loop touches them.
+            wait_lgkm0();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < Sch::HALF; ++m)
+                mfma(acc[NI - AR + m / NJ][m % NJ], fr[1][NI + m % NJ], fr[1][NI - AR + m / NJ]);
+            if constexpr (MI == 16) {
+                mfma_drain();
+                acc_fence(acc);
+            }
+        }
+    };
+
+    // Prologue: tiles 0 .. S-2 in flight; wait for tile 0.
+    const uint32_t pro = nk < (uint32_t)(S - 1) ? nk : (uint32_t)(S - 1);
+    for (uint32_t s = 0; s < pro; ++s) issue(s, s);
+    if constexpr (interior) wait_stage<2 * GPW, S - 2>(pro - 1);
+    else wait_vmcnt<0>();
+    wait_lgkm0();
+    wg_barrier();
+
+    // Iterations whose tile t+S-1 exists copy it into the slot of tile t-1.
+    // The general loader issues whole tiles up front and drains before each
+    // barrier.
+    uint32_t slot_t = 0, slot_fill = S - 1;
+    uint32_t t = 0;
+    const uint32_t nfull = nk >= (uint32_t)S ? nk - (uint32_t)S + 1u : 0u;
+    typedef std::integral_constant<bool, true> with_c;
+    typedef std::integral_constant<bool, false> without_c;
+    typedef std::integral_constant<int, -1> slot_rt;
+    if constexpr (S == 2 && interior) {
+        // tile t sits in slot t % 2: unroll by two so each body knows its slot
+        for (; t + 2 <= nfull; t += 2) {
+            iteration(with_c{}, std::integral_constant<int, 0>{}, t, 0u, 1u, 0u, true);
+            iteration(with_c{}, std::integral_constant<int, 1>{}, t + 1, 1u, 0u, 0u, true);
+        }
+        if (t < nfull) {
+            iteration(with_c{}, std::integral_constant<int, 0>{}, t, 0u, 1u, 0u, true);
+            ++t;
+        }
+        slot_t = t & 1u;
+        slot_fill = slot_t ^ 1u;
+    } else {
+        for (; t < nfull; ++t) {
+            if constexpr (!interior) issue(t + S - 1, slot_fill);
+            iteration(with_c{}, slot_rt{}, t, slot_t, slot_fill, (uint32_t)(S - 2), true);
+            slot_fill = slot_t;
+            slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
+        }
+    }
+    // Tiles without copies: the last S-1 (with two slots, only the last).
+    if constexpr (S > 2) {
+        for (; t + 1 < nk; ++t) {
+            // Tiles issued after tile t+1: t+2 .. nk-1.
+            iteration(without_c{}, slot_rt{}, t, slot_t, slot_fill, nk - t - 2, true);
+            slot_t = slot_t + 1 == (uint32_t)S ? 0u : slot_t + 1;
+        }
+    }
+    iteration(without_c{}, slot_rt{}, t, slot_t, slot_fill, 0u, false);
+    gemm_epilogue<MI>(g, acc, lds0, wave, lane, m0, n0);
+}
+
+// Five-unit ring for 32-deep boxes with 16 x 16 x 32 MFMAs.  A and B boxes
+// are 256 rows x 64 bytes (64-byte swizzle); an iteration consumes two units
+// (64 of K: sub-step 0 is unit 2t, sub-step 1 unit 2t+1) and copies, into the
+// two slots the previous iteration freed, the unit the next iteration needs
+// and the one the iteration after needs -- half of every tile gets two
+// iterations to land instead of one, and the copies spread over the whole
+// iteration.  Unit u lives in slot u % 5; five 32 KiB units fill the 160 KiB
+// LDS.  The loop is unrolled by five so every body knows its slots: the
+// fragment reads carry them as immediate offsets (slot 4, 64 KiB up, from a
+// second set of base addresses).  M, N multiples of 256 and K of 64.
+template <int SWM>
+__global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16_r5(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    constexpr int RING = 5;
+    constexpr uint32_t ROWB = 64;                     // 32 bf16 per LDS row
+    constexpr uint32_t UBOX = kTM * ROWB;             // 16 KiB per operand unit
+    constexpr uint32_t BREG = RING * UBOX;            // B slots after the A slots
+    constexpr uint32_t GPW = UBOX / 1024 / 4;         // copies per wave and operand per unit
+    constexpr uint32_t SW = SWM & 3;
+    constexpr uint32_t KSH = (SWM & 4) ? 8u : 7u;
+    constexpr uint32_t CPR = ROWB / 16;
+    constexpr int MI = 16, NI = 8, NJ = 8, NF = NI + NJ;
+    constexpr int NDMA = 2 * (int)GPW;                // copies per wave per unit
+    typedef f32x4 AccT;
+    static_assert(SW == 2, "64-byte rows take the 64-byte swizzle");
+
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t lane = lane_id();
+    uint32_t tm, tn;
+    gemm_block_tile(g, tm, tn);
+    const uint32_t m0 = tm * kTM, n0 = tn * kTN;
+    const uint32_t NU = g.K / 32u;                   // units (even)
+    const uint32_t NT = NU / 2u;                     // iterations
+    const uint32_t lds0 = lds_addr_of(smem);
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+    uint32_t offA[GPW], offB[GPW];
+#pragma unroll
+    for (uint32_t j = 0; j < GPW; ++j) {
+        const uint32_t p = (wave * GPW + j) * 64u + lane;
+        const uint32_t q = swz_chunk(p, SWM);
+        const uint32_t row = q / CPR, ch = q % CPR;
+        offA[j] = row * (uint32_t)g.A.stride[0] + ch * 16u;
+        offB[j] = row * (uint32_t)g.B.stride[0] + ch * 16u;
+    }
+    const uint64_t baseA = g.A.base + (uint64_t)m0 * g.A.stride[0];
+    const uint64_t baseB = g.B.base + (uint64_t)n0 * g.B.stride[0];
+    // Copy c (0..NDMA-1) of unit u into slot `slot`.
+    auto copy_unit = [&](uint32_t u, uint32_t slot, int c) {
+        const uint32_t la = lds0 + slot * UBOX + wave_u * GPW * 1024u;
+        if (c < (int)GPW) dma16_sv(baseA + (uint64_t)u * ROWB, offA[c], la + (uint32_t)c * 1024u);
+        else dma16_sv(baseB + (uint64_t)u * ROWB, offB[c - GPW], la + BREG + (uint32_t)(c - GPW) * 1024u);
+    };
+
+    AccT acc[NI][NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = AccT{};
+    const uint32_t wm = wave >> 1, wn = wave & 1;
+    // Fragment f of a unit in slot 0 (lane l: row l % 16 of the fragment,
+    // chunk l / 16 of its 64-byte row); slot s is s * UBOX further, slot 4
+    // from the second set.
+    uint32_t fad[NF], fad4[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const uint32_t row = (f < NI ? wm : wn) * 128u + (uint32_t)(f % NI) * 16u + (lane & 15u);
+        const uint32_t rb = row * ROWB;
+        const uint32_t key = (rb >> KSH) & ((1u << SW) - 1u);
+        fad[f] = lds0 + (f < NI ? 0u : BREG) + rb + (((lane >> 4) ^ key) << 4);
+        fad4[f] = fad[f] + 4u * UBOX;
+    }
+    bf16x8 fr[2][NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) fr[1][f] = bf16x8{};
+    acc_fence(acc);
+    asm volatile("s_nop 7" ::: "memory");
+    auto mfma = [&](AccT& c, const bf16x8& b, const bf16x8& a) {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+    };
+
+    // Copies past the last unit re-read unit NU-1 instead (no branch in the
+    // MFMA stream): they land in slots no later iteration reads, and the
+    // wait before the epilogue drains them.
+    const uint32_t ulast = NU - 1u;
+    auto clamp_unit = [&](uint32_t u) { return u < ulast ? u : ulast; };
+
+    // Prologue: units 0, 1, 2 into their slots; wait for 0 and 1.
+    for (uint32_t u = 0; u < 3u; ++u)
+#pragma unroll
+        for (int c = 0; c < NDMA; ++c) copy_unit(clamp_unit(u), u, c);
+    wait_vmcnt<NDMA>();
+    wait_lgkm0();
+    wg_barrier();
+
+    // Iteration t (R = t % 5 fixes its slots at compile time) copies unit
+    // 2t+3 over its first half and unit 2t+4 over its second; units 2t+2
+    // and 2t+3 have landed once at most unit 2t+4's copies (issued last) are
+    // in flight.
+    typedef GemmSched<NI, NJ, 2, 4> Sch;
+    constexpr int SLOTS = Sch::SLOTS;
+    constexpr int HALFS = SLOTS / 2;
+    static_assert(HALFS % NDMA == 0, "copy spacing");
+    auto body = [&](auto rc, uint32_t t) {
+        constexpr int R = decltype(rc)::value;
+        constexpr int SA = (2 * R) % RING, SB = (2 * R + 1) % RING;
+        constexpr uint32_t F1 = (2 * R + 3) % RING, F2 = (2 * R + 4) % RING;
+        const uint32_t u1 = clamp_unit(2u * t + 3u), u2 = clamp_unit(2u * t + 4u);
+        static_for<SLOTS>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            constexpr int W = Sch::lgkm(m);
+            if constexpr (W >= 0) {
+                wait_lgkm<W>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            constexpr int i = Sch::mi(m), j = Sch::mj(m), buf = Sch::mbuf(m);
+            mfma(acc[i][j], fr[buf][NI + j], fr[buf][i]);
+            constexpr int f = Sch::rfrag(m);
+            if constexpr (f >= 0) {
+                constexpr int slot = Sch::rkk(m) == 0 ? SA : SB;
+                if constexpr (slot < 4)
+                    fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16_off<(uint32_t)slot * UBOX>(fad[f]));
+                else
+                    fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16_off<0u>(fad4[f]));
+            }
+            if constexpr (m % (HALFS / NDMA) == 0) {
+                constexpr int c = (m % HALFS) / (HALFS / NDMA);
+                if constexpr (m < HALFS) copy_unit(u1, F1, c);
+                else copy_unit(u2, F2, c);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        wait_vmcnt<NDMA>();
+        wait_lgkm0();
+        wg_barrier();
+        if (t + 1u == NT) {
+            // Rows 4.. of the last sub-step, inside the body: the
+            // accumulators still sit where this body's MFMAs left them.
+            // Then every MFMA retires before code outside the loop (the
+            // compiler's own accumulator copies and spills included) reads
+            // or writes an accumulator.
+            wait_vmcnt<0>();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < Sch::HALF; ++m) mfma(acc[4 + m / NJ][m % NJ], fr[1][NI + m % NJ], fr[1][4 + m / NJ]);
+            mfma_drain();
+            acc_fence(acc);
+        }
+    };
+    for (uint32_t t = 0; t < NT; t += 5u) {
+        body(std::integral_constant<int, 0>{}, t);
+        if (t + 1u < NT) body(std::integral_constant<int, 1>{}, t + 1u);
+        if (t + 2u < NT) body(std::integral_constant<int, 2>{}, t + 2u);
+        if (t + 3u < NT) body(std::integral_constant<int, 3>{}, t + 3u);
+        if (t + 4u < NT) body(std::integral_constant<int, 4>{}, t + 4u);
+    }
+    gemm_epilogue<MI>(g, acc, lds0, wave, lane, m0, n0);
+}
+
+template <int SWM>
+static tmap_status launch_gemm_r5(const GemmArgs& g, hipStream_t st) {
+    constexpr uint32_t lds = 5u * 2u * kTM * 64u;     // 160 KiB: the ring (the C image reuses it)
+    uint32_t limit = 0;
+    tmap_status s = device_lds_limit(&limit);
+    if (s) return s;
+    if (lds > limit) return TMAP_ERR_UNSUPPORTED;
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16_r5<SWM>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+    hipLaunchKernelGGL((k_gemm_bf16_r5<SWM>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st, g);
+    return check_launch("gemm_bf16");
 }
 
 template <int BK, int S, bool EDGE, int SWM, int MI>
@@ -593,7 +816,15 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
     case 2: return launch_gemm<32, 2>(g, swa, mfma, st);
     case 3: return launch_gemm<32, 3>(g, swa, mfma, st);
     case 4: return launch_gemm<32, 4>(g, swa, mfma, st);
-    case 5: return launch_gemm<32, 5>(g, swa, mfma, st);
+    case 5:
+        // whole tiles and K a multiple of 64: the five-unit ring with
+        // 16 x 16 x 32 MFMAs (two units per iteration)
+        if (mfma != 32 && M % kTM == 0 && N % kTN == 0 && K % 64u == 0) {
+            if (swa & 4u) return launch_gemm_r5<TMAP_SWIZZLE_64B_K256>(g, st);
+            return launch_gemm_r5<TMAP_SWIZZLE_64B>(g, st);
+        }
+        if (mfma == 16) return TMAP_ERR_UNSUPPORTED;
+        return launch_gemm<32, 5>(g, swa, 32, st);
     default: return TMAP_ERR_UNSUPPORTED;
     }
 }
