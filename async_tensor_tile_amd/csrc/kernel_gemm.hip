@@ -536,39 +536,41 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     gemm_epilogue<MI>(g, acc, lds0, wave, lane, m0, n0);
 }
 
-// Five-unit ring for 32-deep boxes with 16 x 16 x 32 MFMAs.  A and B boxes
-// are 256 rows x 64 bytes (64-byte swizzle); an iteration consumes two units
-// (64 of K: sub-step 0 is unit 2t, sub-step 1 unit 2t+1) and copies, into the
-// two slots the previous iteration freed, the unit the next iteration needs
-// and the one the iteration after needs -- half of every tile gets two
-// iterations to land instead of one, and the copies spread over the whole
-// iteration.  Unit u lives in slot u % 5; five 32 KiB units fill the 160 KiB
-// LDS.  The loop is unrolled by five so every body knows its slots: the
-// fragment reads carry them as immediate offsets (slot 4, 64 KiB up, from a
-// second set of base addresses).  M, N multiples of 256 and K of 64.
+// Operand ring for 64-deep boxes with 16 x 16 x 32 MFMAs: five 32 KiB slots
+// (the whole 160 KiB LDS) hold operand boxes, A's box of K-step k as unit 2k
+// and B's as unit 2k+1, unit u in slot u % 5.  Iteration t reads A_t and
+// B_t; over its first third it copies B_{t+1}, over the rest A_{t+2}, into
+// the two slots that A_{t-1} and B_{t-1} left.  A is thus three deep
+// and B two deep: the A copies get a whole extra iteration to land, and the
+// copies spread over the whole iteration (the CU's address unit takes 16
+// cycles per 1 KiB copy, half of the iteration's MFMA time).  The loop is
+// unrolled by five, so every body knows its slots.  Fragment reads need one
+// base address per (operand, sub-step, 64 KiB window): the 128-byte swizzle
+// key of a fragment row depends only on the lane (fragments start on 16-row
+// boundaries), so fragment f of a slot sits f * 2048 bytes further and the
+// slot offset within the window rides in the ds_read immediate too.  M, N
+// multiples of 256 and K of 64.
 template <int SWM>
-__global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16_r5(GemmArgs g) {
+__global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16_ring5(GemmArgs g) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    constexpr int RING = 5;
-    constexpr uint32_t ROWB = 64;                     // 32 bf16 per LDS row
-    constexpr uint32_t UBOX = kTM * ROWB;             // 16 KiB per operand unit
-    constexpr uint32_t BREG = RING * UBOX;            // B slots after the A slots
-    constexpr uint32_t GPW = UBOX / 1024 / 4;         // copies per wave and operand per unit
+    constexpr uint32_t RING = 5;
+    constexpr uint32_t ROWB = 128;                    // 64 bf16 per LDS row
+    constexpr uint32_t UBOX = kTM * ROWB;             // 32 KiB: one operand box
+    constexpr uint32_t GPW = UBOX / 1024 / 4;         // copies per wave and unit
     constexpr uint32_t SW = SWM & 3;
     constexpr uint32_t KSH = (SWM & 4) ? 8u : 7u;
     constexpr uint32_t CPR = ROWB / 16;
     constexpr int MI = 16, NI = 8, NJ = 8, NF = NI + NJ;
-    constexpr int NDMA = 2 * (int)GPW;                // copies per wave per unit
+    constexpr int NDMA = (int)GPW;
     typedef f32x4 AccT;
-    static_assert(SW == 2, "64-byte rows take the 64-byte swizzle");
+    static_assert(SW == 3, "128-byte rows take the 128-byte swizzle");
 
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t lane = lane_id();
     uint32_t tm, tn;
     gemm_block_tile(g, tm, tn);
     const uint32_t m0 = tm * kTM, n0 = tn * kTN;
-    const uint32_t NU = g.K / 32u;                   // units (even)
-    const uint32_t NT = NU / 2u;                     // iterations
+    const uint32_t NT = g.K / 64u;                   // K-steps
     const uint32_t lds0 = lds_addr_of(smem);
     const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
 
@@ -583,12 +585,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     }
     const uint64_t baseA = g.A.base + (uint64_t)m0 * g.A.stride[0];
     const uint64_t baseB = g.B.base + (uint64_t)n0 * g.B.stride[0];
-    // Copy c (0..NDMA-1) of unit u into slot `slot`.
-    auto copy_unit = [&](uint32_t u, uint32_t slot, int c) {
-        const uint32_t la = lds0 + slot * UBOX + wave_u * GPW * 1024u;
-        if (c < (int)GPW) dma16_sv(baseA + (uint64_t)u * ROWB, offA[c], la + (uint32_t)c * 1024u);
-        else dma16_sv(baseB + (uint64_t)u * ROWB, offB[c - GPW], la + BREG + (uint32_t)(c - GPW) * 1024u);
+    // K-steps past the last re-read the last one instead (no branch in the
+    // MFMA stream): they land in slots no later iteration reads, and the
+    // last iteration drains them before the epilogue reuses the LDS.
+    const uint32_t klast = NT - 1u;
+    auto clamp_k = [&](uint32_t k) { return k < klast ? k : klast; };
+    // Copy c (0..NDMA-1) of operand OP's box of K-step k into slot `slot`.
+    auto copy_unit = [&](auto opc, uint32_t k, uint32_t slot, int c) {
+        constexpr int OP = decltype(opc)::value;
+        const uint32_t la = lds0 + slot * UBOX + wave_u * GPW * 1024u + (uint32_t)c * 1024u;
+        if constexpr (OP == 0) dma16_sv(baseA + (uint64_t)k * ROWB, offA[c], la);
+        else dma16_sv(baseB + (uint64_t)k * ROWB, offB[c], la);
     };
+    typedef std::integral_constant<int, 0> opA;
+    typedef std::integral_constant<int, 1> opB;
 
     AccT acc[NI][NJ];
 #pragma unroll
@@ -596,17 +606,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = AccT{};
     const uint32_t wm = wave >> 1, wn = wave & 1;
-    // Fragment f of a unit in slot 0 (lane l: row l % 16 of the fragment,
-    // chunk l / 16 of its 64-byte row); slot s is s * UBOX further, slot 4
-    // from the second set.
-    uint32_t fad[NF], fad4[NF];
+    // Lane l reads row l % 16 of each fragment and logical chunk 4kk + l/16
+    // of it; base address per operand, sub-step kk and 64 KiB window w.
+    uint32_t fa[2][3], fb[2][3];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        const uint32_t row = (f < NI ? wm : wn) * 128u + (uint32_t)(f % NI) * 16u + (lane & 15u);
-        const uint32_t rb = row * ROWB;
-        const uint32_t key = (rb >> KSH) & ((1u << SW) - 1u);
-        fad[f] = lds0 + (f < NI ? 0u : BREG) + rb + (((lane >> 4) ^ key) << 4);
-        fad4[f] = fad[f] + 4u * UBOX;
+    for (uint32_t kk = 0; kk < 2; ++kk) {
+        const uint32_t ra = (wm * 128u + (lane & 15u)) * ROWB, rbb = (wn * 128u + (lane & 15u)) * ROWB;
+        const uint32_t ka = (ra >> KSH) & 7u, kb = (rbb >> KSH) & 7u;
+        const uint32_t ch = 4u * kk + (lane >> 4);
+#pragma unroll
+        for (uint32_t w = 0; w < 3; ++w) {
+            fa[kk][w] = lds0 + w * 65536u + ra + ((ch ^ ka) << 4);
+            fb[kk][w] = lds0 + w * 65536u + rbb + ((ch ^ kb) << 4);
+        }
     }
     bf16x8 fr[2][NF];
 #pragma unroll
@@ -617,33 +629,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
     };
 
-    // Copies past the last unit re-read unit NU-1 instead (no branch in the
-    // MFMA stream): they land in slots no later iteration reads, and the
-    // wait before the epilogue drains them.
-    const uint32_t ulast = NU - 1u;
-    auto clamp_unit = [&](uint32_t u) { return u < ulast ? u : ulast; };
-
-    // Prologue: units 0, 1, 2 into their slots; wait for 0 and 1.
-    for (uint32_t u = 0; u < 3u; ++u)
+    // Prologue: A_0, B_0, A_1 into slots 0, 1, 2; wait for A_0 and B_0.
 #pragma unroll
-        for (int c = 0; c < NDMA; ++c) copy_unit(clamp_unit(u), u, c);
+    for (int c = 0; c < NDMA; ++c) copy_unit(opA{}, 0u, 0u, c);
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) copy_unit(opB{}, 0u, 1u, c);
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) copy_unit(opA{}, clamp_k(1u), 2u, c);
     wait_vmcnt<NDMA>();
     wait_lgkm0();
     wg_barrier();
 
-    // Iteration t (R = t % 5 fixes its slots at compile time) copies unit
-    // 2t+3 over its first half and unit 2t+4 over its second; units 2t+2
-    // and 2t+3 have landed once at most unit 2t+4's copies (issued last) are
-    // in flight.
     typedef GemmSched<NI, NJ, 2, 4> Sch;
     constexpr int SLOTS = Sch::SLOTS;
-    constexpr int HALFS = SLOTS / 2;
-    static_assert(HALFS % NDMA == 0, "copy spacing");
+    constexpr int BSP = 5, AST = 48, ASP = 10;       // copy placement (MFMA slots)
+    static_assert(BSP * NDMA <= AST && AST + ASP * (NDMA - 1) < SLOTS, "copy placement");
     auto body = [&](auto rc, uint32_t t) {
-        constexpr int R = decltype(rc)::value;
-        constexpr int SA = (2 * R) % RING, SB = (2 * R + 1) % RING;
-        constexpr uint32_t F1 = (2 * R + 3) % RING, F2 = (2 * R + 4) % RING;
-        const uint32_t u1 = clamp_unit(2u * t + 3u), u2 = clamp_unit(2u * t + 4u);
+        constexpr int R = decltype(rc)::value;        // t % 5
+        constexpr uint32_t SA = (2u * R) % RING, SB = (2u * R + 1u) % RING;
+        constexpr uint32_t F1 = (2u * R + 3u) % RING, F2 = (2u * R + 4u) % RING;
+        const uint32_t kb1 = clamp_k(t + 1u), ka2 = clamp_k(t + 2u);
         static_for<SLOTS>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
             constexpr int W = Sch::lgkm(m);
@@ -655,28 +660,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
             mfma(acc[i][j], fr[buf][NI + j], fr[buf][i]);
             constexpr int f = Sch::rfrag(m);
             if constexpr (f >= 0) {
-                constexpr int slot = Sch::rkk(m) == 0 ? SA : SB;
-                if constexpr (slot < 4)
-                    fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16_off<(uint32_t)slot * UBOX>(fad[f]));
-                else
-                    fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16_off<0u>(fad4[f]));
+                constexpr int kk = Sch::rkk(m);
+                constexpr uint32_t slot = f < NI ? SA : SB;
+                constexpr uint32_t imm = (slot & 1u) * UBOX + (uint32_t)(f % NI) * 16u * ROWB;
+                const uint32_t base = f < NI ? fa[kk][slot >> 1] : fb[kk][slot >> 1];
+                fr[Sch::rbuf(m)][f] = __builtin_bit_cast(bf16x8, lds_read16_off<imm>(base));
             }
-            if constexpr (m % (HALFS / NDMA) == 0) {
-                constexpr int c = (m % HALFS) / (HALFS / NDMA);
-                if constexpr (m < HALFS) copy_unit(u1, F1, c);
-                else copy_unit(u2, F2, c);
-            }
+            // B_{t+1} early (it must land by the end of this iteration), one
+            // copy every BSP slots; A_{t+2} over the rest, every ASP slots
+            if constexpr (m < BSP * NDMA && m % BSP == 0) copy_unit(opB{}, kb1, F1, m / BSP);
+            if constexpr (m >= AST && (m - AST) % ASP == 0 && (m - AST) / ASP < NDMA)
+                copy_unit(opA{}, ka2, F2, (m - AST) / ASP);
             __builtin_amdgcn_sched_barrier(0);
         });
+        // A_{t+1} and B_{t+1} have landed once at most A_{t+2}'s copies
+        // (issued last) are in flight
         wait_vmcnt<NDMA>();
         wait_lgkm0();
         wg_barrier();
         if (t + 1u == NT) {
-            // Rows 4.. of the last sub-step, inside the body: the
-            // accumulators still sit where this body's MFMAs left them.
-            // Then every MFMA retires before code outside the loop (the
-            // compiler's own accumulator copies and spills included) reads
-            // or writes an accumulator.
+            // Rows 4.. of the last sub-step, inside the body, where the
+            // accumulators still sit; then drain (the clamped copies too)
+            // before code outside the loop touches accumulators or LDS.
             wait_vmcnt<0>();
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -696,16 +701,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
 }
 
 template <int SWM>
-static tmap_status launch_gemm_r5(const GemmArgs& g, hipStream_t st) {
-    constexpr uint32_t lds = 5u * 2u * kTM * 64u;     // 160 KiB: the ring (the C image reuses it)
+static tmap_status launch_gemm_ring5(const GemmArgs& g, hipStream_t st) {
+    constexpr uint32_t lds = 5u * kTM * 128u;        // 160 KiB: the ring (the C image reuses it)
     uint32_t limit = 0;
     tmap_status s = device_lds_limit(&limit);
     if (s) return s;
     if (lds > limit) return TMAP_ERR_UNSUPPORTED;
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16_r5<SWM>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16_ring5<SWM>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-    hipLaunchKernelGGL((k_gemm_bf16_r5<SWM>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st, g);
+    hipLaunchKernelGGL((k_gemm_bf16_ring5<SWM>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st, g);
     return check_launch("gemm_bf16");
 }
 
@@ -810,21 +815,20 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
     hipStream_t st = as_stream(stream);
     if (bka == 64) {
         if (stages == 2) return launch_gemm<64, 2>(g, swa, mfma, st);
+        if (stages == 3) {
+            // A three deep, B two deep in five operand slots: whole tiles,
+            // K a multiple of 64, 16 x 16 x 32 MFMAs
+            if (mfma == 32 || M % kTM || N % kTN || K % 64u) return TMAP_ERR_UNSUPPORTED;
+            if (swa & 4u) return launch_gemm_ring5<TMAP_SWIZZLE_128B_K256>(g, st);
+            return launch_gemm_ring5<TMAP_SWIZZLE_128B>(g, st);
+        }
         return TMAP_ERR_UNSUPPORTED;
     }
     switch (stages) {
     case 2: return launch_gemm<32, 2>(g, swa, mfma, st);
     case 3: return launch_gemm<32, 3>(g, swa, mfma, st);
     case 4: return launch_gemm<32, 4>(g, swa, mfma, st);
-    case 5:
-        // whole tiles and K a multiple of 64: the five-unit ring with
-        // 16 x 16 x 32 MFMAs (two units per iteration)
-        if (mfma != 32 && M % kTM == 0 && N % kTN == 0 && K % 64u == 0) {
-            if (swa & 4u) return launch_gemm_r5<TMAP_SWIZZLE_64B_K256>(g, st);
-            return launch_gemm_r5<TMAP_SWIZZLE_64B>(g, st);
-        }
-        if (mfma == 16) return TMAP_ERR_UNSUPPORTED;
-        return launch_gemm<32, 5>(g, swa, 32, st);
+    case 5: return launch_gemm<32, 5>(g, swa, mfma, st);
     default: return TMAP_ERR_UNSUPPORTED;
     }
 }

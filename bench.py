@@ -163,9 +163,9 @@ def run_extra(att, torch, stream, reps: int):
 
 
 # (K step, operand swizzle, ring stages, MFMA shape: 16 = 16x16x32, 32 = 32x32x16)
-GEMM_VARIANTS = ((64, "128b_k256", 2, 16), (32, "64b_k256", 5, 16), (64, "128b_k256", 2, 32), (64, "128b", 2, 16),
+GEMM_VARIANTS = ((64, "128b_k256", 3, 16), (64, "128b_k256", 2, 16), (64, "128b_k256", 2, 32), (64, "128b", 2, 16),
                  (32, "64b_k256", 4, 32), (32, "64b_k256", 3, 32), (32, "64b", 4, 32))
-GEMM_DEFAULT = (64, "128b_k256", 2, 16)
+GEMM_DEFAULT = (64, "128b_k256", 3, 16)
 BF16_PEAK_TFLOPS = 2500.0
 
 

@@ -305,10 +305,13 @@ tmap_status hbm_probe(int32_t kind, const void* d_src, void* d_dst, uint64_t byt
  * `stages`-deep LDS ring and consumed by MFMA bf16 with fp32 accumulation.
  * d_C is M x N row-major bf16 (round to nearest even), leading dimension
  * ldc >= N elements.  Ragged M, N, K are handled by the maps' zero fill and a
- * masked epilogue.  stages = 2 for the 64-deep K step (two 64 KiB stages
- * fit the 160 KiB LDS, three do not).  Errors: NULL, UNSUPPORTED (map shape,
- * dtype, box, swizzle, OOB fill other than zero, stages, ldc < N), HIP.
- * M == 0 or N == 0 is a no-op. */
+ * masked epilogue.  For the 64-deep K step, stages = 2 is the double buffer
+ * (two 64 KiB stages; three do not fit the 160 KiB LDS) and stages = 3 the
+ * operand ring: five 32 KiB slots holding A and B boxes in turn, so that A
+ * runs three deep and B two deep; it takes M and N multiples of 256 and K a
+ * multiple of 64.  Errors: NULL, UNSUPPORTED (map shape, dtype, box,
+ * swizzle, OOB fill other than zero, stages, shape for stages = 3, ldc < N),
+ * HIP.  M == 0 or N == 0 is a no-op. */
 tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
                       uint32_t K, uint32_t ldc, uint32_t stages, void* stream);
 
@@ -318,9 +321,10 @@ tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, u
  * tile grid divides).  Maps
  * with box {32, 256} and TMAP_SWIZZLE_64B or TMAP_SWIZZLE_64B_K256 select the
  * 32-deep K step, for which stages may be 2 to 5; box {64, 256} takes
- * stages = 2.  `mfma` picks the matrix instruction: 16 (16x16x32 tiles, the
- * default for the 64-deep step), 32 (32x32x16 tiles, the only form for the
- * 32-deep step) or 0 for the default; others return ERR_UNSUPPORTED. */
+ * stages 2 or 3 as above.  `mfma` picks the matrix instruction: 16 (16x16x32
+ * tiles, the default for the 64-deep step and the only form of its operand
+ * ring), 32 (32x32x16 tiles, the only form for the 32-deep step) or 0 for
+ * the default; others return ERR_UNSUPPORTED. */
 tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
                          uint32_t K, uint32_t ldc, uint32_t stages, uint32_t group_m, uint32_t xcd,
                          uint32_t mfma, void* stream);

@@ -62,8 +62,8 @@ def check_close(got_bits, ref):
 
 
 @pytest.mark.parametrize("k256", [False, True])
-@pytest.mark.parametrize("bk,stages,mfma", [(64, 2, 16), (64, 2, 32), (32, 2, 32), (32, 3, 32), (32, 4, 32),
-                                           (32, 5, 16), (32, 5, 32)])
+@pytest.mark.parametrize("bk,stages,mfma", [(64, 2, 16), (64, 2, 32), (64, 3, 16), (32, 2, 32), (32, 3, 32),
+                                           (32, 4, 32), (32, 5, 32)])
 def test_identity_exact(bk, stages, mfma, k256):
     """A = I: C equals B exactly (one product per output, exact in fp32)."""
     K = N = 512
@@ -88,36 +88,32 @@ def test_mfma_shape_argument():
 
 @pytest.mark.parametrize("K", [64, 128, 192, 320, 384, 704])
 @pytest.mark.parametrize("k256", [False, True])
-def test_five_unit_ring(K, k256):
-    """32-deep boxes, five stages, whole tiles: the five-unit ring (two units
-    per iteration, loop unrolled by five).  K from one iteration up to two
-    unrolled groups plus one, so every slot pattern and the clamped copies
-    past the last unit run."""
+def test_operand_ring(K, k256):
+    """64-deep boxes, three stages, whole tiles: the five-slot operand ring
+    (A three deep, B two deep, loop unrolled by five).  K from one K-step up
+    to two unrolled groups plus one, so every slot pattern and the clamped
+    copies past the last K-step run."""
     M, N = 512, 256
-    say("gemm r5", K, k256)
+    say("gemm ring5", K, k256)
     A = synthgen.normal_bf16_bits(58, (M, K))
     Bt = synthgen.normal_bf16_bits(59, (N, K))
-    C = run_gemm(A, Bt, M, N, K, 32, 5, k256=k256, mfma=16)
+    C = run_gemm(A, Bt, M, N, K, 64, 3, k256=k256, mfma=16)
     rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     ref = oracle.gemm_bf16_sample(A, Bt, K, rows.reshape(-1), cols.reshape(-1)).reshape(M, N)
     check_close(C, ref)
 
 
-def test_five_unit_ring_shape_limits():
-    """The five-unit ring takes whole 256 x 256 tiles and K a multiple of 64:
-    other shapes with mfma 16 are rejected, with mfma 0 they take the
-    32 x 32 five-stage ring."""
-    A = np.zeros((300, 96), dtype=np.uint16)
-    with pytest.raises(att.TmapError) as ei:
-        run_gemm(A, A, 300, 300, 96, 32, 5, mfma=16)
-    assert ei.value.name == "ERR_UNSUPPORTED"
-    M, N, K = 300, 200, 96
-    A = synthgen.normal_bf16_bits(60, (M, K))
-    Bt = synthgen.normal_bf16_bits(61, (N, K))
-    C = run_gemm(A, Bt, M, N, K, 32, 5, mfma=0)
-    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
-    ref = oracle.gemm_bf16_sample(A, Bt, K, rows.reshape(-1), cols.reshape(-1)).reshape(M, N)
-    check_close(C, ref)
+def test_operand_ring_shape_limits():
+    """The operand ring takes whole 256 x 256 tiles, K a multiple of 64 and
+    16 x 16 x 32 MFMAs; other requests for three 64-deep stages are
+    rejected, as are 16 x 16 MFMAs with 32-deep boxes."""
+    A = np.zeros((300, 128), dtype=np.uint16)
+    for args in [(300, 256, 128, 64, 3, 0), (256, 256, 96, 64, 3, 16), (256, 256, 128, 64, 3, 32),
+                 (256, 256, 128, 32, 5, 16)]:
+        M, N, K, bk, st, mf = args
+        with pytest.raises(att.TmapError) as ei:
+            run_gemm(A[:M, :K], A[:N, :K], M, N, K, bk, st, mfma=mf)
+        assert ei.value.name == "ERR_UNSUPPORTED", args
 
 
 def test_permutation_exact():
@@ -147,7 +143,7 @@ def test_against_oracle_full(M, N, K, bk, stages, k256, mfma):
 
 
 @pytest.mark.parametrize("bk,stages,k256,mfma", [(64, 2, False, 0), (32, 4, True, 0), (64, 2, True, 16),
-                                                 (64, 2, True, 32), (32, 5, True, 16)])
+                                                 (64, 2, True, 32), (64, 3, True, 16)])
 def test_8192_sampled(bk, stages, k256, mfma):
     ex = W.GEMM_8192
     M, N, K = ex["M"], ex["N"], ex["K"]
