@@ -103,6 +103,48 @@ def test_operand_ring(K, k256):
     check_close(C, ref)
 
 
+@pytest.mark.parametrize("K", [64, 128, 192, 576])
+def test_operand_ring_many_tiles_exact(K):
+    """More 256 x 256 tiles (17 x 17) than the GPU has CUs, so workgroups of
+    the operand ring run in several rounds.  A selects one K index per row
+    (A[m, sel[m]] = 1), so C[m, :] = B[sel[m], :] exactly: every output of
+    every tile checked."""
+    M = N = 17 * 256
+    say("gemm ring5 many tiles", K)
+    sel = synthgen.rng(62).integers(0, K, M)
+    A = np.zeros((M, K), dtype=np.uint16)
+    A[np.arange(M), sel] = 0x3F80
+    Bt = synthgen.normal_bf16_bits(63, (N, K))
+    C = run_gemm(A, Bt, M, N, K, 64, 3, k256=True, mfma=16)
+    np.testing.assert_array_equal(C, Bt[:, sel].T)
+
+
+@pytest.mark.parametrize("offset,ldc", [(0, 264), (1, 264), (0, 258)])
+def test_operand_ring_c_leading_dimension(offset, ldc):
+    """The operand ring's C epilogue with leading dimension ldc >= N: the
+    LDS-staged tile store (16-byte aligned C, ldc a multiple of 8) and the
+    element stores otherwise; padding columns and the bytes around C stay
+    untouched."""
+    M, N, K = 512, 256, 192
+    say("gemm ring5 ldc", offset, ldc)
+    A = synthgen.normal_bf16_bits(64, (M, K))
+    Bt = synthgen.normal_bf16_bits(65, (N, K))
+    Ad = torch.from_numpy(A.view(np.int16)).cuda()
+    Bd = torch.from_numpy(Bt.view(np.int16)).cuda()
+    buf = torch.full((M * ldc + 16,), 0x7FFF, dtype=torch.int16, device="cuda")
+    mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (64, 256), None, "128b_k256")
+    mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (64, 256), None, "128b_k256")
+    att.gemm_bf16(mA, mB, buf.data_ptr() + 2 * offset, M, N, K, ldc, 3, stream())
+    torch.cuda.synchronize()
+    out = buf.cpu().numpy().view(np.uint16)
+    C = out[offset:offset + M * ldc].reshape(M, ldc)
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ref = oracle.gemm_bf16_sample(A, Bt, K, rows.reshape(-1), cols.reshape(-1)).reshape(M, N)
+    check_close(C[:, :N], ref)
+    assert (C[:, N:] == 0x7FFF).all()
+    assert (out[:offset] == 0x7FFF).all() and (out[offset + M * ldc:] == 0x7FFF).all()
+
+
 def test_operand_ring_shape_limits():
     """The operand ring takes whole 256 x 256 tiles, K a multiple of 64 and
     16 x 16 x 32 MFMAs; other requests for three 64-deep stages are
