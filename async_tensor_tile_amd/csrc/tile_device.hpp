@@ -423,6 +423,51 @@ __device__ __forceinline__ void reduce_minmax_element(uint8_t dtype, gbyte* dst,
     }
 }
 
+// One 8- or 16-bit element of a reduction, raw bits in and out: the same
+// arithmetic as reduce_add_element / reduce_minmax_element.
+template <int OP>
+__device__ __forceinline__ uint32_t reduce_sub_value(uint8_t dtype, uint32_t cur, uint32_t v) {
+    if constexpr (OP == ST_ADD) {
+        switch (dtype) {
+        case TMAP_U8: return (cur + v) & 0xFFu;
+        case TMAP_U16: return (cur + v) & 0xFFFFu;
+        case TMAP_BF16: return (uint32_t)f32_to_bf16_rne(bf16_to_f32((uint16_t)cur) + bf16_to_f32((uint16_t)v));
+        default: {   // F16
+            const float sum = (float)__builtin_bit_cast(_Float16, (uint16_t)cur) +
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)v);
+            return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sum);
+        }
+        }
+    } else {
+        return (uint32_t)minmax_bits<OP == ST_MAX>(dtype, cur, v);
+    }
+}
+
+// A reduction of the 8- or 16-bit elements of one aligned 32-bit word at
+// once (element i of the word takes part if bit i of `inb` is set), by
+// compare-and-swap: one atomic per word instead of one per element, and no
+// two lanes of an instruction contend for the same word.
+template <int OP>
+__device__ __forceinline__ void reduce_word(uint8_t dtype, uint32_t esize, ATT_GLOBAL uint32_t* w, uint32_t vw,
+                                            uint32_t inb) {
+    const uint32_t bits = esize * 8u, epw = 4u / esize;
+    const uint32_t em = esize == 1 ? 0xFFu : 0xFFFFu;
+    uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (true) {
+        uint32_t nw = old;
+        for (uint32_t i = 0; i < epw; ++i) {
+            if (!((inb >> i) & 1u)) continue;
+            const uint32_t sh = i * bits;
+            const uint32_t nv = reduce_sub_value<OP>(dtype, (old >> sh) & em, (vw >> sh) & em) & em;
+            nw = (nw & ~(em << sh)) | (nv << sh);
+        }
+        if (nw == old) return;
+        if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return;
+    }
+}
+
 // The esize bytes at byte offset `off` of a 16-byte chunk (off a multiple of
 // esize), selected with shifts so that no per-lane array is indexed at run
 // time (that would live in scratch memory).
@@ -444,6 +489,60 @@ __device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_
                                                  uint32_t wave, uint32_t nwaves) {
     const uint32_t lane = lane_id();
     const uint32_t nchunk = m.box_bytes >> 4;
+    if constexpr (OP != ST_STORE) {
+        if (m.esize >= 4 && m.es[0] == 1) {
+            // Reductions on 4- and 8-byte elements go element-major: lane l
+            // of an atomic instruction takes element l of a run of 64
+            // consecutive box elements, so one instruction updates whole
+            // cache lines instead of one element in each of 64 chunks 16
+            // bytes apart (the L2 then merges a line's atomics into one
+            // request).  The result is the same: integer and min / max
+            // updates commute, and float adds are unordered across boxes
+            // anyway.
+            const uint32_t epc = 16u / m.esize;
+            const uint32_t nel = nchunk * epc;
+            for (uint32_t e0 = wave * 64u; e0 < nel; e0 += nwaves * 64u) {
+                const uint32_t E = e0 + lane;
+                if (E >= nel) continue;
+                const uint32_t q = E / epc, eo = E % epc;
+                const ChunkLoc L = chunk_locate(m, c, q);
+                const int64_t g = L.g0 + (int64_t)eo;
+                if (!L.rest_in || g < 0 || g >= m.dim[0]) continue;
+                const uint8_t* src = lds + swz_chunk(q, m.swizzle) * 16u + eo * m.esize;
+                const uint64_t bits = m.esize == 4 ? (uint64_t)*reinterpret_cast<const uint32_t*>(src)
+                                                   : *reinterpret_cast<const uint64_t*>(src);
+                gbyte* dst = gptr(m.base + (uint64_t)L.rest_off) + g * m.esize;
+                if constexpr (OP == ST_ADD) reduce_add_element(m.dtype, dst, bits);
+                else reduce_minmax_element<OP == ST_MAX>(m.dtype, dst, bits);
+            }
+            return;
+        }
+        if (m.es[0] == 1 && (((int64_t)c[0] * m.esize) & 3) == 0) {
+            // 8- and 16-bit elements with a word-aligned box origin: lane l
+            // takes word l of a run of 64 consecutive 32-bit words of the box
+            // (a word holds whole elements, and word-aligned in the box means
+            // word-aligned in memory); elements past either edge of dim 0 are
+            // left alone.  A word with any element inside starts inside.
+            const uint32_t epw = 4u / m.esize;
+            const uint32_t nwd = nchunk * 4u;
+            for (uint32_t w0 = wave * 64u; w0 < nwd; w0 += nwaves * 64u) {
+                const uint32_t W = w0 + lane;
+                if (W >= nwd) continue;
+                const uint32_t q = W >> 2, wo = W & 3u;
+                const ChunkLoc L = chunk_locate(m, c, q);
+                if (!L.rest_in) continue;
+                const int64_t g = L.g0 + (int64_t)(wo * epw);
+                uint32_t inb = 0;
+                for (uint32_t i = 0; i < epw; ++i)
+                    if (g + (int64_t)i >= 0 && g + (int64_t)i < m.dim[0]) inb |= 1u << i;
+                if (!inb) continue;
+                const uint32_t vw = *reinterpret_cast<const uint32_t*>(lds + swz_chunk(q, m.swizzle) * 16u + wo * 4u);
+                reduce_word<OP>(m.dtype, m.esize, (ATT_GLOBAL uint32_t*)(gptr(m.base + (uint64_t)L.rest_off) + g * m.esize),
+                                vw, inb);
+            }
+            return;
+        }
+    }
     const bool fast = (m.es[0] == 1) && ((((int64_t)c[0] * m.esize) & 15) == 0);
     const int64_t n_el = 16 / m.esize;
     for (uint32_t grp = wave; grp * 64u < nchunk; grp += nwaves) {

@@ -125,6 +125,13 @@ def run_extra(att, torch, stream, reps: int):
     ms = timed(lambda: att.tile_reduce(mr, "min", rc.data_ptr(), ex["nbox"], srcs.data_ptr(), stream), reps)
     out["reduce_min_i32_pass"] = {"ms": round(ms, 4),
                                   "GBps_algorithmic": round(ex["nbox"] * 16384 * 3 / ms / 1e6, 1)}
+    # the same pass in fp32 (N(0,1) values, hardware float atomics)
+    dstf = torch.from_numpy(synthgen.normal_f32(ex["seed"], (4096, 4096))).cuda()
+    srcf = torch.from_numpy(synthgen.normal_f32(ex["seed"] * 1000 + 22, (ex["nbox"], 64, 64))).cuda()
+    mf = att.tmap_encode("f32", 2, dstf.data_ptr(), ex["dims"], ex["strides"], ex["box"], None, "none")
+    ms = timed(lambda: att.tile_reduce_add(mf, rc.data_ptr(), ex["nbox"], srcf.data_ptr(), stream), reps)
+    out["reduce_add_f32_pass"] = {"ms": round(ms, 4),
+                                  "GBps_algorithmic": round(ex["nbox"] * 16384 * 3 / ms / 1e6, 1)}
     # the pages' reduce example type: bf16 add (compare-and-swap per element)
     dst16 = torch.from_numpy(synthgen.normal_bf16_bits(ex["seed"], (4096, 4096)).view(np.int16)).cuda()
     src16 = torch.from_numpy(synthgen.normal_bf16_bits(ex["seed"] * 1000 + 21, (ex["nbox"], 64, 64))
