@@ -292,9 +292,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI]
             }
 }
 
-// EDGE = false: every box is inside the tensors (M, N multiples of 256, K a
-// multiple of BK), copies use precomputed per-lane offsets.  EDGE = true: any
-// shape; boxes go through the general loader with zero fill at the edges.
+// EDGE = false: K a multiple of BK; copies use precomputed per-lane offsets,
+// and in a partial tile the rows past M (N) re-read the last row (they only
+// reach C rows / columns the epilogue clips).  EDGE = true: any K; boxes go
+// through the general loader with zero fill at the edges.
 // SWM: the operands' swizzle mode (64B / 128B, or their _K256 forms).
 // MI: the MFMA shape, 32 (v_mfma_f32_32x32x16_bf16, 4 x 4 tiles per wave) or
 // 16 (v_mfma_f32_16x16x32_bf16, 8 x 8 tiles).  Both run 1024 flop per clock
@@ -330,16 +331,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
 
     // Per-lane source offsets inside a box (same for every K step): lane l of
     // group j fills physical chunk p = j*64 + l with logical chunk swz(p).
+    // Rows past M (or N) in a partial tile re-read the last row instead:
+    // they only feed C rows (columns) the epilogue never stores.
     const uint32_t lds0 = lds_addr_of(smem);
     const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t rowsA = g.M - m0 < kTM ? g.M - m0 : kTM, rowsB = g.N - n0 < kTN ? g.N - n0 : kTN;
     uint32_t offA[GPW], offB[GPW];
 #pragma unroll
     for (uint32_t j = 0; j < GPW; ++j) {
         const uint32_t p = (wave * GPW + j) * 64u + lane;
         const uint32_t q = swz_chunk(p, SWM);
         const uint32_t row = q / CPR, ch = q % CPR;
-        offA[j] = row * (uint32_t)g.A.stride[0] + ch * 16u;
-        offB[j] = row * (uint32_t)g.B.stride[0] + ch * 16u;
+        offA[j] = (row < rowsA ? row : rowsA - 1u) * (uint32_t)g.A.stride[0] + ch * 16u;
+        offB[j] = (row < rowsB ? row : rowsB - 1u) * (uint32_t)g.B.stride[0] + ch * 16u;
     }
     const uint64_t baseA = g.A.base + (uint64_t)m0 * g.A.stride[0];
     const uint64_t baseB = g.B.base + (uint64_t)n0 * g.B.stride[0];
@@ -548,8 +552,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
 // base address per (operand, sub-step, 64 KiB window): the 128-byte swizzle
 // key of a fragment row depends only on the lane (fragments start on 16-row
 // boundaries), so fragment f of a slot sits f * 2048 bytes further and the
-// slot offset within the window rides in the ds_read immediate too.  M, N
-// multiples of 256 and K of 64.
+// slot offset within the window rides in the ds_read immediate too.  K a
+// multiple of 64; partial M / N tiles clamp their rows as k_gemm_bf16 does.
 template <int SWM>
 __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16_ring5(GemmArgs g) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -574,14 +578,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     const uint32_t lds0 = lds_addr_of(smem);
     const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
 
+    // rows past M (N) of a partial tile re-read the last row (see k_gemm_bf16)
+    const uint32_t rowsA = g.M - m0 < kTM ? g.M - m0 : kTM, rowsB = g.N - n0 < kTN ? g.N - n0 : kTN;
     uint32_t offA[GPW], offB[GPW];
 #pragma unroll
     for (uint32_t j = 0; j < GPW; ++j) {
         const uint32_t p = (wave * GPW + j) * 64u + lane;
         const uint32_t q = swz_chunk(p, SWM);
         const uint32_t row = q / CPR, ch = q % CPR;
-        offA[j] = row * (uint32_t)g.A.stride[0] + ch * 16u;
-        offB[j] = row * (uint32_t)g.B.stride[0] + ch * 16u;
+        offA[j] = (row < rowsA ? row : rowsA - 1u) * (uint32_t)g.A.stride[0] + ch * 16u;
+        offB[j] = (row < rowsB ? row : rowsB - 1u) * (uint32_t)g.B.stride[0] + ch * 16u;
     }
     const uint64_t baseA = g.A.base + (uint64_t)m0 * g.A.stride[0];
     const uint64_t baseB = g.B.base + (uint64_t)n0 * g.B.stride[0];
@@ -733,7 +739,9 @@ static tmap_status launch_gemm_t(const GemmArgs& g, hipStream_t st) {
 
 template <int BK, int S, int MI>
 static tmap_status launch_gemm_mi(const GemmArgs& g, uint32_t swm, hipStream_t st) {
-    const bool even = g.M % kTM == 0 && g.N % kTN == 0 && g.K % BK == 0;
+    // K a multiple of BK: the fast loader (partial M / N tiles clamp their
+    // rows); otherwise every copy goes through the general loader's K fill.
+    const bool even = g.K % BK == 0;
     constexpr int BASE = BK == 64 ? TMAP_SWIZZLE_128B : TMAP_SWIZZLE_64B;
     if (swm & 4u)
         return even ? launch_gemm_t<BK, S, false, BASE | 4, MI>(g, st) : launch_gemm_t<BK, S, true, BASE | 4, MI>(g, st);
@@ -816,9 +824,9 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
     if (bka == 64) {
         if (stages == 2) return launch_gemm<64, 2>(g, swa, mfma, st);
         if (stages == 3) {
-            // A three deep, B two deep in five operand slots: whole tiles,
-            // K a multiple of 64, 16 x 16 x 32 MFMAs
-            if (mfma == 32 || M % kTM || N % kTN || K % 64u) return TMAP_ERR_UNSUPPORTED;
+            // A three deep, B two deep in five operand slots: K a multiple
+            // of 64, 16 x 16 x 32 MFMAs
+            if (mfma == 32 || K % 64u) return TMAP_ERR_UNSUPPORTED;
             if (swa & 4u) return launch_gemm_ring5<TMAP_SWIZZLE_128B_K256>(g, st);
             return launch_gemm_ring5<TMAP_SWIZZLE_128B>(g, st);
         }

@@ -304,13 +304,14 @@ tmap_status hbm_probe(int32_t kind, const void* d_src, void* d_dst, uint64_t byt
  * by the tile loader into a
  * `stages`-deep LDS ring and consumed by MFMA bf16 with fp32 accumulation.
  * d_C is M x N row-major bf16 (round to nearest even), leading dimension
- * ldc >= N elements.  Ragged M, N, K are handled by the maps' zero fill and a
- * masked epilogue.  For the 64-deep K step, stages = 2 is the double buffer
- * (two 64 KiB stages; three do not fit the 160 KiB LDS) and stages = 3 the
- * operand ring: five 32 KiB slots holding A and B boxes in turn, so that A
- * runs three deep and B two deep; it takes M and N multiples of 256 and K a
+ * ldc >= N elements.  Any M, N and K: partial tiles in M and N are clipped
+ * by the epilogue, and a K that is not a multiple of the box depth is zero-
+ * filled through the maps (a slower loader).  For the 64-deep K step, stages
+ * = 2 is the double buffer (two 64 KiB stages; three do not fit the 160 KiB
+ * LDS) and stages = 3 the operand ring: five 32 KiB slots holding A and B
+ * boxes in turn, so that A runs three deep and B two deep; it takes K a
  * multiple of 64.  Errors: NULL, UNSUPPORTED (map shape, dtype, box,
- * swizzle, OOB fill other than zero, stages, shape for stages = 3, ldc < N),
+ * swizzle, OOB fill other than zero, stages, K for stages = 3, ldc < N),
  * HIP.  M == 0 or N == 0 is a no-op. */
 tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
                       uint32_t K, uint32_t ldc, uint32_t stages, void* stream);

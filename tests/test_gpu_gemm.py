@@ -89,7 +89,7 @@ def test_mfma_shape_argument():
 @pytest.mark.parametrize("K", [64, 128, 192, 320, 384, 704])
 @pytest.mark.parametrize("k256", [False, True])
 def test_operand_ring(K, k256):
-    """64-deep boxes, three stages, whole tiles: the five-slot operand ring
+    """64-deep boxes, three stages: the five-slot operand ring
     (A three deep, B two deep, loop unrolled by five).  K from one K-step up
     to two unrolled groups plus one, so every slot pattern and the clamped
     copies past the last K-step run."""
@@ -103,14 +103,14 @@ def test_operand_ring(K, k256):
     check_close(C, ref)
 
 
-@pytest.mark.parametrize("K", [64, 128, 192, 576])
-def test_operand_ring_many_tiles_exact(K):
+@pytest.mark.parametrize("K,M,N", [(64, 4352, 4352), (128, 4352, 4352), (192, 4352, 4352), (576, 4352, 4352),
+                                   (192, 4252, 4315), (128, 4097, 33)])
+def test_operand_ring_many_tiles_exact(K, M, N):
     """More 256 x 256 tiles (17 x 17) than the GPU has CUs, so workgroups of
-    the operand ring run in several rounds.  A selects one K index per row
-    (A[m, sel[m]] = 1), so C[m, :] = B[sel[m], :] exactly: every output of
-    every tile checked."""
-    M = N = 17 * 256
-    say("gemm ring5 many tiles", K)
+    the operand ring run in several rounds, whole or with partial tiles in M
+    and N.  A selects one K index per row (A[m, sel[m]] = 1), so C[m, :] =
+    B[sel[m], :] exactly: every output of every tile checked."""
+    say("gemm ring5 many tiles", K, M, N)
     sel = synthgen.rng(62).integers(0, K, M)
     A = np.zeros((M, K), dtype=np.uint16)
     A[np.arange(M), sel] = 0x3F80
@@ -146,12 +146,11 @@ def test_operand_ring_c_leading_dimension(offset, ldc):
 
 
 def test_operand_ring_shape_limits():
-    """The operand ring takes whole 256 x 256 tiles, K a multiple of 64 and
-    16 x 16 x 32 MFMAs; other requests for three 64-deep stages are
-    rejected, as are 16 x 16 MFMAs with 32-deep boxes."""
+    """The operand ring takes K a multiple of 64 and 16 x 16 x 32 MFMAs;
+    other requests for three 64-deep stages are rejected, as are 16 x 16
+    MFMAs with 32-deep boxes."""
     A = np.zeros((300, 128), dtype=np.uint16)
-    for args in [(300, 256, 128, 64, 3, 0), (256, 256, 96, 64, 3, 16), (256, 256, 128, 64, 3, 32),
-                 (256, 256, 128, 32, 5, 16)]:
+    for args in [(256, 256, 96, 64, 3, 16), (256, 256, 128, 64, 3, 32), (256, 256, 128, 32, 5, 16)]:
         M, N, K, bk, st, mf = args
         with pytest.raises(att.TmapError) as ei:
             run_gemm(A[:M, :K], A[:N, :K], M, N, K, bk, st, mfma=mf)
@@ -173,7 +172,11 @@ def test_permutation_exact():
     (512, 768, 1024, 64, 2, True, 0), (768, 512, 1024, 32, 4, True, 0), (300, 200, 100, 32, 3, True, 0),
     (300, 200, 100, 64, 2, False, 0), (257, 513, 96, 32, 2, False, 0), (1, 1, 64, 64, 2, False, 0),
     (256, 256, 8, 64, 2, False, 0), (512, 768, 1024, 64, 2, True, 32), (300, 200, 100, 64, 2, True, 32),
-    (257, 513, 96, 64, 2, True, 16), (1, 1, 64, 64, 2, True, 16)])
+    (257, 513, 96, 64, 2, True, 16), (1, 1, 64, 64, 2, True, 16),
+    # partial M / N tiles with K a multiple of the box depth: the fast loader
+    # with clamped rows (double buffer, operand ring, 32-deep ring)
+    (300, 200, 192, 64, 2, True, 16), (257, 513, 128, 64, 3, True, 16), (1, 1, 64, 64, 3, False, 16),
+    (300, 520, 320, 64, 3, False, 0), (511, 257, 128, 32, 4, True, 0), (300, 200, 192, 64, 2, False, 32)])
 def test_against_oracle_full(M, N, K, bk, stages, k256, mfma):
     say("gemm", M, N, K, bk, stages, k256, mfma)
     A = synthgen.normal_bf16_bits(54, (M, K))
