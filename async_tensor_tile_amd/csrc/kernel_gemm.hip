@@ -349,8 +349,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     const uint64_t baseB = g.B.base + (uint64_t)n0 * g.B.stride[0];
 
     // Whole-tile issue (prologue, and every copy of the general loader).
+    // Whole-tile copy through the general loader: zero fill past K (and
+    // past M / N).
+    auto issue_general = [&](uint32_t kt, uint32_t slot) {
+        const int32_t ca[5] = {(int32_t)(kt * BK), (int32_t)m0, 0, 0, 0};
+        const int32_t cb[5] = {(int32_t)(kt * BK), (int32_t)n0, 0, 0, 0};
+        tile_load_issue(g.A, ca, smem + slot * BOX, wave, 4);
+        tile_load_issue(g.B, cb, smem + BREG + slot * BOX, wave, 4);
+    };
+    // With two slots the fast loader also serves a K that is not a multiple
+    // of BK: only the last, partial K tile goes through the general loader
+    // (every wait of the two-slot ring is vmcnt(0), so its copy count does
+    // not matter).
+    const bool ktail = S == 2 && interior && g.K % BK != 0;
     auto issue = [&](uint32_t kt, uint32_t slot) {
         if constexpr (interior) {
+            if (ktail && kt + 1u == nk) {
+                issue_general(kt, slot);
+                return;
+            }
             const uint64_t ka = baseA + (uint64_t)kt * ROWB;
             const uint64_t kb = baseB + (uint64_t)kt * ROWB;
             const uint32_t la = lds0 + slot * BOX + wave_u * GPW * 1024u;
@@ -359,10 +376,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
             for (uint32_t j = 0; j < GPW; ++j) dma16_sv(kb, offB[j], la + BREG + j * 1024u);
         } else {
-            const int32_t ca[5] = {(int32_t)(kt * BK), (int32_t)m0, 0, 0, 0};
-            const int32_t cb[5] = {(int32_t)(kt * BK), (int32_t)n0, 0, 0, 0};
-            tile_load_issue(g.A, ca, smem + slot * BOX, wave, 4);
-            tile_load_issue(g.B, cb, smem + BREG + slot * BOX, wave, 4);
+            issue_general(kt, slot);
         }
     };
 
@@ -510,12 +524,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     typedef std::integral_constant<int, -1> slot_rt;
     if constexpr (S == 2 && interior) {
         // tile t sits in slot t % 2: unroll by two so each body knows its slot
-        for (; t + 2 <= nfull; t += 2) {
+        const uint32_t nfast = ktail && nfull ? nfull - 1u : nfull;
+        for (; t + 2 <= nfast; t += 2) {
             iteration(with_c{}, std::integral_constant<int, 0>{}, t, 0u, 1u, 0u, true);
             iteration(with_c{}, std::integral_constant<int, 1>{}, t + 1, 1u, 0u, 0u, true);
         }
-        if (t < nfull) {
+        if (t < nfast) {
             iteration(with_c{}, std::integral_constant<int, 0>{}, t, 0u, 1u, 0u, true);
+            ++t;
+        }
+        if (t < nfull) {
+            // the partial last K tile, copied whole before this iteration
+            issue_general(t + 1u, (t + 1u) & 1u);
+            iteration(without_c{}, slot_rt{}, t, t & 1u, (t + 1u) & 1u, 0u, true);
             ++t;
         }
         slot_t = t & 1u;
@@ -739,9 +760,10 @@ static tmap_status launch_gemm_t(const GemmArgs& g, hipStream_t st) {
 
 template <int BK, int S, int MI>
 static tmap_status launch_gemm_mi(const GemmArgs& g, uint32_t swm, hipStream_t st) {
-    // K a multiple of BK: the fast loader (partial M / N tiles clamp their
-    // rows); otherwise every copy goes through the general loader's K fill.
-    const bool even = g.K % BK == 0;
+    // K a multiple of BK, or two slots: the fast loader (partial M / N tiles
+    // clamp their rows; with two slots a partial last K tile goes through the
+    // general loader); otherwise every copy goes through the general loader.
+    const bool even = g.K % BK == 0 || S == 2;
     constexpr int BASE = BK == 64 ? TMAP_SWIZZLE_128B : TMAP_SWIZZLE_64B;
     if (swm & 4u)
         return even ? launch_gemm_t<BK, S, false, BASE | 4, MI>(g, st) : launch_gemm_t<BK, S, true, BASE | 4, MI>(g, st);

@@ -306,7 +306,8 @@ tmap_status hbm_probe(int32_t kind, const void* d_src, void* d_dst, uint64_t byt
  * d_C is M x N row-major bf16 (round to nearest even), leading dimension
  * ldc >= N elements.  Any M, N and K: partial tiles in M and N are clipped
  * by the epilogue, and a K that is not a multiple of the box depth is zero-
- * filled through the maps (a slower loader).  For the 64-deep K step, stages
+ * filled through the maps' OOB fill (with stages = 2 only the last K tile
+ * takes that slower loader, with more stages every tile).  For the 64-deep K step, stages
  * = 2 is the double buffer (two 64 KiB stages; three do not fit the 160 KiB
  * LDS) and stages = 3 the operand ring: five 32 KiB slots holding A and B
  * boxes in turn, so that A runs three deep and B two deep; it takes K a

@@ -176,7 +176,11 @@ def test_permutation_exact():
     # partial M / N tiles with K a multiple of the box depth: the fast loader
     # with clamped rows (double buffer, operand ring, 32-deep ring)
     (300, 200, 192, 64, 2, True, 16), (257, 513, 128, 64, 3, True, 16), (1, 1, 64, 64, 3, False, 16),
-    (300, 520, 320, 64, 3, False, 0), (511, 257, 128, 32, 4, True, 0), (300, 200, 192, 64, 2, False, 32)])
+    (300, 520, 320, 64, 3, False, 0), (511, 257, 128, 32, 4, True, 0), (300, 200, 192, 64, 2, False, 32),
+    # K not a multiple of the box depth with two slots: the fast loader, and
+    # the general loader for the partial last K tile only
+    (512, 256, 4000, 64, 2, True, 16), (300, 520, 136, 64, 2, False, 32), (256, 256, 40, 64, 2, True, 0),
+    (257, 300, 1000, 32, 2, True, 0)])
 def test_against_oracle_full(M, N, K, bk, stages, k256, mfma):
     say("gemm", M, N, K, bk, stages, k256, mfma)
     A = synthgen.normal_bf16_bits(54, (M, K))
