@@ -265,7 +265,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI]
                 if (row >= Mc || col >= Nc) continue;
                 gbyte* dst = gptr(g.Cm.base + row * cstride + (uint64_t)col * 2u);
                 if (col + 8u <= Nc) {
-                    *(ATT_GLOBAL u32x4*)dst = v;
+                    // non-temporal: C is not read back, and the write burst
+                    // of all workgroups finishing together drains faster
+                    // without displacing the operand panels from L2
+                    __builtin_nontemporal_store(v, (ATT_GLOBAL u32x4*)dst);
                 } else {
 #pragma unroll
                     for (uint32_t e = 0; e < 8; ++e)
