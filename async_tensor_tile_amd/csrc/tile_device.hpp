@@ -28,6 +28,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // global_* instructions rather than flat_* ones.
 #define ATT_GLOBAL __attribute__((address_space(1)))
 typedef ATT_GLOBAL uint8_t gbyte;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ gbyte* gptr(uint64_t addr) { return (gbyte*)addr; }
 __device__ __forceinline__ gbyte* gptr(const void* p) { return (gbyte*)(uintptr_t)p; }
@@ -306,7 +308,7 @@ __device__ __forceinline__ void reduce_add_element(uint8_t dtype, gbyte* dst, ui
         const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
         cas_update_sub(dst, 16, [v](uint32_t cur) {
             const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)cur) + v;
-            return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
+            return s != s ? 0x7E00u : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
         });
         break;
     }
@@ -435,7 +437,7 @@ __device__ __forceinline__ uint32_t reduce_sub_value(uint8_t dtype, uint32_t cur
         default: {   // F16
             const float sum = (float)__builtin_bit_cast(_Float16, (uint16_t)cur) +
                               (float)__builtin_bit_cast(_Float16, (uint16_t)v);
-            return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sum);
+            return sum != sum ? 0x7E00u : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)sum);
         }
         }
     } else {
@@ -517,28 +519,61 @@ __device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_
             }
             return;
         }
-        if (m.es[0] == 1 && (((int64_t)c[0] * m.esize) & 3) == 0) {
-            // 8- and 16-bit elements with a word-aligned box origin: lane l
-            // takes word l of a run of 64 consecutive 32-bit words of the box
-            // (a word holds whole elements, and word-aligned in the box means
-            // word-aligned in memory); elements past either edge of dim 0 are
-            // left alone.  A word with any element inside starts inside.
-            const uint32_t epw = 4u / m.esize;
-            const uint32_t nwd = nchunk * 4u;
+        if (m.es[0] == 1) {
+            // 8- and 16-bit elements: lane l takes one aligned 32-bit word of
+            // global memory, so that one atomic updates all its elements.  A
+            // box row of L0 elements starting at c0 touches words
+            // floor(c0 / epw) .. floor((c0 + L0 - 1) / epw); with an origin
+            // that is not word-aligned a word's elements come from two
+            // neighbouring box elements, read from LDS one by one.  Elements
+            // past either end of the box row or of dim 0 are left alone.
+            const uint32_t esz = m.esize, epw = 4u / esz, L0 = m.L[0];
+            const int64_t c0 = c[0];
+            const int64_t w_first = c0 >= 0 ? c0 / epw : -((-c0 + epw - 1) / epw);
+            const uint32_t head = (uint32_t)(c0 - w_first * (int64_t)epw);     // 0 .. epw-1
+            const uint32_t wpr = (head + L0 + epw - 1u) / epw;                 // words per box row
+            const uint32_t cpr = m.cpr;                                         // chunks per box row
+            const uint32_t nrow = nchunk / cpr;
+            const uint32_t nwd = nrow * wpr;
             for (uint32_t w0 = wave * 64u; w0 < nwd; w0 += nwaves * 64u) {
                 const uint32_t W = w0 + lane;
                 if (W >= nwd) continue;
-                const uint32_t q = W >> 2, wo = W & 3u;
-                const ChunkLoc L = chunk_locate(m, c, q);
+                const uint32_t row = W / wpr, wi = W % wpr;
+                const uint32_t q_row = row * cpr;
+                const ChunkLoc L = chunk_locate(m, c, q_row);
                 if (!L.rest_in) continue;
-                const int64_t g = L.g0 + (int64_t)(wo * epw);
-                uint32_t inb = 0;
-                for (uint32_t i = 0; i < epw; ++i)
-                    if (g + (int64_t)i >= 0 && g + (int64_t)i < m.dim[0]) inb |= 1u << i;
+                const int64_t g = (w_first + (int64_t)wi) * (int64_t)epw;      // first element of the word
+                uint32_t inb = 0, vw = 0;
+                for (uint32_t h = 0; h < epw; ++h) {
+                    const int64_t gg = g + (int64_t)h;
+                    const int64_t e = gg - c0;                                 // box element in the row
+                    if (e < 0 || e >= (int64_t)L0 || gg < 0 || gg >= m.dim[0]) continue;
+                    const uint32_t eb = (uint32_t)e * esz;
+                    const uint8_t* src = lds + swz_chunk(q_row + (eb >> 4), m.swizzle) * 16u + (eb & 15u);
+                    const uint32_t v = esz == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(src) : (uint32_t)*src;
+                    vw |= v << (h * esz * 8u);
+                    inb |= 1u << h;
+                }
                 if (!inb) continue;
-                const uint32_t vw = *reinterpret_cast<const uint32_t*>(lds + swz_chunk(q, m.swizzle) * 16u + wo * 4u);
-                reduce_word<OP>(m.dtype, m.esize, (ATT_GLOBAL uint32_t*)(gptr(m.base + (uint64_t)L.rest_off) + g * m.esize),
-                                vw, inb);
+                ATT_GLOBAL uint32_t* wp = (ATT_GLOBAL uint32_t*)(gptr(m.base + (uint64_t)L.rest_off) + g * (int64_t)esz);
+                if constexpr (OP == ST_ADD) {
+                    // both halves inside: the packed hardware add, which
+                    // rounds the exact sum once to nearest even like the
+                    // f32-then-round definition (f32 carries more than
+                    // 2p + 2 bits); NaN results are made canonical by the
+                    // pass that follows the reduction
+                    if (inb == 3u && m.dtype == TMAP_BF16) {
+                        __builtin_amdgcn_global_atomic_fadd_v2bf16((ATT_GLOBAL bf16x2_t*)wp,
+                                                                   __builtin_bit_cast(bf16x2_t, vw));
+                        continue;
+                    }
+                    if (inb == 3u && m.dtype == TMAP_F16) {
+                        __builtin_amdgcn_global_atomic_fadd_v2f16((ATT_GLOBAL f16x2_t*)wp,
+                                                                  __builtin_bit_cast(f16x2_t, vw));
+                        continue;
+                    }
+                }
+                reduce_word<OP>(m.dtype, esz, wp, vw, inb);
             }
             return;
         }

@@ -239,6 +239,33 @@ def test_float_reduce_single_contribution_exact(dtype):
     np.testing.assert_array_equal(to_host(acc), hw)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", ["aligned", "even_origin_edge", "odd_origin_edges"])
+def test_half_reduce_special_values_exact(dtype, layout):
+    """16-bit float reduce-add with random bit patterns on both sides (NaNs
+    with payloads, infinities of both signs, subnormals, signed zeros): one
+    contribution per element, bit-exact against the oracle, canonical NaN
+    results included.  Word-aligned boxes take the packed hardware add for
+    whole words; odd origins and boxes cut by the dim-0 edge also take the
+    per-word compare-and-swap."""
+    L0 = 32
+    dims, strides, box = (133, 24), (288,), (L0, 8)     # odd width: a word cut by the edge
+    foot = strides[0] * dims[1]
+    dst0 = synthgen.random_bytes(41, foot)
+    imgs = synthgen.random_bytes(42, 12 * L0 * 8 * 2)
+    # disjoint boxes in every layout
+    xs = {"aligned": [0, 32, 64, 96],                   # whole words only
+          "even_origin_edge": [-6, 34, 70, 104],        # crossing x = 0 and x = 133
+          "odd_origin_edges": [-7, 27, 59, 117]}[layout]
+    coords = np.array([[xs[i % 4], 8 * (i // 4)] for i in range(12)], dtype=np.int32)
+    acc = to_dev(dst0)
+    m = encode(acc, dtype, dims, strides, box)
+    att.tile_reduce_add(m, to_dev(coords), 12, to_dev(imgs), stream())
+    hw = dst0.copy()
+    oracle.Map(dtype, dims, strides, box).reduce_add(hw, coords, imgs)
+    np.testing.assert_array_equal(to_host(acc), hw)
+
+
 # ------------------------------- edge cases ---------------------------------
 
 def test_empty_and_fully_outside():
