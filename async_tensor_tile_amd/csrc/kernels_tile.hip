@@ -196,32 +196,6 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_store(TmapImpl m, const 
     tile_store_issue<OP>(m, c, smem, wave, nwaves);
 }
 
-// After a bf16 / f16 reduce-add: every in-bounds element of box b that holds
-// a NaN gets the canonical quiet NaN, which is what each element update
-// yields once a NaN is involved (the packed hardware adds keep an operand's
-// payload or set the sign).  Runs after the reduction on the same stream;
-// overlapping boxes write the same value.
-__global__ __launch_bounds__(kBatchThreads) void k_canon_nan16(TmapImpl m, const int32_t* __restrict__ coords) {
-    const uint32_t b = blockIdx.x;
-    int32_t c[5];
-    read_coords(m, coords, b, c);
-    const uint32_t nchunk = m.box_bytes >> 4;
-    const uint16_t canon = m.dtype == TMAP_BF16 ? 0x7FC0u : 0x7E00u;
-    const uint16_t inf = m.dtype == TMAP_BF16 ? 0x7F80u : 0x7C00u;
-    for (uint32_t q = threadIdx.x; q < nchunk; q += blockDim.x) {
-        const ChunkLoc L = chunk_locate(m, c, q);
-        if (!L.rest_in) continue;
-        ATT_GLOBAL uint16_t* row = (ATT_GLOBAL uint16_t*)gptr(m.base + (uint64_t)L.rest_off);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t g = L.g0 + (int64_t)e * m.es[0];
-            if (g < 0 || g >= m.dim[0]) continue;
-            const uint16_t v = row[g];
-            if ((v & 0x7FFFu) > inf && v != canon) row[g] = canon;
-        }
-    }
-}
-
 // Byte-counted barrier self-test: one barrier (arrival count 1) completes
 // after `ntile` copies signal their own byte counts.  Trace records are
 // (who, arrivals_left, pending, phase); who = -1 init, -2 arrive.expect_tx,
@@ -361,13 +335,6 @@ static tmap_status launch_store(const tmap_t* m, const int32_t* d_coords, uint32
     if (st) return st;
     hipLaunchKernelGGL(k_tile_store<OP>, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), t,
                        d_coords, static_cast<const uint8_t*>(d_in));
-    if constexpr (OP == ST_ADD) {
-        if (t.dtype == TMAP_BF16 || t.dtype == TMAP_F16) {
-            st = check_launch(name);
-            if (st) return st;
-            hipLaunchKernelGGL(k_canon_nan16, dim3(nbox), dim3(kBatchThreads), 0, as_stream(stream), t, d_coords);
-        }
-    }
     return check_launch(name);
 }
 

@@ -470,6 +470,30 @@ __device__ __forceinline__ void reduce_word(uint8_t dtype, uint32_t esize, ATT_G
     }
 }
 
+// Whether the 16-bit float sum a + b (low halves of the arguments, bf16 or
+// f16) is a NaN: an operand is one, or they are infinities of opposite sign.
+__device__ __forceinline__ bool half_sum_nan(bool bf, uint32_t a, uint32_t b) {
+    const uint32_t inf = bf ? 0x7F80u : 0x7C00u;
+    const uint32_t ma = a & 0x7FFFu, mb = b & 0x7FFFu;
+    return ma > inf || mb > inf || (ma == inf && mb == inf && ((a ^ b) & 0x8000u));
+}
+
+// Every NaN half of the word becomes the canonical quiet NaN (the other
+// half is left as it is, whatever concurrent updates do to it).
+__device__ __forceinline__ void canon_nan_word(bool bf, ATT_GLOBAL uint32_t* w) {
+    const uint32_t inf = bf ? 0x7F80u : 0x7C00u, canon = bf ? 0x7FC0u : 0x7E00u;
+    uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (true) {
+        uint32_t nw = old;
+        if ((old & 0x7FFFu) > inf) nw = (nw & 0xFFFF0000u) | canon;
+        if (((old >> 16) & 0x7FFFu) > inf) nw = (nw & 0x0000FFFFu) | (canon << 16);
+        if (nw == old) return;
+        if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return;
+    }
+}
+
 // The esize bytes at byte offset `off` of a 16-byte chunk (off a multiple of
 // esize), selected with shifts so that no per-lane array is indexed at run
 // time (that would live in scratch memory).
@@ -560,16 +584,17 @@ __device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_
                     // both halves inside: the packed hardware add, which
                     // rounds the exact sum once to nearest even like the
                     // f32-then-round definition (f32 carries more than
-                    // 2p + 2 bits); NaN results are made canonical by the
-                    // pass that follows the reduction
-                    if (inb == 3u && m.dtype == TMAP_BF16) {
-                        __builtin_amdgcn_global_atomic_fadd_v2bf16((ATT_GLOBAL bf16x2_t*)wp,
-                                                                   __builtin_bit_cast(bf16x2_t, vw));
-                        continue;
-                    }
-                    if (inb == 3u && m.dtype == TMAP_F16) {
-                        __builtin_amdgcn_global_atomic_fadd_v2f16((ATT_GLOBAL f16x2_t*)wp,
-                                                                  __builtin_bit_cast(f16x2_t, vw));
+                    // 2p + 2 bits).  A NaN result keeps an operand's payload
+                    // or gets a sign there; the old value it returns tells
+                    // when that happened, and the word's NaN halves are then
+                    // set to the canonical NaN.
+                    if (inb == 3u && (m.dtype == TMAP_BF16 || m.dtype == TMAP_F16)) {
+                        const bool bf = m.dtype == TMAP_BF16;
+                        const uint32_t old = bf ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2bf16(
+                                                                                  (ATT_GLOBAL bf16x2_t*)wp, __builtin_bit_cast(bf16x2_t, vw)))
+                                                : __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2f16(
+                                                                                  (ATT_GLOBAL f16x2_t*)wp, __builtin_bit_cast(f16x2_t, vw)));
+                        if (half_sum_nan(bf, old, vw) || half_sum_nan(bf, old >> 16, vw >> 16)) canon_nan_word(bf, wp);
                         continue;
                     }
                 }
