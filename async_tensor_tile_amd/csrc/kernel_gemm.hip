@@ -766,11 +766,16 @@ static tmap_status launch_gemm_mi(const GemmArgs& g, uint32_t swm, hipStream_t s
     // K a multiple of BK, or two slots: the fast loader (partial M / N tiles
     // clamp their rows; with two slots a partial last K tile goes through the
     // general loader); otherwise every copy goes through the general loader.
-    const bool even = g.K % BK == 0 || S == 2;
     constexpr int BASE = BK == 64 ? TMAP_SWIZZLE_128B : TMAP_SWIZZLE_64B;
-    if (swm & 4u)
-        return even ? launch_gemm_t<BK, S, false, BASE | 4, MI>(g, st) : launch_gemm_t<BK, S, true, BASE | 4, MI>(g, st);
-    return even ? launch_gemm_t<BK, S, false, BASE, MI>(g, st) : launch_gemm_t<BK, S, true, BASE, MI>(g, st);
+    if constexpr (S == 2) {
+        if (swm & 4u) return launch_gemm_t<BK, S, false, BASE | 4, MI>(g, st);
+        return launch_gemm_t<BK, S, false, BASE, MI>(g, st);
+    } else {
+        const bool even = g.K % BK == 0;
+        if (swm & 4u)
+            return even ? launch_gemm_t<BK, S, false, BASE | 4, MI>(g, st) : launch_gemm_t<BK, S, true, BASE | 4, MI>(g, st);
+        return even ? launch_gemm_t<BK, S, false, BASE, MI>(g, st) : launch_gemm_t<BK, S, true, BASE, MI>(g, st);
+    }
 }
 
 // The 16 x 16 x 32 form needs an even number of 32-deep sub-steps per stage,
