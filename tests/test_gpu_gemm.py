@@ -207,6 +207,35 @@ def test_8192_sampled(bk, stages, k256, mfma):
     assert not (C == 0x7FFF).any()
 
 
+def _random_gemm_case(seed):
+    g = synthgen.rng(90000 + seed)
+    bk, stages, mfma = [(64, 2, 16), (64, 2, 32), (64, 3, 16), (64, 2, 0), (32, 2, 32), (32, 3, 32),
+                        (32, 4, 32), (32, 5, 32)][int(g.integers(0, 8))]
+    M, N = (int(x) for x in g.integers(1, 1100, 2))
+    K = int(g.integers(1, 900))
+    if stages == 3 and bk == 64:
+        K = max(64, K // 64 * 64)          # the operand ring takes K a multiple of 64
+    return M, N, K, bk, stages, mfma, bool(g.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes_sampled(seed):
+    """Random M, N, K (partial tiles in every direction, K below one box
+    up to many), every ring depth and MFMA form: 2048 sampled outputs
+    against the oracle, plus the four corners."""
+    M, N, K, bk, stages, mfma, k256 = _random_gemm_case(seed)
+    say("gemm random", seed, M, N, K, bk, stages, mfma, k256)
+    A = synthgen.normal_bf16_bits(91000 + seed, (M, K))
+    Bt = synthgen.normal_bf16_bits(92000 + seed, (N, K))
+    C = run_gemm(A, Bt, M, N, K, bk, stages, k256=k256, mfma=mfma)
+    rows, cols = synthgen.sample_pairs(93000 + seed, 2048, M, N)
+    rows = np.concatenate([rows, [0, 0, M - 1, M - 1]])
+    cols = np.concatenate([cols, [0, N - 1, 0, N - 1]])
+    ref = oracle.gemm_bf16_sample(A, Bt, K, rows, cols)
+    check_close(C[rows, cols], ref)
+    assert not (C == 0x7FFF).any()
+
+
 @pytest.mark.parametrize("offset,ldc", [(0, 264), (1, 264), (0, 203)])
 def test_c_leading_dimension(offset, ldc):
     """C written with leading dimension ldc >= N: the LDS-staged tile store
