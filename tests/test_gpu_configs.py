@@ -70,6 +70,55 @@ def test_copy_other_shapes(dims, box, swizzle):
     assert same
 
 
+def _tensor_byte_mask(c):
+    """Bytes of the buffer that hold tensor elements (the rest is stride
+    padding, which a round trip must leave alone)."""
+    es = {"u8": 1, "u16": 2, "u32": 4, "i32": 4, "u64": 8, "i64": 8,
+          "f16": 2, "bf16": 2, "f32": 4, "f64": 8}[c.dtype]
+    mask = np.zeros(c.buf.size, dtype=bool)
+    row = np.arange(c.dims[0] * es)
+    idx = [np.arange(n) for n in c.dims[1:]]
+    grids = np.meshgrid(*idx, indexing="ij") if idx else []
+    offs = np.zeros(grids[0].shape if grids else (), dtype=np.int64)
+    for d, gr in enumerate(grids):
+        offs = offs + gr.astype(np.int64) * c.strides[d]
+    for o in np.ravel(offs):
+        mask[o + row] = True
+    return mask
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_copy_random_maps(seed):
+    """tile_copy_ex over random legal maps (ranks 1-5, every element type and
+    swizzle, element strides 1) with random ring depth, grid and variant
+    flags (stores, tile order, XCD renumbering, boxes per stage): every
+    tensor byte arrives, stride padding in the destination is untouched."""
+    from cases import random_case
+    g = synthgen.rng(95000 + seed)
+    c = random_case(g)
+    c.estride = [1] * c.rank
+    if c.swizzle == "none":
+        c.box[0] = (16 // {"u8": 1, "u16": 2, "u32": 4, "i32": 4, "u64": 8, "i64": 8, "f16": 2, "bf16": 2,
+                           "f32": 4, "f64": 8}[c.dtype]) * int(g.integers(1, 4))
+    else:
+        es = {"u8": 1, "u16": 2, "u32": 4, "i32": 4, "u64": 8, "i64": 8, "f16": 2, "bf16": 2, "f32": 4, "f64": 8}
+        c.box[0] = (16 << {"32b": 1, "64b": 2, "128b": 3}[c.swizzle.split("_")[0]]) // es[c.dtype]
+    stages = int(g.choice([1, 2, 3, 4, 5, 6, 8]))
+    variant = int(g.integers(0, 64))
+    grid = int(g.choice([0, 0, 1, 3, 64, 1000]))
+    say("copy random", seed, c.dtype, c.dims, c.box, c.swizzle, stages, variant, grid)
+    sd = to_dev(c.buf)
+    dd = empty_dev(c.buf.size, 0x5A)
+    ms = encode(sd, c.dtype, c.dims, c.strides, c.box, None, c.swizzle)
+    md = encode(dd, c.dtype, c.dims, c.strides, c.box, None, c.swizzle)
+    att.tile_copy_ex(ms, md, stages, grid, variant, stream())
+    torch.cuda.synchronize()
+    got = to_host(dd)
+    mask = _tensor_byte_mask(c)
+    want = np.where(mask, c.buf, np.uint8(0x5A))
+    np.testing.assert_array_equal(got, want)
+
+
 def test_copy_grid_sweep_small():
     ex = W.COPY_8192
     for grid in (1, 255, 256, 1024, 4096):
