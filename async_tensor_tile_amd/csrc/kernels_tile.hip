@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load(TmapImpl m, const i
     const uint32_t nchunk = m.box_bytes >> 4;
     uint8_t* dst = out + (size_t)b * m.box_bytes;
     for (uint32_t i = tid; i < nchunk; i += blockDim.x)
-        *reinterpret_cast<u32x4*>(dst + i * 16u) = *reinterpret_cast<const u32x4*>(smem + i * 16u);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(smem + i * 16u), reinterpret_cast<u32x4*>(dst + i * 16u));
 }
 
 // ---- im2col mode ------------------------------------------------------------
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load_im2col(Im2colImpl m
     txbar_wait(bar, 0);
     uint8_t* dst = out + (size_t)b * m.box_bytes;
     for (uint32_t i = tid; i < nchunk; i += blockDim.x)
-        *reinterpret_cast<u32x4*>(dst + i * 16u) = *reinterpret_cast<const u32x4*>(smem + i * 16u);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(smem + i * 16u), reinterpret_cast<u32x4*>(dst + i * 16u));
 }
 
 // Stage the raw image of box b into LDS, then store / reduce it through the map.
