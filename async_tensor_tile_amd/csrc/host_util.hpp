@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "tmap.h"
-#include "tmap_impl.hpp"
+#include "att/tmap_impl.hpp"
 
 namespace att {
 

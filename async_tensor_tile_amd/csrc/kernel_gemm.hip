@@ -24,7 +24,7 @@
 #include <utility>
 
 #include "host_util.hpp"
-#include "tile_device.hpp"
+#include "att/tile_device.hpp"
 #include "tmap.h"
 
 namespace att {

@@ -9,7 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include "host_util.hpp"
-#include "tile_device.hpp"
+#include "att/tile_device.hpp"
 #include "tmap.h"
 
 namespace att {

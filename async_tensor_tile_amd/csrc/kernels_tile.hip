@@ -1,6 +1,7 @@
 // kernels_tile.hip -- batch load / store / reduce-add kernels, the
 // byte-counted barrier self-test and the LDS bank-sector probe, with their
-// C-ABI launchers.
+// C-ABI launchers.  The batch kernels are written against the public device
+// API (tile.hpp) and take the host's 128-byte map by value.
 //
 // Batch kernels run one workgroup (4 waves) per box: the box goes through a
 // real LDS image, exactly as a single copy of [HPC] "single-tile load" /
@@ -10,7 +11,7 @@
 #include <cstring>
 
 #include "host_util.hpp"
-#include "tile_device.hpp"
+#include "tile.hpp"
 #include "tmap.h"
 
 namespace att {
@@ -24,23 +25,22 @@ __device__ __forceinline__ void read_coords(const TmapImpl& m, const int32_t* __
 }
 
 // Load box b into LDS with the byte-counted barrier, then dump the image.
-__global__ __launch_bounds__(kBatchThreads) void k_tile_load(TmapImpl m, const int32_t* __restrict__ coords,
+__global__ __launch_bounds__(kBatchThreads) void k_tile_load(tmap_t map, const int32_t* __restrict__ coords,
                                                             uint8_t* __restrict__ out, uint32_t bar_off) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     TxBar* bar = reinterpret_cast<TxBar*>(smem + bar_off);
+    const TmapImpl& m = tmap_tiled(map);
     const uint32_t b = blockIdx.x;
     const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
     int32_t c[5];
     read_coords(m, coords, b, c);
     if (tid == 0) {
         txbar_init(bar, 1);
-        txbar_arrive_expect_tx(bar, (int32_t)m.box_bytes);   // expect before any copy is issued
+        txbar_arrive_expect_tx(bar, (int32_t)tile_box_bytes(map));   // expect before any copy is issued
     }
     __syncthreads();
-    const uint32_t bytes = tile_load_issue(m, c, smem, wave, nwaves);
-    wait_vmcnt<0>();
-    wait_lgkm0();
-    if (lane_id() == 0 && bytes) txbar_complete_tx(bar, (int32_t)bytes);
+    const uint32_t bytes = tile_load_async(map, c, smem, wave, nwaves);
+    tile_load_arrive(bar, bytes);
     txbar_wait(bar, 0);
     const uint32_t nchunk = m.box_bytes >> 4;
     uint8_t* dst = out + (size_t)b * m.box_bytes;
@@ -48,81 +48,14 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load(TmapImpl m, const i
         __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(smem + i * 16u), reinterpret_cast<u32x4*>(dst + i * 16u));
 }
 
-// ---- im2col mode ------------------------------------------------------------
-// Window origins form a mixed-radix number (W digit fastest, image index
-// last); pixel r of a load is the origin r positions after the one its
-// coordinates name (a start between grid points snaps down to the grid).
-
-__device__ __forceinline__ int64_t floor_div64(int64_t a, int64_t b) {
-    int64_t q = a / b;
-    if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
-    return q;
-}
-
-// One pixel row: whether the whole pixel (all spatial dims and the image
-// index) lies inside the tensor, and its byte offset without the channel.
-struct PixelLoc {
-    int64_t off;
-    bool in;
-};
-
-__device__ __forceinline__ PixelLoc im2col_pixel(const Im2colImpl& m, int64_t L, const int32_t off[3]) {
-    const int S = m.rank - 2;
-    PixelLoc r;
-    r.off = 0;
-    r.in = true;
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        if (s < S) {
-            const int64_t n = (int64_t)m.npos[s];
-            const int64_t q = floor_div64(L, n);
-            const int64_t digit = L - q * n;
-            L = q;
-            const int64_t x = (int64_t)m.lower[s] + digit * (int64_t)m.es[s + 1] + (int64_t)off[s];
-            r.in = r.in && x >= 0 && x < m.dim[s + 1];
-            r.off += x * (int64_t)m.stride[s];
-        }
-    }
-    r.in = r.in && L >= 0 && L < m.dim[m.rank - 1];
-    r.off += L * (int64_t)m.stride[m.rank - 2];
-    return r;
-}
-
-template <typename T>
-__device__ __forceinline__ u32x4 im2col_gather_t(const Im2colImpl& m, const PixelLoc& P, int64_t ch0) {
-    constexpr int N = 16 / (int)sizeof(T);
-    union { u32x4 v; T e[N]; } u;
-    const T fillv = *reinterpret_cast<const T*>(g_fill_rows[m.fill_idx]);
-    const ATT_GLOBAL T* row = (const ATT_GLOBAL T*)gptr(m.base + (uint64_t)P.off);
-#pragma unroll
-    for (int e = 0; e < N; ++e) {
-        const int64_t ch = ch0 + e;
-        const bool in = P.in && ch >= 0 && ch < m.dim[0];
-        u.e[e] = in ? row[ch] : fillv;
-    }
-    return u.v;
-}
-
-__device__ __forceinline__ u32x4 im2col_gather(const Im2colImpl& m, const PixelLoc& P, int64_t ch0) {
-    switch (m.esize) {
-    case 1: return im2col_gather_t<uint8_t>(m, P, ch0);
-    case 2: return im2col_gather_t<uint16_t>(m, P, ch0);
-    case 4: return im2col_gather_t<uint32_t>(m, P, ch0);
-    default: return im2col_gather_t<uint64_t>(m, P, ch0);
-    }
-}
-
 // Load box b of an im2col map into LDS (swizzle on write, byte-counted
-// completion as in the tiled load), then dump the image.  Lane l of group grp
-// fills physical chunk grp*64 + l with logical chunk swz(p): its pixel row and
-// channel block.  Whole in-range, 16-byte aligned chunks and wholly
-// out-of-range chunks (read from the fill row) go through global_load_lds;
-// chunks cut by the channel edge are gathered by their lane.
-__global__ __launch_bounds__(kBatchThreads) void k_tile_load_im2col(Im2colImpl m, const int32_t* __restrict__ coords,
+// completion as in the tiled load), then dump the image.
+__global__ __launch_bounds__(kBatchThreads) void k_tile_load_im2col(tmap_t map, const int32_t* __restrict__ coords,
                                                                    const int32_t* __restrict__ offsets,
                                                                    uint8_t* __restrict__ out, uint32_t bar_off) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     TxBar* bar = reinterpret_cast<TxBar*>(smem + bar_off);
+    const Im2colImpl& m = tmap_im2col(map);
     const uint32_t b = blockIdx.x;
     const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
     const int R = m.rank, S = R - 2;
@@ -134,43 +67,15 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load_im2col(Im2colImpl m
 #pragma unroll
     for (int s = 0; s < 3; ++s)
         if (s < S) off[s] = offsets[(size_t)b * S + s];
-    int64_t L0 = c[R - 1];
-#pragma unroll
-    for (int s = 2; s >= 0; --s)
-        if (s < S)
-            L0 = L0 * (int64_t)m.npos[s] + floor_div64((int64_t)c[s + 1] - m.lower[s], (int64_t)m.es[s + 1]);
     if (tid == 0) {
         txbar_init(bar, 1);
         txbar_arrive_expect_tx(bar, (int32_t)m.box_bytes);
     }
     __syncthreads();
-    const uint32_t lane = lane_id();
-    const uint32_t nchunk = m.box_bytes >> 4;
-    const int64_t n_el = 16 / m.esize;
-    const bool aligned = (((int64_t)c[0] * m.esize) & 15) == 0;
-    const void* fill = g_fill_rows[m.fill_idx];
-    uint32_t bytes = 0;
-    for (uint32_t grp = wave; grp * 64u < nchunk; grp += nwaves) {
-        const uint32_t p = grp * 64u + lane;
-        const bool active = p < nchunk;
-        const uint32_t rem = nchunk - grp * 64u;
-        bytes += 16u * (rem < 64u ? rem : 64u);
-        const uint32_t q = active ? swz_chunk(p, m.swizzle) : 0u;
-        const uint32_t row = q / m.cpr;
-        const uint32_t j = q - row * m.cpr;
-        const PixelLoc P = im2col_pixel(m, L0 + (int64_t)row, off);
-        const int64_t ch0 = (int64_t)c[0] + (int64_t)j * n_el;
-        const bool full_in = P.in && ch0 >= 0 && ch0 + n_el <= m.dim[0];
-        const bool full_out = !P.in || ch0 >= m.dim[0] || ch0 + n_el <= 0;
-        const bool partial = !aligned || (!full_in && !full_out);
-        const void* src = full_in ? (const void*)(uintptr_t)(m.base + (uint64_t)P.off + (uint64_t)ch0 * m.esize) : fill;
-        if (active && !partial) dma16(src, smem + grp * 1024u);
-        if (active && partial) *reinterpret_cast<u32x4*>(smem + p * 16u) = im2col_gather(m, P, ch0);
-    }
-    wait_vmcnt<0>();
-    wait_lgkm0();
-    if (lane == 0 && bytes) txbar_complete_tx(bar, (int32_t)bytes);
+    const uint32_t bytes = tile_load_im2col_async(map, c, off, smem, wave, nwaves);
+    tile_load_arrive(bar, bytes);
     txbar_wait(bar, 0);
+    const uint32_t nchunk = m.box_bytes >> 4;
     uint8_t* dst = out + (size_t)b * m.box_bytes;
     for (uint32_t i = tid; i < nchunk; i += blockDim.x)
         __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(smem + i * 16u), reinterpret_cast<u32x4*>(dst + i * 16u));
@@ -178,9 +83,10 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load_im2col(Im2colImpl m
 
 // Stage the raw image of box b into LDS, then store / reduce it through the map.
 template <int OP>
-__global__ __launch_bounds__(kBatchThreads) void k_tile_store(TmapImpl m, const int32_t* __restrict__ coords,
+__global__ __launch_bounds__(kBatchThreads) void k_tile_store(tmap_t map, const int32_t* __restrict__ coords,
                                                              const uint8_t* __restrict__ in) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    const TmapImpl& m = tmap_tiled(map);
     const uint32_t b = blockIdx.x;
     const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
     int32_t c[5];
@@ -193,25 +99,29 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_store(TmapImpl m, const 
     }
     wait_vmcnt<0>();
     __syncthreads();
-    tile_store_issue<OP>(m, c, smem, wave, nwaves);
+    if constexpr (OP == ST_STORE) tile_store_async(map, c, smem, wave, nwaves);
+    else if constexpr (OP == ST_ADD) tile_reduce_async<TMAP_REDUCE_ADD>(map, c, smem, wave, nwaves);
+    else if constexpr (OP == ST_MIN) tile_reduce_async<TMAP_REDUCE_MIN>(map, c, smem, wave, nwaves);
+    else tile_reduce_async<TMAP_REDUCE_MAX>(map, c, smem, wave, nwaves);
 }
 
 // Byte-counted barrier self-test: one barrier (arrival count 1) completes
 // after `ntile` copies signal their own byte counts.  Trace records are
 // (who, arrivals_left, pending, phase); who = -1 init, -2 arrive.expect_tx,
 // t >= 0 the complete-tx of tile t.
-__global__ __launch_bounds__(kBatchThreads) void k_txbar_selftest(TmapImpl m, const int32_t* __restrict__ coords,
+__global__ __launch_bounds__(kBatchThreads) void k_txbar_selftest(tmap_t map, const int32_t* __restrict__ coords,
                                                                  uint32_t ntile, int32_t* __restrict__ trace,
                                                                  uint8_t* __restrict__ out, uint32_t img_stride,
                                                                  uint32_t bar_off) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     TxBar* bar = reinterpret_cast<TxBar*>(smem + bar_off);
     uint32_t* counter = reinterpret_cast<uint32_t*>(smem + bar_off + sizeof(TxBar));
+    const TmapImpl& m = tmap_tiled(map);
     const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
     if (tid == 0) {
         txbar_init(bar, 1);
         trace[0] = -1; trace[1] = bar->expected; trace[2] = 0; trace[3] = 0;
-        const TxState s = txbar_arrive_expect_tx(bar, (int32_t)(m.box_bytes * ntile));
+        const TxState s = txbar_arrive_expect_tx(bar, (int32_t)(tile_box_bytes(map) * ntile));
         trace[4] = -2; trace[5] = s.arrivals_left; trace[6] = s.pending; trace[7] = (int32_t)s.phase;
         *counter = 0;
     }
@@ -219,7 +129,9 @@ __global__ __launch_bounds__(kBatchThreads) void k_txbar_selftest(TmapImpl m, co
     for (uint32_t t = wave; t < ntile; t += nwaves) {
         int32_t c[5];
         read_coords(m, coords, t, c);
-        const uint32_t bytes = tile_load_issue(m, c, smem + t * img_stride, 0, 1);
+        // one wave issues the whole box, then reports its bytes itself so the
+        // state after each complete-tx can be recorded
+        const uint32_t bytes = tile_load_async(map, c, smem + t * img_stride, 0, 1);
         wait_vmcnt<0>();
         wait_lgkm0();
         if (lane_id() == 0) {
@@ -317,7 +229,7 @@ extern "C" tmap_status tile_load(const tmap_t* m, const int32_t* d_coords, uint3
     const uint32_t lds = bar_off + 64u;
     tmap_status st = prepare_dynamic_lds((const void*)k_tile_load, lds);
     if (st) return st;
-    hipLaunchKernelGGL(k_tile_load, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), t, d_coords,
+    hipLaunchKernelGGL(k_tile_load, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), *m, d_coords,
                        static_cast<uint8_t*>(d_lds_image_out), bar_off);
     return check_launch("tile_load");
 }
@@ -333,7 +245,7 @@ static tmap_status launch_store(const tmap_t* m, const int32_t* d_coords, uint32
     const uint32_t lds = round_up(t.box_bytes, 1024u);
     tmap_status st = prepare_dynamic_lds((const void*)k_tile_store<OP>, lds);
     if (st) return st;
-    hipLaunchKernelGGL(k_tile_store<OP>, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), t,
+    hipLaunchKernelGGL(k_tile_store<OP>, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), *m,
                        d_coords, static_cast<const uint8_t*>(d_in));
     return check_launch(name);
 }
@@ -370,7 +282,7 @@ extern "C" tmap_status tile_load_im2col(const tmap_t* m, const int32_t* d_coords
     const uint32_t lds = bar_off + 64u;
     tmap_status st = prepare_dynamic_lds((const void*)k_tile_load_im2col, lds);
     if (st) return st;
-    hipLaunchKernelGGL(k_tile_load_im2col, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), t, d_coords,
+    hipLaunchKernelGGL(k_tile_load_im2col, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), *m, d_coords,
                        d_offsets, static_cast<uint8_t*>(d_lds_image_out), bar_off);
     return check_launch("tile_load_im2col");
 }
@@ -387,7 +299,7 @@ extern "C" tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, 
     const uint32_t lds = bar_off + 64u;
     tmap_status st = prepare_dynamic_lds((const void*)k_txbar_selftest, lds);
     if (st) return st;
-    hipLaunchKernelGGL(k_txbar_selftest, dim3(1), dim3(kBatchThreads), lds, as_stream(stream), t, d_coords, ntile,
+    hipLaunchKernelGGL(k_txbar_selftest, dim3(1), dim3(kBatchThreads), lds, as_stream(stream), *m, d_coords, ntile,
                        d_trace, static_cast<uint8_t*>(d_lds_image_out), img_stride, bar_off);
     return check_launch("txbar_selftest");
 }

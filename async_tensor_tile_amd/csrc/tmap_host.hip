@@ -11,7 +11,7 @@
 #include <cstring>
 
 #include "tmap.h"
-#include "tmap_impl.hpp"
+#include "att/tmap_impl.hpp"
 #include "host_util.hpp"
 
 namespace att {

@@ -26,8 +26,8 @@ BYTES_PER_STEP = 2 * 8192 * 8192 * 2
 HBM_PEAK_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 COUNTERS_FILE = os.path.join(PROFILE_DIR, "tile_copy_bf16_8192_counters.json")
-KERNEL_SOURCES = ("async_tensor_tile_amd/csrc/kernel_copy.hip", "async_tensor_tile_amd/csrc/tile_device.hpp",
-                  "async_tensor_tile_amd/csrc/tmap_impl.hpp")
+KERNEL_SOURCES = ("async_tensor_tile_amd/csrc/kernel_copy.hip", "include/att/tile_device.hpp",
+                  "include/att/tmap_impl.hpp")
 
 
 def kernel_source_hash() -> str:

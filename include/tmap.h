@@ -25,6 +25,9 @@
  *     text for tmap_last_error().
  *   - Calls are reentrant; concurrent calls on different streams are safe as
  *     long as their destination memory does not overlap.
+ *
+ * Kernels that move tiles themselves use the device API in tile.hpp with the
+ * same maps, passed to the kernel by value.
  */
 #ifndef ATT_TMAP_H
 #define ATT_TMAP_H
