@@ -204,6 +204,14 @@ __global__ __launch_bounds__(64) void k_lds_bank_probe(int32_t layout, uint32_t 
     if (sink == 0xFFFFFFFFu) hist[0] = -1;   // keeps the timed reads alive
 }
 
+// The caller's descriptor by value for a kernel argument; copied bytewise,
+// since the caller's 128 bytes need not sit at tmap_t's 64-byte alignment.
+static tmap_t map_value(const tmap_t* m) {
+    tmap_t v;
+    std::memcpy(&v, m, sizeof(v));
+    return v;
+}
+
 static tmap_status prepare_dynamic_lds(const void* fn, uint32_t bytes) {
     uint32_t limit = 0;
     tmap_status st = device_lds_limit(&limit);
@@ -229,7 +237,7 @@ extern "C" tmap_status tile_load(const tmap_t* m, const int32_t* d_coords, uint3
     const uint32_t lds = bar_off + 64u;
     tmap_status st = prepare_dynamic_lds((const void*)k_tile_load, lds);
     if (st) return st;
-    hipLaunchKernelGGL(k_tile_load, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), *m, d_coords,
+    hipLaunchKernelGGL(k_tile_load, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), map_value(m), d_coords,
                        static_cast<uint8_t*>(d_lds_image_out), bar_off);
     return check_launch("tile_load");
 }
@@ -245,7 +253,7 @@ static tmap_status launch_store(const tmap_t* m, const int32_t* d_coords, uint32
     const uint32_t lds = round_up(t.box_bytes, 1024u);
     tmap_status st = prepare_dynamic_lds((const void*)k_tile_store<OP>, lds);
     if (st) return st;
-    hipLaunchKernelGGL(k_tile_store<OP>, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), *m,
+    hipLaunchKernelGGL(k_tile_store<OP>, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), map_value(m),
                        d_coords, static_cast<const uint8_t*>(d_in));
     return check_launch(name);
 }
@@ -282,7 +290,7 @@ extern "C" tmap_status tile_load_im2col(const tmap_t* m, const int32_t* d_coords
     const uint32_t lds = bar_off + 64u;
     tmap_status st = prepare_dynamic_lds((const void*)k_tile_load_im2col, lds);
     if (st) return st;
-    hipLaunchKernelGGL(k_tile_load_im2col, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), *m, d_coords,
+    hipLaunchKernelGGL(k_tile_load_im2col, dim3(nbox), dim3(kBatchThreads), lds, as_stream(stream), map_value(m), d_coords,
                        d_offsets, static_cast<uint8_t*>(d_lds_image_out), bar_off);
     return check_launch("tile_load_im2col");
 }
@@ -299,7 +307,7 @@ extern "C" tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, 
     const uint32_t lds = bar_off + 64u;
     tmap_status st = prepare_dynamic_lds((const void*)k_txbar_selftest, lds);
     if (st) return st;
-    hipLaunchKernelGGL(k_txbar_selftest, dim3(1), dim3(kBatchThreads), lds, as_stream(stream), *m, d_coords, ntile,
+    hipLaunchKernelGGL(k_txbar_selftest, dim3(1), dim3(kBatchThreads), lds, as_stream(stream), map_value(m), d_coords, ntile,
                        d_trace, static_cast<uint8_t*>(d_lds_image_out), img_stride, bar_off);
     return check_launch("txbar_selftest");
 }
