@@ -89,6 +89,7 @@ __device__ __forceinline__ void mfma_drain() {
 
 template <int NI, int NJ, int KK, int AR = NI / 2>
 struct GemmSched {
+    static constexpr int NA = NI;                     // A fragments (ids 0..NA-1; B fragments follow)
     static constexpr int SUB = NI * NJ;
     static constexpr int HALF = AR * NJ;              // slots of rows NI-AR.. of the last sub-step
     static constexpr int NF = NI + NJ;                // fragments per sub-step
@@ -143,6 +144,51 @@ static_assert(GemmSched<4, 4, 2>::lgkm(0) == -1 && GemmSched<4, 4, 2>::lgkm(31) 
 static_assert(GemmSched<8, 8, 2>::lgkm(32) == 14 && GemmSched<8, 8, 2>::SLOTS == 128, "schedule");
 static_assert(GemmSched<8, 8, 2, 6>::mi(0) == 2 && GemmSched<8, 8, 2, 6>::mi(47) == 7 && GemmSched<8, 8, 2, 6>::mi(127) == 1,
               "schedule");
+
+// The schedule's lgkmcnt waits with the redundant ones dropped: LDS reads
+// complete in issue order, so once a wait has covered read p, a later MFMA
+// that needs read p or an earlier one needs no wait of its own (which would
+// cost an issue slot and nothing else).  w[m] is the count to wait for before
+// slot m's MFMA, or -1 for none; every wait that remains equals Sch::lgkm(m).
+template <typename Sch>
+struct GemmWaits {
+    int w[Sch::SLOTS];
+    constexpr GemmWaits() : w() {
+        int last[2][Sch::NF] = {};   // index of the latest read of fragment f into buffer b, -1 for none
+        for (int b = 0; b < 2; ++b)
+            for (int f = 0; f < Sch::NF; ++f) last[b][f] = -1;
+        int nread = 0, covered = -1;
+        for (int m = 0; m < Sch::SLOTS; ++m) {
+            const int b = Sch::mbuf(m);
+            const int pa = last[b][Sch::mi(m)], pb = last[b][Sch::NA + Sch::mj(m)];
+            const int p = pa > pb ? pa : pb;
+            if (p < 0 || p <= covered) {
+                w[m] = -1;
+            } else {
+                const int c = nread - p - 1 > 15 ? 15 : nread - p - 1;
+                w[m] = c;
+                covered = nread - c - 1;
+            }
+            const int f = Sch::rfrag(m);
+            if (f >= 0) last[Sch::rbuf(m)][f] = nread++;
+        }
+    }
+};
+template <typename Sch>
+constexpr GemmWaits<Sch> kGemmWaits{};
+
+template <typename Sch>
+constexpr bool waits_consistent() {
+    int kept = 0;
+    for (int m = 0; m < Sch::SLOTS; ++m) {
+        const int w = kGemmWaits<Sch>.w[m];
+        if (w >= 0 && w != Sch::lgkm(m)) return false;
+        if (w < 0 && Sch::lgkm(m) < 0) continue;
+        kept += w >= 0;
+    }
+    return kept > 0;
+}
+static_assert(waits_consistent<GemmSched<8, 8, 2, 4>>() && waits_consistent<GemmSched<4, 4, 2>>(), "pruned waits");
 
 template <int N>
 __device__ __forceinline__ void wait_lgkm() {
@@ -460,7 +506,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         const uint32_t la = lds0 + slot_fill * BOX + wave_u * GPW * 1024u;
         static_for<SLOTS>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
-            constexpr int W = Sch::lgkm(m);
+            constexpr int W = kGemmWaits<Sch>.w[m];
             if constexpr (W >= 0) {
                 wait_lgkm<W>();
                 __builtin_amdgcn_sched_barrier(0);
@@ -681,7 +727,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         const uint32_t kb1 = clamp_k(t + 1u), ka2 = clamp_k(t + 2u);
         static_for<SLOTS>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
-            constexpr int W = Sch::lgkm(m);
+            constexpr int W = kGemmWaits<Sch>.w[m];
             if constexpr (W >= 0) {
                 wait_lgkm<W>();
                 __builtin_amdgcn_sched_barrier(0);
