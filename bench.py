@@ -74,8 +74,14 @@ def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 8):
             break
     dt = time.perf_counter() - t0
     ok = bool(np.array_equal(dst, src))
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": round(passes * BYTES_PER_STEP / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "verified": ok,
+            "kind": "oracle", "verified": ok, "cpu_model": cpu,
             "sample": f"{passes} full pass(es) of the 8192-box bf16 8192x8192 round trip "
                       f"(load to LDS image + store), {dt:.1f} s on one host thread"}
 
