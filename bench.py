@@ -327,8 +327,9 @@ def main():
                     help="bk,stages[,k256][,mfma] e.g. 32,4,k256 or 64,2,k256,32 (with --only gemm)")
     ap.add_argument("--ref-copy", action="store_true",
                     help="also time a plain device-to-device copy of the same bytes")
-    ap.add_argument("--ceiling", action="store_true",
-                    help="also time plain read-only, write-only and copy kernels over the same working sets")
+    ap.add_argument("--ceiling", action="store_true", help="time the HBM ceiling too (the default)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip timing plain read-only, write-only and copy kernels over the same working sets")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -462,8 +463,10 @@ def main():
     }
     if ref_copy:
         result["reference_copy"] = ref_copy
-    if args.ceiling:
-        result["hbm_ceiling"] = hbm_ceiling(att, torch, stream)
+    if not args.no_ceiling:
+        ceil = hbm_ceiling(att, torch, stream)
+        result["hbm_ceiling"] = ceil
+        result["frac_of_linear_copy"] = round(gbs / ceil["copy_GBps"], 4)
     if not args.no_extra:
         result["extra"] = run_extra(att, torch, stream, 20)
     if not args.no_cpu_baseline:
