@@ -676,6 +676,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     typedef std::integral_constant<int, 0> opA;
     typedef std::integral_constant<int, 1> opB;
 
+    // Prologue: A_0, B_0, A_1 into slots 0, 1, 2, issued first so that the
+    // register set-up below overlaps their latency.
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) copy_unit(opA{}, 0u, 0u, c);
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) copy_unit(opB{}, 0u, 1u, c);
+#pragma unroll
+    for (int c = 0; c < NDMA; ++c) copy_unit(opA{}, clamp_k(1u), 2u, c);
+    __builtin_amdgcn_sched_barrier(0);
+
     AccT acc[NI][NJ];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
@@ -705,13 +715,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
     };
 
-    // Prologue: A_0, B_0, A_1 into slots 0, 1, 2; wait for A_0 and B_0.
-#pragma unroll
-    for (int c = 0; c < NDMA; ++c) copy_unit(opA{}, 0u, 0u, c);
-#pragma unroll
-    for (int c = 0; c < NDMA; ++c) copy_unit(opB{}, 0u, 1u, c);
-#pragma unroll
-    for (int c = 0; c < NDMA; ++c) copy_unit(opA{}, clamp_k(1u), 2u, c);
+    // wait for A_0 and B_0
     wait_vmcnt<NDMA>();
     wait_lgkm0();
     wg_barrier();
