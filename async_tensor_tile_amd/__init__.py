@@ -97,9 +97,10 @@ def lib():
         L.hbm_probe.argtypes = [_I32, _V, _V, ctypes.c_uint64, _V]
         L.gemm_bf16.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
         L.gemm_bf16_ex.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _V]
+        L.gemm_bf16_f32.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
         for name in ("tmap_encode", "tmap_replace_address", "tmap_query", "tile_load", "tile_store",
                      "tile_reduce_add", "tile_reduce", "tmap_encode_im2col", "tile_load_im2col", "tile_copy", "tile_copy_ex", "txbar_selftest",
-                     "lds_bank_probe", "hbm_probe", "gemm_bf16", "gemm_bf16_ex"):
+                     "lds_bank_probe", "hbm_probe", "gemm_bf16", "gemm_bf16_ex", "gemm_bf16_f32"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -240,6 +241,13 @@ def gemm_bf16(A: tmap_t, B: tmap_t, d_C, M: int, N: int, K: int, ldc: int, stage
               stream=0) -> None:
     _check(lib().gemm_bf16(ctypes.byref(A), ctypes.byref(B), _addr(d_C), int(M), int(N), int(K),
                            int(ldc), int(stages), _addr(stream)), "gemm_bf16")
+
+
+def gemm_bf16_f32(A: tmap_t, B: tmap_t, d_C, M: int, N: int, K: int, ldc: int, stages: int = 2,
+                  stream=0) -> None:
+    """gemm_bf16 with an fp32 C: the unrounded accumulators."""
+    _check(lib().gemm_bf16_f32(ctypes.byref(A), ctypes.byref(B), _addr(d_C), int(M), int(N), int(K),
+                               int(ldc), int(stages), _addr(stream)), "gemm_bf16_f32")
 
 
 def gemm_bf16_ex(A: tmap_t, B: tmap_t, d_C, M: int, N: int, K: int, ldc: int, stages: int = 2,

@@ -241,7 +241,7 @@ __device__ __forceinline__ void gemm_block_tile(const GemmArgs& g, uint32_t& tm,
 
 // Epilogue of a workgroup's 256 x 256 C tile from the accumulators of its
 // four waves (2 x 2 blocks of 128 x 128, NI x NJ tiles of MI x MI each).
-template <int MI, typename AccT, int NI, int NJ>
+template <int MI, bool CF32, typename AccT, int NI, int NJ>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI][NJ], uint32_t lds0, uint32_t wave,
                                               uint32_t lane, uint32_t m0, uint32_t n0) {
     // Epilogue.  The MFMAs take B as their first operand, so accumulator
@@ -253,6 +253,33 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI]
     const uint32_t wm = wave >> 1, wn = wave & 1;
     const uint32_t rloc = wm * 128u + (lane % (uint32_t)MI);
     const uint32_t cloc = wn * 128u + (lane / (uint32_t)MI) * 4u;
+    if constexpr (CF32) {
+        // fp32 C straight from the accumulators: each group of four
+        // registers is four consecutive columns of one row, one 16-byte
+        // store where C allows it, element stores at the N edge.
+        ATT_GLOBAL float* C = (ATT_GLOBAL float*)gptr(g.C);
+        const bool vec = (g.C & 15u) == 0 && g.ldc % 4u == 0;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const uint32_t row = m0 + rloc + (uint32_t)i * (uint32_t)MI;
+                    const uint32_t col = n0 + cloc + (uint32_t)j * (uint32_t)MI + (uint32_t)q * 8u;
+                    if (row >= g.M) continue;
+                    ATT_GLOBAL float* dst = C + (uint64_t)row * g.ldc + col;
+                    if (vec && col + 4u <= g.N) {
+                        *(ATT_GLOBAL f32x4*)dst = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                        acc[i][j][4 * q + 3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (col + (uint32_t)e < g.N) dst[e] = acc[i][j][4 * q + e];
+                    }
+                }
+        return;
+    }
     if (g.c_staged) {
         // Registers -> LDS -> global, as the pages' epilogue does: the
         // workgroup's 256 x 256 tile becomes four 256 x 64 box images of the
@@ -350,7 +377,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI]
 // 16 (v_mfma_f32_16x16x32_bf16, 8 x 8 tiles).  Both run 1024 flop per clock
 // per SIMD; the 16 x 16 form moves less accumulator and operand register
 // data per flop, which under the chip's power limit holds a higher clock.
-template <int BK, int S, bool EDGE, int SWM, int MI>
+template <int BK, int S, bool EDGE, int SWM, int MI, bool CF32>
 __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16(GemmArgs g) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr uint32_t ROWB = BK * 2;                 // bytes per LDS row (128 or 64)
@@ -607,7 +634,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         }
     }
     iteration(without_c{}, slot_rt{}, t, slot_t, slot_fill, 0u, false);
-    gemm_epilogue<MI>(g, acc, lds0, wave, lane, m0, n0);
+    gemm_epilogue<MI, CF32>(g, acc, lds0, wave, lane, m0, n0);
 }
 
 // Operand ring for 64-deep boxes with 16 x 16 x 32 MFMAs: five 32 KiB slots
@@ -624,7 +651,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
 // boundaries), so fragment f of a slot sits f * 2048 bytes further and the
 // slot offset within the window rides in the ds_read immediate too.  K a
 // multiple of 64; partial M / N tiles clamp their rows as k_gemm_bf16 does.
-template <int SWM>
+template <int SWM, bool CF32>
 __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16_ring5(GemmArgs g) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr uint32_t RING = 5;
@@ -777,24 +804,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         if (t + 3u < NT) body(std::integral_constant<int, 3>{}, t + 3u);
         if (t + 4u < NT) body(std::integral_constant<int, 4>{}, t + 4u);
     }
-    gemm_epilogue<MI>(g, acc, lds0, wave, lane, m0, n0);
+    gemm_epilogue<MI, CF32>(g, acc, lds0, wave, lane, m0, n0);
 }
 
-template <int SWM>
+template <int SWM, bool CF32 = false>
 static tmap_status launch_gemm_ring5(const GemmArgs& g, hipStream_t st) {
     constexpr uint32_t lds = 5u * kTM * 128u;        // 160 KiB: the ring (the C image reuses it)
     uint32_t limit = 0;
     tmap_status s = device_lds_limit(&limit);
     if (s) return s;
     if (lds > limit) return TMAP_ERR_UNSUPPORTED;
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16_ring5<SWM>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16_ring5<SWM, CF32>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-    hipLaunchKernelGGL((k_gemm_bf16_ring5<SWM>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st, g);
+    hipLaunchKernelGGL((k_gemm_bf16_ring5<SWM, CF32>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st, g);
     return check_launch("gemm_bf16");
 }
 
-template <int BK, int S, bool EDGE, int SWM, int MI>
+template <int BK, int S, bool EDGE, int SWM, int MI, bool CF32 = false>
 static tmap_status launch_gemm_t(const GemmArgs& g, hipStream_t st) {
     // The ring, or the 128 KiB C staging image if that is larger.
     constexpr uint32_t ring = (uint32_t)S * 2u * kTM * BK * 2u;
@@ -803,10 +830,10 @@ static tmap_status launch_gemm_t(const GemmArgs& g, hipStream_t st) {
     tmap_status s = device_lds_limit(&limit);
     if (s) return s;
     if (lds > limit) return TMAP_ERR_UNSUPPORTED;
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16<BK, S, EDGE, SWM, MI>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_bf16<BK, S, EDGE, SWM, MI, CF32>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-    hipLaunchKernelGGL((k_gemm_bf16<BK, S, EDGE, SWM, MI>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st,
+    hipLaunchKernelGGL((k_gemm_bf16<BK, S, EDGE, SWM, MI, CF32>), dim3(g.tiles_m * g.tiles_n), dim3(kGemmThreads), lds, st,
                        g);
     return check_launch("gemm_bf16");
 }
@@ -858,13 +885,14 @@ static tmap_status check_operand(const TmapImpl& t, uint32_t rows, uint32_t K, u
 
 using namespace att;
 
-extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
-                                    uint32_t K, uint32_t ldc, uint32_t stages, uint32_t group_m, uint32_t xcd,
-                                    uint32_t mfma, void* stream) {
+static tmap_status gemm_run(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N, uint32_t K,
+                            uint32_t ldc, uint32_t stages, uint32_t group_m, uint32_t xcd, uint32_t mfma,
+                            bool c_f32, void* stream) {
     if (mfma != 0 && mfma != 16 && mfma != 32) return TMAP_ERR_UNSUPPORTED;
     if (!A || !B || !d_C) return TMAP_ERR_NULL;
     if (M == 0 || N == 0) return TMAP_OK;
-    if (K == 0 || ldc < N || (reinterpret_cast<uintptr_t>(d_C) & 1u)) return TMAP_ERR_UNSUPPORTED;
+    const uintptr_t calign = c_f32 ? 3u : 1u;
+    if (K == 0 || ldc < N || (reinterpret_cast<uintptr_t>(d_C) & calign)) return TMAP_ERR_UNSUPPORTED;
     GemmArgs g;
     g.A = load_map(A);
     g.B = load_map(B);
@@ -889,7 +917,7 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
         if (g.group_m > g.blk_m || g.blk_m % g.group_m) g.group_m = g.blk_m;
     }
     g.c_staged = 0;
-    if ((reinterpret_cast<uintptr_t>(d_C) & 15u) == 0 && ldc % 8u == 0) {
+    if (!c_f32 && (reinterpret_cast<uintptr_t>(d_C) & 15u) == 0 && ldc % 8u == 0) {
         tmap_t cm;
         const uint64_t cdim[2] = {N, M};
         const uint64_t cstride[1] = {(uint64_t)ldc * 2u};
@@ -901,6 +929,20 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
         }
     }
     hipStream_t st = as_stream(stream);
+    if (c_f32) {
+        // fp32 C: the 64-deep K step with 16 x 16 x 32 MFMAs
+        if (bka != 64 || mfma == 32) return TMAP_ERR_UNSUPPORTED;
+        if (stages == 2) {
+            if (swa & 4u) return launch_gemm_t<64, 2, false, TMAP_SWIZZLE_128B_K256, 16, true>(g, st);
+            return launch_gemm_t<64, 2, false, TMAP_SWIZZLE_128B, 16, true>(g, st);
+        }
+        if (stages == 3) {
+            if (K % 64u) return TMAP_ERR_UNSUPPORTED;
+            if (swa & 4u) return launch_gemm_ring5<TMAP_SWIZZLE_128B_K256, true>(g, st);
+            return launch_gemm_ring5<TMAP_SWIZZLE_128B, true>(g, st);
+        }
+        return TMAP_ERR_UNSUPPORTED;
+    }
     if (bka == 64) {
         if (stages == 2) return launch_gemm<64, 2>(g, swa, mfma, st);
         if (stages == 3) {
@@ -921,7 +963,18 @@ extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C,
     }
 }
 
+extern "C" tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
+                                    uint32_t K, uint32_t ldc, uint32_t stages, uint32_t group_m, uint32_t xcd,
+                                    uint32_t mfma, void* stream) {
+    return gemm_run(A, B, d_C, M, N, K, ldc, stages, group_m, xcd, mfma, false, stream);
+}
+
 extern "C" tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N, uint32_t K,
                                  uint32_t ldc, uint32_t stages, void* stream) {
-    return gemm_bf16_ex(A, B, d_C, M, N, K, ldc, stages, 0u, 1u, 0u, stream);
+    return gemm_run(A, B, d_C, M, N, K, ldc, stages, 0u, 1u, 0u, false, stream);
+}
+
+extern "C" tmap_status gemm_bf16_f32(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
+                                     uint32_t K, uint32_t ldc, uint32_t stages, void* stream) {
+    return gemm_run(A, B, d_C, M, N, K, ldc, stages, 0u, 1u, 0u, true, stream);
 }

@@ -334,6 +334,16 @@ tmap_status gemm_bf16_ex(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M
                          uint32_t K, uint32_t ldc, uint32_t stages, uint32_t group_m, uint32_t xcd,
                          uint32_t mfma, void* stream);
 
+/* gemm_bf16 with C written as fp32: the accumulators as the mainloop leaves
+ * them, before any rounding to bf16, so that the mainloop's own accuracy can
+ * be checked.  d_C is M x N row-major fp32, leading dimension ldc >= N
+ * elements, 4-byte aligned (16-byte stores where C and ldc allow them,
+ * element stores otherwise).  Maps with box {64, 256} only (the 64-deep K
+ * step, 16x16x32 MFMAs), stages 2 or 3 as in gemm_bf16; other maps or
+ * stages return ERR_UNSUPPORTED, and errors are otherwise as gemm_bf16. */
+tmap_status gemm_bf16_f32(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
+                          uint32_t K, uint32_t ldc, uint32_t stages, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -260,3 +260,106 @@ def test_c_leading_dimension(offset, ldc):
     check_close(C[:, :N], ref)
     assert (C[:, N:] == 0x7FFF).all()
     assert (out[:offset] == 0x7FFF).all() and (out[offset + M * ldc:] == 0x7FFF).all()
+
+
+# ---- fp32 C: the accumulators before the bf16 rounding ----------------------
+
+def run_gemm_f32(A_bits, Bt_bits, M, N, K, stages, k256=True, ldc=None, offset=0):
+    """gemm_bf16_f32 on the 64-deep K step; returns C (M, N) as float32 and
+    the whole output buffer (for the untouched-padding check)."""
+    ld = (K + 7) // 8 * 8
+    ldc = ldc or N
+    Ap = np.zeros((M, ld), dtype=np.uint16)
+    Ap[:, :K] = A_bits
+    Bp = np.zeros((N, ld), dtype=np.uint16)
+    Bp[:, :K] = Bt_bits
+    Ad = torch.from_numpy(Ap.view(np.int16)).cuda()
+    Bd = torch.from_numpy(Bp.view(np.int16)).cuda()
+    buf = torch.full((offset + M * ldc,), float("nan"), dtype=torch.float32, device="cuda")
+    sw = "128b_k256" if k256 else "128b"
+    mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (ld * 2,), (64, 256), None, sw)
+    mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (ld * 2,), (64, 256), None, sw)
+    att.gemm_bf16_f32(mA, mB, buf.data_ptr() + 4 * offset, M, N, K, ldc, stages, stream())
+    torch.cuda.synchronize()
+    full = buf.cpu().numpy()
+    C = full[offset:].reshape(M, ldc)[:, :N]
+    return C, full
+
+
+def check_f32(got, ref):
+    """The accumulator itself: 2e-2 absolute, as stated for the GEMM."""
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.isfinite(got).all()
+    assert err.max() <= 2e-2, f"worst {err.max()}"
+
+
+@pytest.mark.parametrize("stages", [2, 3])
+def test_f32_identity_exact(stages):
+    """A = I: the fp32 C equals B exactly."""
+    K = N = M = 512
+    eye = np.zeros((M, K), dtype=np.uint16)
+    eye[np.arange(M), np.arange(K)] = 0x3F80
+    Bt = synthgen.normal_bf16_bits(61, (N, K))
+    C, _ = run_gemm_f32(eye, Bt, M, N, K, stages)
+    np.testing.assert_array_equal(C, bf16_to_f64(Bt.T).astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K,stages", [(512, 512, 512, 2), (512, 512, 512, 3), (300, 270, 448, 3),
+                                          (257, 513, 200, 2), (33, 1000, 64, 3), (700, 17, 1030, 2)])
+def test_f32_against_oracle_full(M, N, K, stages):
+    """Every output of ragged shapes (partial M / N tiles, a K tail with two
+    stages) within 2e-2 of the fp64 oracle."""
+    say("gemm f32", M, N, K, stages)
+    A = synthgen.normal_bf16_bits(62, (M, K))
+    Bt = synthgen.normal_bf16_bits(63, (N, K))
+    C, _ = run_gemm_f32(A, Bt, M, N, K, stages)
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ref = oracle.gemm_bf16_sample(A, Bt, K, rows.reshape(-1), cols.reshape(-1)).reshape(M, N)
+    check_f32(C, ref)
+
+
+@pytest.mark.parametrize("stages", [2, 3])
+def test_f32_8192_sampled(stages):
+    """The full-size product, 4096 sampled accumulators within 2e-2."""
+    ex = W.GEMM_8192
+    M, N, K = ex["M"], ex["N"], ex["K"]
+    say("gemm f32 8192^3", stages)
+    A = synthgen.normal_bf16_bits(ex["seed"] * 1000 + 1, (M, K))
+    Bt = synthgen.normal_bf16_bits(ex["seed"] * 1000 + 2, (N, K))
+    C, _ = run_gemm_f32(A, Bt, M, N, K, stages)
+    rows, cols = synthgen.sample_pairs(ex["seed"] * 1000 + 3, ex["nsample"], M, N)
+    ref = oracle.gemm_bf16_sample(A, Bt, K, rows, cols)
+    check_f32(C[rows, cols], ref)
+    assert np.isfinite(C).all()
+
+
+@pytest.mark.parametrize("offset,ldc", [(0, 264), (1, 264), (3, 259)])
+def test_f32_c_leading_dimension(offset, ldc):
+    """C at any 4-byte offset and any ldc >= N: element stores where 16-byte
+    ones do not fit; the padding past N is never written."""
+    M, N, K = 300, 250, 128
+    A = synthgen.normal_bf16_bits(64, (M, K))
+    Bt = synthgen.normal_bf16_bits(65, (N, K))
+    C, full = run_gemm_f32(A, Bt, M, N, K, 3, ldc=ldc, offset=offset)
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ref = oracle.gemm_bf16_sample(A, Bt, K, rows.reshape(-1), cols.reshape(-1)).reshape(M, N)
+    check_f32(C, ref)
+    assert np.isnan(full[:offset]).all()
+    assert np.isnan(full[offset:].reshape(M, ldc)[:, N:]).all()
+
+
+def test_f32_rejects_what_it_does_not_serve():
+    """The 32-deep K step and a misaligned C are refused before any launch."""
+    A = torch.zeros((256, 64), dtype=torch.int16, device="cuda")
+    C = torch.zeros(256 * 256 + 1, dtype=torch.float32, device="cuda")
+    m64 = att.tmap_encode("bf16", 2, A.data_ptr(), (64, 256), (128,), (64, 256), None, "128b")
+    m32 = att.tmap_encode("bf16", 2, A.data_ptr(), (64, 256), (128,), (32, 256), None, "64b")
+    with pytest.raises(att.TmapError):
+        att.gemm_bf16_f32(m32, m32, C.data_ptr(), 256, 256, 64, 256, 2, stream())
+    with pytest.raises(att.TmapError):
+        att.gemm_bf16_f32(m64, m64, C.data_ptr() + 2, 256, 256, 64, 256, 2, stream())
+    with pytest.raises(att.TmapError):
+        att.gemm_bf16_f32(m64, m64, C.data_ptr(), 256, 256, 64, 256, 4, stream())
+    att.gemm_bf16_f32(m64, m64, C.data_ptr(), 256, 256, 64, 256, 3, stream())
+    torch.cuda.synchronize()
+    assert float(C[:256 * 256].abs().max()) == 0.0
