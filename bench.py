@@ -226,12 +226,14 @@ def run_gemm_raster(att, torch, stream, reps: int, rounds: int = 3):
 
 
 def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int = 10, vendor: bool = False,
-             rounds: int = 3):
+             rounds: int = 3, c_f32: bool = False):
     """bf16 GEMM mainloop, M = N = K = 8192, A row-major, B column-major,
     N(0,1) operands; 2*M*N*K flop per launch.  Each variant is timed in
     `rounds` interleaved rounds of `reps` launches (median reported), after
     `warmup` launches so that clocks have settled under sustained MFMA load.
-    With `vendor`, torch's A @ B^T on the same operands joins the rounds."""
+    With `vendor`, torch's A @ B^T on the same operands joins the rounds.
+    With `c_f32`, C is written as the fp32 accumulators (gemm_bf16_f32, no
+    LDS staging of C), for counters of the mainloop alone."""
     from synthgen import workloads as W
 
     ex = W.GEMM_8192
@@ -239,13 +241,18 @@ def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int 
     g = torch.Generator(device="cuda").manual_seed(ex["seed"])
     Ad = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
     Bd = torch.randn(N, K, generator=g, device="cuda").to(torch.bfloat16)
-    Cd = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Cd = torch.empty(M, N, dtype=torch.float32 if c_f32 else torch.bfloat16, device="cuda")
     fns = {}
     keep = []
     for bk, sw, stages, mi in variants:
         mA = att.tmap_encode("bf16", 2, Ad.data_ptr(), (K, M), (K * 2,), (bk, 256), None, sw)
         mB = att.tmap_encode("bf16", 2, Bd.data_ptr(), (K, N), (K * 2,), (bk, 256), None, sw)
         keep.append((mA, mB))
+        if c_f32:
+            fns[f"gemm_bf16_f32_8192_bk{bk}_{sw}_s{stages}"] = (
+                lambda mA=mA, mB=mB, stages=stages: att.gemm_bf16_f32(mA, mB, Cd.data_ptr(), M, N, K, N, stages,
+                                                                      stream))
+            continue
         fns[f"gemm_bf16_8192_bk{bk}_{sw}_s{stages}_mfma{mi}"] = (
             lambda mA=mA, mB=mB, stages=stages, mi=mi: att.gemm_bf16_ex(mA, mB, Cd.data_ptr(), M, N, K, N, stages,
                                                                         0, 1, stream, mi))
@@ -325,6 +332,8 @@ def main():
                          "rasterisation; lds-probe: run the LDS bank probe layouts (profiling runs)")
     ap.add_argument("--gemm-variant", default="all",
                     help="bk,stages[,k256][,mfma] e.g. 32,4,k256 or 64,2,k256,32 (with --only gemm)")
+    ap.add_argument("--gemm-c-f32", action="store_true",
+                    help="with --only gemm: write C as the fp32 accumulators (gemm_bf16_f32; 64-deep K step)")
     ap.add_argument("--ref-copy", action="store_true",
                     help="also time a plain device-to-device copy of the same bytes")
     ap.add_argument("--ceiling", action="store_true", help="time the HBM ceiling too (the default)")
@@ -371,11 +380,15 @@ def main():
             mi = [int(x) for x in rest if x.isdigit()]
             mi = mi[0] if mi else (16 if bk == 64 else 32)
             variants = ((bk, ("128b" if bk == 64 else "64b") + ("_k256" if k256 else ""), st, mi),)
-        res = run_gemm(att, torch, stream, args.steps, variants, vendor=True)
+        if args.gemm_c_f32:
+            variants = tuple(v for v in variants if v[0] == 64 and v[3] == 16)
+        res = run_gemm(att, torch, stream, args.steps, variants, vendor=not args.gemm_c_f32,
+                       c_f32=args.gemm_c_f32)
         best = res[res["gemm_best"]]
+        workload = "bf16 GEMM M=N=K=8192" + (", fp32 C" if args.gemm_c_f32 else "")
         print(json.dumps({"metric": "bf16 GEMM 8192^3 TFLOP/s", "value": best["TFLOPs"], "unit": "TFLOP/s",
                           "n_gpus": 1, "steps": args.steps, "higher_is_better": True, "dtype": "bf16",
-                          "data": "synthetic", "config": {"workload": "bf16 GEMM M=N=K=8192"},
+                          "data": "synthetic", "config": {"workload": workload},
                           "roofline": {"bound": "mfma", "achieved": best["TFLOPs"], "peak": 2500.0,
                                        "unit": "TFLOP/s", "frac": round(best["TFLOPs"] / 2500.0, 4),
                                        "traffic": None},
