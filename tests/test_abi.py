@@ -6,7 +6,6 @@ import glob
 import os
 import re
 
-import numpy as np
 import pytest
 
 import async_tensor_tile_amd as att

@@ -6,7 +6,6 @@ a dropped term, a wrong sign or index, or a transposed operand fails here.
 Page keys: [MLC] Modern GPU Programming for MLSys (zh), chapter "TMA";
 [H200] blog.coolgpu.cn "H200 // TMA" feature card; [HPC] gpu-hpc-book ch. 08.
 """
-import itertools
 import math
 
 import numpy as np
