@@ -30,25 +30,38 @@ KERNEL_SOURCES = ("async_tensor_tile_amd/csrc/kernel_copy.hip", "include/att/til
                   "include/att/tmap_impl.hpp")
 
 
-def kernel_source_hash() -> str:
+GEMM_COUNTERS_FILE = os.path.join(PROFILE_DIR, "gemm_bf16_8192_counters.json")
+GEMM_SOURCES = ("async_tensor_tile_amd/csrc/kernel_gemm.hip", "include/att/tile_device.hpp",
+                "include/att/tmap_impl.hpp")
+
+
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def committed_counters():
-    """HBM traffic and LDS bank conflicts measured by rocprofv3 for this exact
-    kernel source; None once the kernel has changed since."""
+def committed_counters(path=COUNTERS_FILE, sources=KERNEL_SOURCES):
+    """HBM traffic (and, for the copy, LDS bank conflicts) measured by
+    rocprofv3 for this exact kernel source; None once the kernel has changed
+    since."""
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(path) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_sha") != kernel_source_hash():
+    if c.get("kernel_source_sha") != kernel_source_hash(sources):
         return None
     return c
+
+
+def gemm_traffic():
+    """HBM bytes per launch of the default GEMM (FETCH_SIZE and WRITE_SIZE,
+    calibrated like the copy's), or None once its sources have changed."""
+    c = committed_counters(GEMM_COUNTERS_FILE, GEMM_SOURCES)
+    return c.get("hbm_bytes_per_launch") if c else None
 
 
 def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 8):
@@ -170,7 +183,7 @@ def run_extra(att, torch, stream, reps: int):
     g = run_gemm(att, torch, stream, max(3, reps // 2), variants=(GEMM_DEFAULT,), vendor=True)
     best = g[g["gemm_best"]]
     best["roofline"] = {"bound": "mfma", "achieved": best["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(best["TFLOPs"] / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                        "frac": round(best["TFLOPs"] / BF16_PEAK_TFLOPS, 4), "traffic": gemm_traffic()}
     out.update(g)
     return out
 
@@ -391,7 +404,8 @@ def main():
                           "data": "synthetic", "config": {"workload": workload},
                           "roofline": {"bound": "mfma", "achieved": best["TFLOPs"], "peak": 2500.0,
                                        "unit": "TFLOP/s", "frac": round(best["TFLOPs"] / 2500.0, 4),
-                                       "traffic": None},
+                                       "traffic": gemm_traffic() if (variants == (GEMM_DEFAULT,)
+                                                                     and not args.gemm_c_f32) else None},
                           "detail": res}), flush=True)
         return
     ex = W.COPY_8192
