@@ -167,6 +167,34 @@ __global__ __launch_bounds__(64) void k_lds_bank_probe(int32_t layout, uint32_t 
     for (uint32_t i = lane; i < 256; i += 64) reinterpret_cast<u32x4*>(grid)[i] = u32x4{i, i, i, i};
     __syncthreads();
     uint32_t sink = 0;
+    if (layout >= 4) {
+        // The GEMM epilogue's C staging into 128-byte-row box images of the
+        // C map: layout 4 (128B_K256) and 6 (128B) write as the epilogue's
+        // first ds_write_b64 does (lane l: row l % 16, four bf16 columns at
+        // 4 * (l / 16)); layout 5 reads as its first ds_read_b128 does
+        // (lane l: row l / 8, logical chunk l % 8) under 128B_K256.
+        const uint32_t sw = layout == 6 ? TMAP_SWIZZLE_128B : TMAP_SWIZZLE_128B_K256;
+        uint32_t a;
+        if (layout == 5) {
+            a = swz_chunk(lane, sw) * 16u;
+        } else {
+            const uint32_t row = lane & 15u, col = (lane >> 4) * 4u;
+            a = (swz_chunk(row * 8u + (col >> 3), sw) << 4) + (col & 7u) * 2u;
+        }
+        const uint32_t la = lds_addr_of(grid) + a;
+        for (uint32_t it = 0; it < iters; ++it) {
+            if (layout == 5) {
+                const u32x4 v = lds_read16(la);
+                wait_lgkm0();
+                sink ^= v.x;
+            } else {
+                asm volatile("ds_write_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(la), "v"(uint2{it, lane}) : "memory");
+            }
+        }
+        hist[lane] = (int32_t)a;
+        if (sink == 0xFFFFFFFFu) hist[64] = -1;
+        return;
+    }
     if (layout >= 2) {
         // One MFMA 32x32x16 operand fragment from a 32-row x 128-byte box:
         // lane l reads row l % 32, logical chunk l / 32, at the physical
@@ -314,7 +342,7 @@ extern "C" tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, 
 
 extern "C" tmap_status lds_bank_probe(int32_t layout, uint32_t iters, int32_t* d_hist, void* stream) {
     if (!d_hist) return TMAP_ERR_NULL;
-    if (layout < 0 || layout > 3) return TMAP_ERR_UNSUPPORTED;
+    if (layout < 0 || layout > 6) return TMAP_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(k_lds_bank_probe, dim3(1), dim3(64), 0, as_stream(stream), layout, iters, d_hist);
     return check_launch("lds_bank_probe");
 }

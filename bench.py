@@ -371,13 +371,14 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     if args.only == "lds-probe":
         # one dispatch per layout: the pages' grouped / 256-byte-stride sector
-        # reads (0, 1) and an MFMA 32x32 operand fragment under 128B (2) and
-        # 128B_K256 (3), each read 1000 times for the LDS counters
+        # reads (0, 1), an MFMA 32x32 operand fragment under 128B (2) and
+        # 128B_K256 (3), and the GEMM epilogue's C staging writes (4: 128B_K256,
+        # 6: 128B) and reads (5), each repeated 1000 times for the LDS counters
         h = torch.zeros(9 * 16 * 8, dtype=torch.int32, device="cuda")
-        for layout in range(4):
+        for layout in range(7):
             att.lds_bank_probe(layout, 1000, h.data_ptr(), stream)
         torch.cuda.synchronize()
-        print(json.dumps({"lds_probe_layouts": 4, "iters": 1000}), flush=True)
+        print(json.dumps({"lds_probe_layouts": 7, "iters": 1000}), flush=True)
         return
     if args.only == "gemm-raster":
         print(json.dumps({"gemm_raster": run_gemm_raster(att, torch, stream, args.steps),

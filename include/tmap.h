@@ -285,6 +285,11 @@ tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, uint32_t nt
  * 32-row x 128-byte box (lane l: row l % 32, logical chunk l / 32) under
  * TMAP_SWIZZLE_128B (2) or TMAP_SWIZZLE_128B_K256 (3), `iters` times, and
  * write each lane's physical LDS byte offset to d_hist[l] (64 entries).
+ * Layouts 4 to 6 replay the GEMM epilogue's C staging in a 128-byte-row box
+ * image: 4 and 6 its 8-byte writes (lane l: row l % 16, four bf16 columns
+ * from 4 * (l / 16)) under TMAP_SWIZZLE_128B_K256 (4) or TMAP_SWIZZLE_128B
+ * (6), 5 its 16-byte reads (lane l: row l / 8, logical chunk l % 8) under
+ * TMAP_SWIZZLE_128B_K256; d_hist[l] as for layouts 2 and 3.
  * Errors: NULL, UNSUPPORTED (layout), HIP. */
 tmap_status lds_bank_probe(int32_t layout, uint32_t iters, int32_t* d_hist, void* stream);
 

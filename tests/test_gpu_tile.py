@@ -114,6 +114,21 @@ def test_bank_probe_mfma_fragment_addresses(layout, mode):
     assert got.tolist() == want
 
 
+@pytest.mark.parametrize("layout,mode", [(4, "128b_k256"), (5, "128b_k256"), (6, "128b")])
+def test_bank_probe_c_staging_addresses(layout, mode):
+    """The GEMM epilogue's C staging addresses replayed by the probe equal the
+    oracle's swizzle: 8-byte writes at (row l % 16, column 4 (l / 16)) and
+    16-byte reads at (row l / 8, chunk l % 8) of a 128-byte-row image."""
+    h = empty_dev(65 * 4, 0)
+    att.lds_bank_probe(layout, 4, h, stream())
+    got = to_host(h).view(np.int32)[:64]
+    if layout == 5:
+        want = [oracle.swizzle((l // 8) * 128 + (l % 8) * 16, mode) for l in range(64)]
+    else:
+        want = [oracle.swizzle((l % 16) * 128 + (l // 16) * 8, mode) for l in range(64)]
+    assert got.tolist() == want
+
+
 def test_txbar_4096_bytes(table):
     """[MLC] waiting for a TMA load: two 2048-byte tiles complete one phase
     with expect_tx(4096); states replayed on the oracle barrier model."""
