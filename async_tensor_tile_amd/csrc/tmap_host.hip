@@ -150,16 +150,21 @@ extern "C" tmap_status tmap_encode_im2col(tmap_t* out, int32_t dtype, uint32_t r
     uint64_t npos[3] = {1, 1, 1};
     // the linear window index (image most significant) must fit signed
     // 64-bit arithmetic
-    unsigned __int128 total = gdim[rank - 1];
     for (uint32_t sd = 0; sd < S; ++sd) {
         if (lower[sd] < -32768 || lower[sd] > 32767 || upper[sd] < -32768 || upper[sd] > 32767) return TMAP_ERR_BOX;
         const int64_t lo = lower[sd];
         const int64_t hi = (int64_t)gdim[sd + 1] - 1 + (int64_t)upper[sd];
         if (hi < lo) return TMAP_ERR_BOX;
         npos[sd] = (uint64_t)((hi - lo) / (int64_t)esv[sd + 1] + 1);
-        total *= npos[sd];
     }
+    // checked after every factor (each below 2^34), so the product never
+    // wraps the 128-bit counter
+    unsigned __int128 total = gdim[rank - 1];
     if (total > ((unsigned __int128)1 << 62)) return TMAP_ERR_DIM;
+    for (uint32_t sd = 0; sd < S; ++sd) {
+        total *= npos[sd];
+        if (total > ((unsigned __int128)1 << 62)) return TMAP_ERR_DIM;
+    }
     const uint32_t row_bytes = channels * (uint32_t)es;
     if (swizzle != TMAP_SWIZZLE_NONE && row_bytes != (16u << (swizzle & 3))) return TMAP_ERR_SWIZZLE_WIDTH;
     if (oob == TMAP_OOB_NAN && !is_float(dtype)) return TMAP_ERR_OOB_FILL_DTYPE;

@@ -178,7 +178,9 @@ const char* tmap_last_error(void);
  * multiple of 16 (equal to the swizzle span when swizzled),
  * pixels_per_column 1..1024, corners in [-32768, 32767] with a non-empty
  * grid, estride 1 on C and N and 1..8 on spatial dimensions (NULL = all 1),
- * at most 2^62 windows in total.  Errors as tmap_encode (ERR_BOX for the
+ * at most 2^62 windows in total (a limit of this library: a window is
+ * located through a signed 64-bit linear index; the pages set no bound).
+ * Errors as tmap_encode (ERR_BOX for the
  * pixel / channel / corner limits, ERR_DIM for the window count).  The
  * result is a tmap_t usable only with tile_load_im2col (tiled entry points
  * return ERR_UNSUPPORTED for it); tmap_query reports lds_extent =

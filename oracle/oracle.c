@@ -16,11 +16,18 @@
  *   orc_validate        pinned by [H200] section 03's constraint table.
  *   orc_swizzle 128B    pinned by [MLC] "TMA writes swizzled layout" and
  *                       "3D TMA for several swizzle atoms" worked examples.
- *   orc_swizzle 32B/64B parity unpinned: the pages only say the narrower
- *                       modes exist ([MLC] "grouping requirement" closing
- *                       paragraph); pinned by invariants only.
- *   orc_swizzle *_K256  parity unpinned: not on the pages (a key taken one
- *                       address bit higher); pinned by invariants only.
+ *   orc_swizzle 32B/64B the pages only name the narrower modes ([MLC]
+ *                       "grouping requirement" closing paragraph); the key
+ *                       is read as the 128-byte unit index, as in that
+ *                       section's 256-byte-row formula.  Pinned by that
+ *                       section's bank-sector criterion (one 16-byte column
+ *                       of an 8-row atom hits 8 distinct sectors; the
+ *                       row-index key fails it), the shared key of the rows
+ *                       of one 128-byte unit, and the key sequences.
+ *   orc_swizzle *_K256  not on the pages (this library's gfx950 modes: the
+ *                       key one address bit higher); pinned relative to the
+ *                       base modes (key of row r = base key of row r / 2)
+ *                       and by 16 distinct sectors of a 64-bank model.
  *   orc_load/store      pinned against an independent NumPy pad-and-slice
  *                       formulation and the worked examples above.
  *   orc_reduce_add      pinned by closed forms (integer wrap, IEEE sums).
@@ -200,6 +207,16 @@ static int64_t floor_div(int64_t a, int64_t b)
     return q;
 }
 
+/* The same floor division on 128-bit integers: a window's linear index is a
+ * mixed-radix number whose digits may each be close to 2^32, so it is kept
+ * exact at any tensor size. */
+static __int128 floor_div128(__int128 a, __int128 b)
+{
+    __int128 q = a / b;
+    if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+    return q;
+}
+
 static int64_t im2col_positions(const orc_im2col* m, int s)
 {
     int64_t lo = m->lower[s];
@@ -229,15 +246,11 @@ int orc_im2col_validate(const orc_im2col* m)
     if (t->estride[0] != 1 || t->estride[t->rank - 1] != 1) return ORC_ERR_ESTRIDE;
     for (int d = 1; d < t->rank - 1; ++d)
         if (t->estride[d] < 1 || t->estride[d] > 8) return ORC_ERR_ESTRIDE;
-    double windows = (double)t->dim[t->rank - 1];
     for (int s = 0; s < t->rank - 2; ++s) {
         if (m->lower[s] < -32768 || m->lower[s] > 32767) return ORC_ERR_BOX;
         if (m->upper[s] < -32768 || m->upper[s] > 32767) return ORC_ERR_BOX;
         if (im2col_positions(m, s) < 1) return ORC_ERR_BOX;
-        windows *= (double)im2col_positions(m, s);
     }
-    /* a limit of this library: every window has a signed 64-bit linear index */
-    if (windows > 4611686018427387904.0) return ORC_ERR_DIM;   /* 2^62 */
     uint32_t row_bytes = m->channels * (uint32_t)es;
     if (t->swizzle != ORC_SW_NONE && row_bytes != (16u << (t->swizzle & 3))) return ORC_ERR_SWIZZLE_WIDTH;
     if (t->fill == ORC_FILL_NAN && !is_float(t->dtype)) return ORC_ERR_OOB_FILL_DTYPE;
@@ -261,20 +274,20 @@ void orc_im2col_load(const orc_im2col* m, const uint8_t* gmem, const int32_t* co
     int64_t npos[3];
     for (int s = 0; s < S; ++s) npos[s] = im2col_positions(m, s);
     /* linear index of the start: image index is the most significant digit */
-    int64_t L0 = coords[t->rank - 1];
+    __int128 L0 = coords[t->rank - 1];
     for (int s = S - 1; s >= 0; --s)
         L0 = L0 * npos[s] + floor_div((int64_t)coords[s + 1] - m->lower[s], (int64_t)t->estride[s + 1]);
     for (uint32_t p = 0; p < m->pixels; ++p) {
-        int64_t L = L0 + (int64_t)p;
+        __int128 L = L0 + (__int128)p;
         int64_t x[3];
         for (int s = 0; s < S; ++s) {
-            int64_t q = floor_div(L, npos[s]);
-            int64_t digit = L - q * npos[s];
+            __int128 q = floor_div128(L, npos[s]);
+            int64_t digit = (int64_t)(L - q * npos[s]);
             x[s] = (int64_t)m->lower[s] + digit * (int64_t)t->estride[s + 1] + (int64_t)offsets[s];
             L = q;
         }
-        int64_t img = L;
-        int inb_pix = img >= 0 && (uint64_t)img < t->dim[t->rank - 1];
+        __int128 img = L;
+        int inb_pix = img >= 0 && img < (__int128)t->dim[t->rank - 1];
         uint64_t pix_off = inb_pix ? (uint64_t)img * t->stride[t->rank - 1] : 0;
         for (int s = 0; s < S; ++s) {
             if (x[s] < 0 || (uint64_t)x[s] >= t->dim[s + 1]) inb_pix = 0;

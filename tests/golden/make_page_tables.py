@@ -67,7 +67,12 @@ def txbar_4096():
             "# load: two operand tiles of 2048 bytes each share one barrier initialised with an",
             "# expected arrival count of 1; arrive.expect_tx(4096) leaves arrival count 0 and",
             "# 4096 pending bytes; when both copies are done the pending bytes are 0 and the",
-            "# phase completes, so a wait on phase 0 succeeds.",
+            "# phase completes, so a wait on phase 0 succeeds.  The page prints the counts at",
+            "# completion as arrival count 0, pending bytes 0.",
+            "# Reading (not printed on the page): the operation that completes a phase flips the",
+            "# phase and re-arms the arrival count to the count given at init, ready for the next",
+            "# phase, as a hardware barrier phase does.  So the last row records the state after",
+            "# that re-arm: arrivals_left 1 (the page's 0, re-armed), pending 0, phase 1.",
             "# Table: op argument -> arrivals_left pending_bytes phase try_wait(0)",
             "init 1 -> 1 0 0 0",
             "arrive_expect_tx 4096 -> 0 4096 0 0",

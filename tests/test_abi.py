@@ -156,10 +156,14 @@ IM2COL_CASES = [
     dict(dims=(8, 11, 2), strides=(32, 352), lower=(-2,), upper=(1,), estride=(1, 3, 1)),
     dict(dims=(8, 5, 5, 5, 2), strides=(32, 160, 800, 4000), lower=(0, -1, 0), upper=(0, 0, -4),
          estride=(1, 1, 2, 1, 1)),
-    dict(dims=(8, 1 << 32, 1 << 32, 1 << 32, 4), strides=(32, 1 << 35, 1 << 36, 1 << 37), lower=(0, 0, 0),
-         upper=(0, 0, 0), estride=(1, 1, 1, 1, 1)),
     dict(dims=(0, 11, 9, 2)), dict(base=BASE + 8),
 ]
+
+# More windows than a signed 64-bit index counts: accepted by the oracle (the
+# pages set no bound), rejected by the library, whose kernels decode a
+# window's position from a 64-bit linear index.
+HUGE_WINDOWS = dict(dims=(8, 1 << 32, 1 << 32, 1 << 32, 4), strides=(32, 1 << 35, 1 << 36, 1 << 37),
+                    lower=(0, 0, 0), upper=(0, 0, 0), estride=(1, 1, 1, 1, 1))
 
 
 def _im2col_args(**kw):
@@ -188,6 +192,24 @@ def test_im2col_encode_agrees_with_oracle(case):
         q = att.tmap_query(m)
         assert q["box_bytes"] == om.box_bytes()
         assert q["lds_extent"] == [a["channels"], a["pixels"], 1, 1, 1]
+
+
+def test_im2col_window_count_limit_of_the_library():
+    """The library's own limit (at most 2^62 windows, one 64-bit linear
+    index each); the oracle validates the same map."""
+    a = _im2col_args(**HUGE_WINDOWS)
+    om = oracle.Im2colMap(a["dtype"], a["dims"], a["strides"], a["lower"], a["upper"], a["channels"],
+                          a["pixels"], a["estride"], a["swizzle"], a["fill"], base_addr=a["base"])
+    assert om.validate() == "OK"
+    with pytest.raises(att.TmapError) as ei:
+        att.tmap_encode_im2col(a["dtype"], len(a["dims"]), a["base"], a["dims"], a["strides"], a["lower"],
+                               a["upper"], a["channels"], a["pixels"], a["estride"], a["swizzle"], a["fill"])
+    assert ei.value.name == "ERR_DIM"
+    # 2^62 windows exactly are accepted: 2^20 x 2^20 x 2^20 positions x 4 images
+    ok = dict(HUGE_WINDOWS, dims=(8, 1 << 20, 1 << 20, 1 << 20, 4), strides=(32, 1 << 25, 1 << 30, 1 << 35))
+    b = _im2col_args(**ok)
+    att.tmap_encode_im2col(b["dtype"], len(b["dims"]), b["base"], b["dims"], b["strides"], b["lower"], b["upper"],
+                           b["channels"], b["pixels"], b["estride"], b["swizzle"], b["fill"])
 
 
 def test_im2col_map_rejected_by_tiled_entry_points():

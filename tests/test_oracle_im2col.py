@@ -186,8 +186,9 @@ def _im(**kw):
     (dict(dtype="i32", fill="nan"), "ERR_OOB_FILL_DTYPE"),
     (dict(channels=256, pixels=1024), "ERR_LDS_CAPACITY"),
     (dict(strides=(24, 352, 3168)), "ERR_STRIDE"),
+    # the pages set no bound on the number of windows: 2^98 windows validate
     (dict(dims=(8, 1 << 32, 1 << 32, 1 << 32, 4), strides=(32, 1 << 35, 1 << 36, 1 << 37), lower=(0, 0, 0),
-          upper=(0, 0, 0), estride=(1, 1, 1, 1, 1)), "ERR_DIM"),
+          upper=(0, 0, 0), estride=(1, 1, 1, 1, 1)), "OK"),
 ])
 def test_im2col_validate(kw, status):
     assert _im(**kw).validate() == status

@@ -194,6 +194,90 @@ def test_swizzle_invariants_all_modes():
             assert keys[:8] == list(range(8))                 # col XOR row
 
 
+def _row_index_key_swizzle(off, mode):
+    """The rejected reading of the narrower modes: XOR key = row % (N/16) on
+    N-byte rows.  Kept here only to show that the pins below reject it."""
+    span = {"32b": 32, "64b": 64, "128b": 128}[mode]
+    nsec = span // 16
+    row, c = off // span, (off % span) // 16
+    return row * span + ((c ^ (row % nsec)) * 16) + off % 16
+
+
+def _narrow_mode_violations(swz, mode):
+    """Ways a swizzle of N-byte rows breaks what [MLC] 'grouping requirement'
+    fixes for the 128-byte mode, carried over to the narrower spans:
+    (a) bank sectors -- eight consecutive rows of one atom reading the same
+        16-byte column must hit eight distinct bank sectors of the pages'
+        model (32 banks x 4 bytes, sector = (address >> 4) % 8), the
+        section's stated purpose of the swizzle;
+    (b) the XOR key is the 128-byte unit index of the address -- the
+        section's 256-byte-row formula, local_col XOR ((2*row + col//8) % 8),
+        keys the two 128-byte halves of one row 2*row and 2*row + 1 -- so the
+        rows that share a 128-byte unit share a key."""
+    span = {"32b": 32, "64b": 64, "128b": 128}[mode]
+    nsec = span // 16
+    bad = []
+    for atom in range(4):
+        for c in range(nsec):
+            sectors = {(swz((8 * atom + r) * span + 16 * c, mode) >> 4) % 8 for r in range(8)}
+            if len(sectors) != 8:
+                bad.append(("sectors", atom, c, len(sectors)))
+    keys = [((swz(r * span, mode) // 16) % nsec) for r in range(32)]
+    for r in range(32):
+        if keys[r] != keys[(r * span // 128) * 128 // span]:
+            bad.append(("unit key", r))
+    return bad
+
+
+def test_swizzle_narrow_modes_pinned_by_bank_criterion():
+    """32B / 64B: the pages print no pattern; the reading (XOR key = 128-byte
+    unit index mod N/16) is pinned by the bank-sector criterion and the
+    address-unit key of [MLC] 'grouping requirement'.  The row-index key
+    (row % (N/16)) fails both, so a planted row-index key fails here."""
+    for mode in ("32b", "64b", "128b"):
+        assert _narrow_mode_violations(oracle.swizzle, mode) == [], mode
+    for mode in ("32b", "64b"):
+        bad = _narrow_mode_violations(_row_index_key_swizzle, mode)
+        assert any(b[0] == "sectors" for b in bad) and any(b[0] == "unit key" for b in bad), mode
+    # the 128-byte mode is the same under both readings (128-byte rows)
+    assert _narrow_mode_violations(_row_index_key_swizzle, "128b") == []
+
+
+def test_swizzle_key_sequences():
+    """The key of each row of an N-byte-row box (the physical sector that
+    logical sector 0 lands in), rows 0..15: the reading written out."""
+    def keys(mode, span, n=16):
+        return [(oracle.swizzle(r * span, mode) // 16) % (span // 16) for r in range(n)]
+    assert keys("128b", 128) == [r % 8 for r in range(16)]            # [MLC]: col XOR (row % 8)
+    assert keys("64b", 64)[:8] == [0, 0, 1, 1, 2, 2, 3, 3]
+    assert keys("64b", 64)[8:] == [0, 0, 1, 1, 2, 2, 3, 3]
+    assert keys("32b", 32)[:8] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert keys("128b_k256", 128) == [r // 2 for r in range(16)]
+    assert keys("64b_k256", 64) == [0, 0, 0, 0, 1, 1, 1, 1, 2, 2, 2, 2, 3, 3, 3, 3]
+    assert keys("32b_k256", 32) == [0] * 8 + [1] * 8
+    # every sector of a row moves by the row's key
+    for mode, span in (("32b", 32), ("64b", 64), ("128b", 128), ("64b_k256", 64)):
+        k = keys(mode, span, 32)
+        for r in range(32):
+            for c in range(span // 16):
+                assert oracle.swizzle(r * span + 16 * c, mode) == r * span + 16 * (c ^ k[r])
+
+
+def test_swizzle_k256_sixteen_sectors():
+    """The _K256 modes exist for a 64-bank LDS (gfx950: one ds_read_b128 wave
+    instruction reads 256 bytes per clock).  Sixteen consecutive rows of one
+    16-byte column must then hit sixteen distinct 16-byte sectors of a
+    256-byte bank line, sector = (address >> 4) % 16; the pages' 8-row modes
+    hit eight sectors twice each on 128-byte rows."""
+    for mode, span in (("128b_k256", 128), ("64b_k256", 64), ("32b_k256", 32)):
+        for atom in range(2):
+            for c in range(span // 16):
+                sectors = {(oracle.swizzle((16 * atom + r) * span + 16 * c, mode) >> 4) % 16 for r in range(16)}
+                assert len(sectors) == 16, (mode, atom, c)
+    sectors = {(oracle.swizzle(r * 128, "128b") >> 4) % 16 for r in range(16)}
+    assert len(sectors) == 8
+
+
 # ------------------------- the pages' worked examples -----------------------
 
 def test_example_2d_sector_table(table):
