@@ -132,10 +132,15 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_group) {
 // The same 16-byte copy with a wave-uniform 64-bit base (SGPRs), a per-lane
 // 32-bit offset and the LDS group address in M0, issued as inline asm so the
 // compiler's LDS alias tracking does not see it: the caller orders it against
-// LDS reads with its own vmcnt waits and barriers (the s_nop covers the M0
-// write hazard).
+// LDS reads with its own vmcnt waits and barriers.
+// The compiler's hazard recogniser does not look inside inline asm, so the
+// asm provides its own wait states: a vector-memory instruction must come at
+// least five wait states after a VALU instruction that wrote one of the
+// SGPRs it reads (here the base, which the compiler may produce with
+// v_readfirstlane), and an LDS-DMA one after the write of M0.  s_nop 4 gives
+// five, whatever the compiler placed just before the asm.
 __device__ __forceinline__ void dma16_sv(uint64_t sbase, uint32_t voff, uint32_t lds_group_addr) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(sbase), "{m0}"(lds_group_addr)
                  : "memory");
@@ -272,6 +277,38 @@ __device__ __forceinline__ void atomic_add_g(gbyte* dst, T v) {
     __hip_atomic_fetch_add((ATT_GLOBAL T*)dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// IEEE addition of a 4- or 8-byte float `bits` into global memory, rounded
+// to nearest even.  The hardware float atomic rounds that way, but an L2
+// adder may treat subnormal operands or results as zero.  That can change
+// the sum only when the added value is zero, not finite, or tiny: for
+// |v| >= 2^(emin + p + 2) (exponent field >= p + 3, p the significand bits)
+// a subnormal other operand is below a quarter ulp of v, so the correctly
+// rounded sum is v either way, and a cancellation cannot end in the
+// subnormal range (both operands are then multiples of 2^(emin + 2)).  Those
+// values take the hardware atomic; the rest a compare-and-swap loop whose
+// sum the VALU forms with subnormals kept.  A NaN result is a quiet NaN
+// whose payload is not fixed (IEEE 754 leaves it open).
+template <typename F, typename U>
+__device__ __forceinline__ void float_add_atomic(gbyte* dst, U bits) {
+    constexpr int MB = sizeof(F) == 4 ? 23 : 52;              // stored significand bits
+    constexpr U EMAX = sizeof(F) == 4 ? 0xFFu : 0x7FFu;        // exponent field of inf / NaN
+    const U e = (bits >> MB) & EMAX;
+    if (e >= (U)(MB + 4) && e < EMAX) {
+        __hip_atomic_fetch_add((ATT_GLOBAL F*)dst, __builtin_bit_cast(F, bits), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    ATT_GLOBAL U* w = (ATT_GLOBAL U*)dst;
+    U old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (true) {
+        const U nw = __builtin_bit_cast(U, __builtin_bit_cast(F, old) + __builtin_bit_cast(F, bits));
+        if (nw == old) return;
+        if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return;
+    }
+}
+
 // Element `bits` (the low esize bytes hold it) added into dst.
 __device__ __forceinline__ void reduce_add_element(uint8_t dtype, gbyte* dst, uint64_t bits) {
     switch (dtype) {
@@ -282,10 +319,10 @@ __device__ __forceinline__ void reduce_add_element(uint8_t dtype, gbyte* dst, ui
         atomic_add_g<uint64_t>(dst, bits);
         break;
     case TMAP_F32:
-        atomic_add_g<float>(dst, __builtin_bit_cast(float, (uint32_t)bits));
+        float_add_atomic<float, uint32_t>(dst, (uint32_t)bits);
         break;
     case TMAP_F64:
-        atomic_add_g<double>(dst, __builtin_bit_cast(double, bits));
+        float_add_atomic<double, uint64_t>(dst, bits);
         break;
     case TMAP_U8: {
         const uint32_t v = (uint32_t)bits & 0xFFu;

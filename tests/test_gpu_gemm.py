@@ -207,6 +207,61 @@ def test_8192_sampled(bk, stages, k256, mfma):
     assert not (C == 0x7FFF).any()
 
 
+# Tile grids (256 x 256 C tiles) for the rasterisation orders: 8 x 4 and
+# 12 x 2 let xcd = 2 give each XCD a 2-D block, 4 x 6 gives 1 x 3 blocks;
+# 2000 x 1000 has partial last tiles on the same 8 x 4 grid; 5 x 3 tiles
+# (15 workgroups) make both XCD-aware orders fall back to plain order.
+RASTER_GRIDS = [(2048, 1024), (3072, 512), (1024, 1536), (2000, 1000), (1280, 768)]
+
+
+@pytest.mark.parametrize("stages", [2, 3])
+@pytest.mark.parametrize("MN", RASTER_GRIDS)
+@pytest.mark.parametrize("group_m", [1, 3, 4, 8])
+@pytest.mark.parametrize("xcd", [0, 1, 2])
+def test_raster_orders_exact(xcd, group_m, MN, stages):
+    """Every rasterisation order writes every C tile, with the right data:
+    A selects one K index per row, so C[m, :] = B[sel[m], :] exactly and a
+    tile that is skipped (left at the sentinel) or taken from the wrong A /
+    B panel fails."""
+    M, N = MN
+    K = 128
+    say("gemm raster", xcd, group_m, M, N, stages)
+    sel = synthgen.rng(66).integers(0, K, M)
+    A = np.zeros((M, K), dtype=np.uint16)
+    A[np.arange(M), sel] = 0x3F80
+    Bt = synthgen.normal_bf16_bits(67, (N, K))
+    C = run_gemm(A, Bt, M, N, K, 64, stages, group_m=group_m, xcd=xcd, k256=True, mfma=16)
+    np.testing.assert_array_equal(C, Bt[:, sel].T)
+
+
+_OPERANDS_8192 = {}
+
+
+def _operands_8192():
+    if not _OPERANDS_8192:
+        ex = W.GEMM_8192
+        M, N, K = ex["M"], ex["N"], ex["K"]
+        _OPERANDS_8192["A"] = synthgen.normal_bf16_bits(ex["seed"] * 1000 + 1, (M, K))
+        _OPERANDS_8192["Bt"] = synthgen.normal_bf16_bits(ex["seed"] * 1000 + 2, (N, K))
+    return _OPERANDS_8192["A"], _OPERANDS_8192["Bt"]
+
+
+@pytest.mark.parametrize("xcd,group_m", [(0, 1), (0, 8), (2, 4), (2, 8)])
+def test_8192_sampled_rasters(xcd, group_m):
+    """The full-size product under the rasterisation orders the benchmark
+    times beside the default: 4096 sampled outputs against the oracle, and
+    every output written."""
+    ex = W.GEMM_8192
+    M, N, K = ex["M"], ex["N"], ex["K"]
+    say("gemm 8192^3 raster", xcd, group_m)
+    A, Bt = _operands_8192()
+    C = run_gemm(A, Bt, M, N, K, 64, 3, group_m=group_m, xcd=xcd, k256=True, mfma=16)
+    rows, cols = synthgen.sample_pairs(ex["seed"] * 1000 + 3, ex["nsample"], M, N)
+    ref = oracle.gemm_bf16_sample(A, Bt, K, rows, cols)
+    check_close(C[rows, cols], ref)
+    assert not (C == 0x7FFF).any()
+
+
 def _random_gemm_case(seed):
     g = synthgen.rng(90000 + seed)
     bk, stages, mfma = [(64, 2, 16), (64, 2, 32), (64, 3, 16), (64, 2, 0), (32, 2, 32), (32, 3, 32),

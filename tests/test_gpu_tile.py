@@ -281,6 +281,70 @@ def test_half_reduce_special_values_exact(dtype, layout):
     np.testing.assert_array_equal(to_host(acc), hw)
 
 
+def _float_class_mix(dtype, n, seed):
+    """n f32 / f64 bit patterns, each drawn from one of thirteen classes
+    picked uniformly: random bits, +0, -0, subnormals, the smallest normal,
+    values around the size below which the library's add leaves the
+    hardware atomic (exponent field p .. p + 4), small and ordinary normals,
+    +inf, -inf, the canonical quiet NaN, NaNs with random payloads (quiet and
+    signalling, either sign), the largest finite value."""
+    ut, ft, mb, ew = {"f32": (np.uint32, np.float32, 23, 8), "f64": (np.uint64, np.float64, 52, 11)}[dtype]
+    emax = (1 << ew) - 1
+    U = np.uint64
+    g = synthgen.rng(seed)
+    cls = g.integers(0, 13, n)
+    sign = g.integers(0, 2, n, dtype=np.uint64) << U(mb + ew)
+    man = g.integers(0, 1 << mb, n, dtype=np.uint64)
+    exp_near = g.integers(mb + 1, mb + 6, n, dtype=np.uint64)
+    exp_small = g.integers(1, 40, n, dtype=np.uint64)
+    raw = g.integers(0, 1 << (mb + ew + 1), n, dtype=np.uint64) if dtype == "f32" else \
+        g.integers(0, np.iinfo(np.uint64).max, n, dtype=np.uint64, endpoint=True)
+    ordinary = g.standard_normal(n).astype(ft).view(ut).astype(np.uint64)
+    one = np.ones(n, dtype=np.uint64)
+    top = U(emax) << U(mb)
+    choices = [raw, np.zeros(n, np.uint64), U(1) << U(mb + ew) | np.zeros(n, np.uint64),
+               sign | np.maximum(man, one), sign | (U(1) << U(mb)), sign | (exp_near << U(mb)) | man,
+               sign | (exp_small << U(mb)) | man, ordinary, top | np.zeros(n, np.uint64),
+               (U(1) << U(mb + ew)) | top, top | (U(1) << U(mb - 1)), sign | top | np.maximum(man, one),
+               sign | (U(emax - 1) << U(mb)) | U((1 << mb) - 1)]
+    out = np.choose(cls, choices)
+    return out.astype(ut)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("layout", ["aligned", "edges"])
+def test_float_reduce_special_values_exact(dtype, layout):
+    """f32 / f64 reduce-add with operands of every class on both sides
+    (subnormals, signed zeros, infinities, NaN payloads, values at the size
+    where the add leaves the hardware atomic), one contribution per element:
+    IEEE addition rounded to nearest even, bit-exact against the oracle; a
+    NaN result must be a NaN (IEEE 754 leaves its payload open)."""
+    es = ESIZE[dtype]
+    L0 = 128 // es
+    dims = (4 * L0 + 5, 24)
+    strides = ((dims[0] * es + 15) // 16 * 16,)
+    box = (L0, 8)
+    ut = np.uint32 if dtype == "f32" else np.uint64
+    foot = strides[0] * dims[1]
+    dst0 = _float_class_mix(dtype, foot // es, 71).view(np.uint8)
+    imgs = _float_class_mix(dtype, 12 * L0 * 8, 72).view(np.uint8)
+    xs = {"aligned": [0, L0, 2 * L0, 3 * L0], "edges": [-3, L0 - 3, 2 * L0 + 1, 3 * L0 + 9]}[layout]
+    coords = np.array([[xs[i % 4], 8 * (i // 4)] for i in range(12)], dtype=np.int32)
+    acc = to_dev(dst0)
+    m = encode(acc, dtype, dims, strides, box)
+    att.tile_reduce_add(m, to_dev(coords), 12, to_dev(imgs), stream())
+    hw = dst0.copy()
+    oracle.Map(dtype, dims, strides, box).reduce_add(hw, coords, imgs)
+    got = to_host(acc).view(ut)
+    want = hw.view(ut)
+    ft = np.float32 if dtype == "f32" else np.float64
+    want_nan = np.isnan(want.view(ft))
+    assert (np.isnan(got.view(ft)) == want_nan).all()
+    np.testing.assert_array_equal(got[~want_nan], want[~want_nan])
+    # the mix really reaches the cases the CAS path serves
+    assert (want.view(ft)[~want_nan] != 0).any() and want_nan.any()
+
+
 # ------------------------------- edge cases ---------------------------------
 
 def test_empty_and_fully_outside():
