@@ -26,7 +26,7 @@ OOB = {"zero": 0, "nan": 1}
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_RANK", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
           5: "ERR_DIM", 6: "ERR_STRIDE", 7: "ERR_BOX", 8: "ERR_ESTRIDE",
           9: "ERR_SWIZZLE_WIDTH", 10: "ERR_OOB_FILL_DTYPE", 11: "ERR_LDS_CAPACITY",
-          12: "ERR_UNSUPPORTED", 13: "ERR_HIP"}
+          12: "ERR_UNSUPPORTED", 13: "ERR_HIP", 14: "ERR_TIMEOUT", 15: "ERR_DEVICE_CHECK"}
 
 
 class NativeLibraryMissing(RuntimeError):
@@ -93,13 +93,16 @@ def lib():
         L.tile_copy.argtypes = [tp, tp, _U32, _V]
         L.tile_copy_ex.argtypes = [tp, tp, _U32, _U32, _U32, _V]
         L.txbar_selftest.argtypes = [tp, _V, _U32, _V, _V, _V]
+        L.txbar_selftest_ex.argtypes = [tp, _V, _U32, _U32, _U32, _V, _V, _V]
+        L.tile_device_status.argtypes = [_V]
         L.lds_bank_probe.argtypes = [_I32, _U32, _V, _V]
         L.hbm_probe.argtypes = [_I32, _V, _V, ctypes.c_uint64, _V]
         L.gemm_bf16.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
         L.gemm_bf16_ex.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _V]
         L.gemm_bf16_f32.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
         for name in ("tmap_encode", "tmap_replace_address", "tmap_query", "tile_load", "tile_store",
-                     "tile_reduce_add", "tile_reduce", "tmap_encode_im2col", "tile_load_im2col", "tile_copy", "tile_copy_ex", "txbar_selftest",
+                     "tile_reduce_add", "tile_reduce", "tmap_encode_im2col", "tile_load_im2col", "tile_copy", "tile_copy_ex",
+                     "txbar_selftest", "txbar_selftest_ex", "tile_device_status",
                      "lds_bank_probe", "hbm_probe", "gemm_bf16", "gemm_bf16_ex", "gemm_bf16_f32"):
             getattr(L, name).restype = _I32
         _lib = L
@@ -224,6 +227,19 @@ def tile_copy_ex(src: tmap_t, dst: tmap_t, stages: int = 2, grid: int = 0, varia
 def txbar_selftest(m: tmap_t, d_coords, ntile: int, d_trace, d_lds_image_out, stream=0) -> None:
     _check(lib().txbar_selftest(ctypes.byref(m), _addr(d_coords), int(ntile), _addr(d_trace),
                                 _addr(d_lds_image_out), _addr(stream)), "txbar_selftest")
+
+
+def txbar_selftest_ex(m: tmap_t, d_coords, ntile: int, extra_bytes: int, max_polls: int, d_trace,
+                      d_lds_image_out, stream=0) -> None:
+    _check(lib().txbar_selftest_ex(ctypes.byref(m), _addr(d_coords), int(ntile), int(extra_bytes), int(max_polls),
+                                   _addr(d_trace), _addr(d_lds_image_out), _addr(stream)), "txbar_selftest_ex")
+
+
+def tile_device_status(stream=0) -> None:
+    """Synchronise `stream` and raise TmapError (ERR_TIMEOUT,
+    ERR_DEVICE_CHECK) if a batch kernel recorded a device-side failure since
+    the last call; the record is cleared."""
+    _check(lib().tile_device_status(_addr(stream)), "tile_device_status")
 
 
 def hbm_probe(kind, d_src, d_dst, nbytes: int, stream=0) -> None:

@@ -20,11 +20,12 @@
 // (16 lanes x 16 bytes per clock); the _K256 modes' 16-row key removes that.
 #include <hip/hip_runtime.h>
 
+#include <cstring>
 #include <type_traits>
 #include <utility>
 
 #include "host_util.hpp"
-#include "att/tile_device.hpp"
+#include "tile.hpp"
 #include "tmap.h"
 
 namespace att {
@@ -50,6 +51,42 @@ struct GemmArgs {
     uint32_t c_staged;       // 1: C written back through Cm (LDS image + tile store)
     TmapImpl Cm;             // C map: dims {N, M}, box {64, 256}, 128B_K256 swizzle
 };
+
+// The C map of the staged epilogue: dims {N, M} with a row stride of
+// ld_bytes, box {64, 256}, bf16, 128B_K256 swizzle, zero fill -- exactly
+// what tmap_encode makes of those arguments (the host compares the two
+// before choosing the staged epilogue).  Built here from constants but the
+// base, stride and dims, so the box store inlined into the epilogue folds
+// its per-map fields instead of keeping them in scalar registers.
+__host__ __device__ __forceinline__ TmapImpl gemm_c_box_map(uint64_t base, uint64_t ld_bytes, uint32_t N,
+                                                           uint32_t M) {
+    TmapImpl t;
+    t.base = base;
+    t.stride[0] = ld_bytes;
+    t.stride[1] = t.stride[2] = t.stride[3] = 0;
+    t.dim[0] = N;
+    t.dim[1] = M;
+    t.dim[2] = t.dim[3] = t.dim[4] = 1;
+    t.L[0] = 64;
+    t.L[1] = 256;
+    t.L[2] = t.L[3] = t.L[4] = 1;
+    t.box_m1[0] = 63;
+    t.box_m1[1] = 255;
+    t.box_m1[2] = t.box_m1[3] = t.box_m1[4] = 0;
+    t.es[0] = t.es[1] = t.es[2] = t.es[3] = t.es[4] = 1;
+    t.rank = 2;
+    t.dtype = TMAP_BF16;
+    t.esize = 2;
+    t.swizzle = TMAP_SWIZZLE_128B_K256;
+    t.oob = TMAP_OOB_ZERO;
+    t.fill_idx = FILL_ZERO;
+    t.cpr = 8;
+    t.box_bytes = 32768;
+    t.magic_cpr = 0x20000000u;      // ceil(2^32 / 8)
+    t.magic_L[0] = 0x01000000u;     // ceil(2^32 / 256)
+    t.magic_L[1] = t.magic_L[2] = 0;
+    return t;
+}
 
 // One iteration of the main loop as a fixed sequence of MFMA slots (see the
 // kernel): which MFMA each slot runs, which fragment read follows it, and the
@@ -190,6 +227,21 @@ constexpr bool waits_consistent() {
 }
 static_assert(waits_consistent<GemmSched<8, 8, 2, 4>>() && waits_consistent<GemmSched<4, 4, 2>>(), "pruned waits");
 
+// The operand ring's copies: dma16_sv with only the one wait state the M0
+// write needs.  dma16_sv's four more (for a VALU write of the base SGPRs
+// just before) sit on the ring's issue path and cost 5 % of the GEMM.  The
+// ring's bases and M0 values come from scalar arithmetic, and its kernels
+// spill no SGPRs (a spill restore is a VALU write, v_readlane); the CPU
+// suite compiles this file to gfx950 assembly and checks both: no
+// SGPR-base DMA of any kernel here has a VALU write of its base or M0 within
+// five wait states on any path, and the ring kernels report no SGPR spills.
+__device__ __forceinline__ void dma16_sv_ring(uint64_t sbase, uint32_t voff, uint32_t lds_group_addr) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "{m0}"(lds_group_addr)
+                 : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_lgkm() {
     static_assert(N >= 0 && N < 16, "lgkmcnt range");
@@ -242,8 +294,8 @@ __device__ __forceinline__ void gemm_block_tile(const GemmArgs& g, uint32_t& tm,
 // Epilogue of a workgroup's 256 x 256 C tile from the accumulators of its
 // four waves (2 x 2 blocks of 128 x 128, NI x NJ tiles of MI x MI each).
 template <int MI, bool CF32, typename AccT, int NI, int NJ>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI][NJ], uint32_t lds0, uint32_t wave,
-                                              uint32_t lane, uint32_t m0, uint32_t n0) {
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI][NJ], uint8_t* smem, uint32_t lds0,
+                                              uint32_t wave, uint32_t lane, uint32_t m0, uint32_t n0) {
     // Epilogue.  The MFMAs take B as their first operand, so accumulator
     // (i, j) holds the transposed MI x MI tile: register 4q + r of lane l is C
     // row i*MI + l%MI of the wave's block and column j*MI + q*8 + (l/MI)*4 + r,
@@ -281,72 +333,62 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI]
         return;
     }
     if (g.c_staged) {
-        // Registers -> LDS -> global, as the pages' epilogue does: the
-        // workgroup's 256 x 256 tile becomes four 256 x 64 box images of the
-        // C map (128-byte rows, 16-row XOR key: the 8-byte writes of rows r
-        // and r+1..r+15 land in distinct bank groups), then every wave writes
-        // boxes back 16 bytes per lane through the tile store, which clips
+        // Registers -> LDS -> global through the tile store, as the pages'
+        // epilogue does ([MLC] "waiting for a TMA store": write the output
+        // tile to shared memory, store it, wait on the store group, then
+        // reuse the buffer).  The 256 x 256 tile is four 256 x 64 boxes of
+        // the C map (128-byte rows, 16-row XOR key: the 8-byte writes of rows
+        // r and r+1..r+15 land in distinct bank groups).  Two LDS stages of
+        // one box each are used twice: in round r the waves of column half
+        // wn write box 2*wn + r (their accumulator columns j*MI with
+        // j in [r*NJ/2, (r+1)*NJ/2)) into stage wn, then every wave stores
+        // its share of both boxes as two store groups; round 1 refills the
+        // stages once those groups no longer read them.  The box store clips
         // at the M / N edges.  The ring is free once every wave has passed
-        // this barrier (all fragment reads completed before the last MFMAs).
+        // the first barrier (all fragment reads completed before the last
+        // MFMAs).
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         typedef __attribute__((address_space(3))) u32x2 lds_u2_t;
+        constexpr uint32_t kStage = 256u * 128u;      // one C box image
+        const TmapImpl cm = gemm_c_box_map(g.Cm.base, g.Cm.stride[0], (uint32_t)g.Cm.dim[0], (uint32_t)g.Cm.dim[1]);
+        const tmap_t& cmap = reinterpret_cast<const tmap_t&>(cm);
+        StoreGroups sg;
+        store_groups_init(sg);
         wg_barrier();
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) {
-                    const uint32_t row = rloc + (uint32_t)i * (uint32_t)MI;
-                    const uint32_t col = cloc + (uint32_t)j * (uint32_t)MI + (uint32_t)q * 8u;
-                    const uint32_t chunk = row * 8u + ((col & 63u) >> 3);
-                    const uint32_t addr = lds0 + (col >> 6) * 32768u +
-                                          (swz_chunk(chunk, TMAP_SWIZZLE_128B_K256) << 4) + (col & 7u) * 2u;
-                    const f32x2 lo = {acc[i][j][4 * q], acc[i][j][4 * q + 1]};
-                    const f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    const u32x2 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
-                                     __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
-                    *(lds_u2_t*)(uintptr_t)addr = v;
-                }
-        __syncthreads();
-        // Box store specialised to the 2-D C map: lane l of wave w handles
-        // logical chunk q = k*256 + w*64 + l of each box (8 rows x 128 bytes
-        // per wave and step, whole cache lines), reads its physical slot
-        // (conflict-free: the key only permutes chunks inside a 128-byte
-        // row), and writes 16 bytes, or element by element where the row
-        // crosses N.  Rows at or past M are skipped.  Every copy has landed
-        // by now, so the reads are ordinary LDS loads whose waits the
-        // compiler places itself.
-        typedef __attribute__((address_space(3))) const u32x4 lds_u4_t;
-        const uint64_t cstride = (uint64_t)g.Cm.stride[0];
-        const uint32_t Mc = (uint32_t)g.Cm.dim[1], Nc = (uint32_t)g.Cm.dim[0];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            u32x4 vs[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t q = (uint32_t)k * 256u + wave * 64u + lane;
-                const uint32_t addr = lds0 + (uint32_t)b * 32768u + (swz_chunk(q, TMAP_SWIZZLE_128B_K256) << 4);
-                vs[k] = *(lds_u4_t*)(uintptr_t)addr;
+        for (int r = 0; r < 2; ++r) {
+            if (r == 1) {
+                store_wait_read<0>(sg);               // this wave's stores no longer read either stage
+                wg_barrier();                         // ... nor any other wave's
             }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t q = (uint32_t)k * 256u + wave * 64u + lane;
-                const uint32_t row = m0 + (q >> 3);
-                const uint32_t col = n0 + (uint32_t)b * 64u + (q & 7u) * 8u;
-                const u32x4 v = vs[k];
-                if (row >= Mc || col >= Nc) continue;
-                gbyte* dst = gptr(g.Cm.base + row * cstride + (uint64_t)col * 2u);
-                if (col + 8u <= Nc) {
-                    // non-temporal: C is not read back, and the write burst
-                    // of all workgroups finishing together drains faster
-                    // without displacing the operand panels from L2
-                    __builtin_nontemporal_store(v, (ATT_GLOBAL u32x4*)dst);
-                } else {
+            for (int i = 0; i < NI; ++i)
 #pragma unroll
-                    for (uint32_t e = 0; e < 8; ++e)
-                        if (col + e < Nc) *(ATT_GLOBAL uint16_t*)(dst + 2u * e) = (uint16_t)chunk_element(v, 2u * e, 2u);
-                }
+                for (int jj = 0; jj < NJ / 2; ++jj)
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        const int j = r * (NJ / 2) + jj;
+                        const uint32_t row = rloc + (uint32_t)i * (uint32_t)MI;
+                        const uint32_t col = cloc + (uint32_t)j * (uint32_t)MI + (uint32_t)q * 8u;
+                        const uint32_t chunk = row * 8u + ((col & 63u) >> 3);
+                        const uint32_t addr = lds0 + wn * kStage + (swz_chunk(chunk, TMAP_SWIZZLE_128B_K256) << 4) +
+                                              (col & 7u) * 2u;
+                        const f32x2 lo = {acc[i][j][4 * q], acc[i][j][4 * q + 1]};
+                        const f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        const u32x2 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                                         __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
+                        *(lds_u2_t*)(uintptr_t)addr = v;
+                    }
+            wait_lgkm0();
+            wg_barrier();                             // both box images complete
+#pragma unroll
+            for (uint32_t st = 0; st < 2; ++st) {
+                const int32_t cb[5] = {(int32_t)(n0 + (2u * st + (uint32_t)r) * 64u), (int32_t)m0, 0, 0, 0};
+                // non-temporal: C is not read back, and the write burst of
+                // all workgroups finishing together drains faster without
+                // displacing the operand panels from L2
+                tile_store_async(cmap, cb, smem + st * kStage, wave, 4u, sg, true);
+                store_commit(sg);
             }
         }
         return;
@@ -401,7 +443,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     const uint32_t lane = lane_id();
     uint32_t tm, tn;
     gemm_block_tile(g, tm, tn);
-    const uint32_t m0 = tm * kTM, n0 = tn * kTN;
+    // tile origin, taken to scalar registers once: the operand copies take
+    // their bases from scalar arithmetic on these
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(tm * kTM), n0 = __builtin_amdgcn_readfirstlane(tn * kTN);
     const uint32_t nk = (g.K + BK - 1) / BK;
     constexpr bool interior = !EDGE;
 
@@ -634,7 +678,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         }
     }
     iteration(without_c{}, slot_rt{}, t, slot_t, slot_fill, 0u, false);
-    gemm_epilogue<MI, CF32>(g, acc, lds0, wave, lane, m0, n0);
+    gemm_epilogue<MI, CF32>(g, acc, smem, lds0, wave_u, lane, m0, n0);
 }
 
 // Operand ring for 64-deep boxes with 16 x 16 x 32 MFMAs: five 32 KiB slots
@@ -670,7 +714,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     const uint32_t lane = lane_id();
     uint32_t tm, tn;
     gemm_block_tile(g, tm, tn);
-    const uint32_t m0 = tm * kTM, n0 = tn * kTN;
+    // tile origin, taken to scalar registers once: the operand copies take
+    // their bases from scalar arithmetic on these
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(tm * kTM), n0 = __builtin_amdgcn_readfirstlane(tn * kTN);
     const uint32_t NT = g.K / 64u;                   // K-steps
     const uint32_t lds0 = lds_addr_of(smem);
     const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -697,8 +743,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
     auto copy_unit = [&](auto opc, uint32_t k, uint32_t slot, int c) {
         constexpr int OP = decltype(opc)::value;
         const uint32_t la = lds0 + slot * UBOX + wave_u * GPW * 1024u + (uint32_t)c * 1024u;
-        if constexpr (OP == 0) dma16_sv(baseA + (uint64_t)k * ROWB, offA[c], la);
-        else dma16_sv(baseB + (uint64_t)k * ROWB, offB[c], la);
+        if constexpr (OP == 0) dma16_sv_ring(baseA + (uint64_t)k * ROWB, offA[c], la);
+        else dma16_sv_ring(baseB + (uint64_t)k * ROWB, offB[c], la);
     };
     typedef std::integral_constant<int, 0> opA;
     typedef std::integral_constant<int, 1> opB;
@@ -804,7 +850,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         if (t + 3u < NT) body(std::integral_constant<int, 3>{}, t + 3u);
         if (t + 4u < NT) body(std::integral_constant<int, 4>{}, t + 4u);
     }
-    gemm_epilogue<MI, CF32>(g, acc, lds0, wave, lane, m0, n0);
+    gemm_epilogue<MI, CF32>(g, acc, smem, lds0, wave_u, lane, m0, n0);
 }
 
 template <int SWM, bool CF32 = false>
@@ -925,7 +971,8 @@ static tmap_status gemm_run(const tmap_t* A, const tmap_t* B, void* d_C, uint32_
         if (tmap_encode(&cm, TMAP_BF16, 2, d_C, cdim, cstride, cbox, nullptr, TMAP_SWIZZLE_128B_K256,
                         TMAP_OOB_ZERO) == TMAP_OK) {
             g.Cm = load_map(&cm);
-            g.c_staged = 1;
+            const TmapImpl want = gemm_c_box_map(g.Cm.base, g.Cm.stride[0], N, M);
+            g.c_staged = std::memcmp(&want, &g.Cm, sizeof(want)) == 0 ? 1u : 0u;
         }
     }
     hipStream_t st = as_stream(stream);

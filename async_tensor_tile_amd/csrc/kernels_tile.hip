@@ -18,6 +18,46 @@ namespace att {
 
 constexpr uint32_t kBatchThreads = 256;
 
+// Error bits the batch kernels record instead of trapping: a bounded barrier
+// wait gave up (the box it guarded is not valid), and, in builds with
+// ATT_DEBUG, a box whose waves issued other than its byte count or a barrier
+// found in the wrong state when its box was consumed.  Read and cleared by
+// tile_device_status.
+enum : uint32_t { DEVERR_TIMEOUT = 1u, DEVERR_BYTES = 2u, DEVERR_PHASE = 4u };
+static __device__ uint32_t g_dev_error;
+
+__device__ __forceinline__ void record_error(uint32_t bits) {
+    __hip_atomic_fetch_or(&g_dev_error, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Consume-side check of a barrier that completed phase 0: its state must be
+// re-armed (arrivals = count, pending 0) with the phase flipped, unless a
+// wait timed out (already recorded).  Debug builds only.
+__device__ __forceinline__ void check_consumed(TxBar* bar, bool ok) {
+    if (!ok) {
+        if (threadIdx.x % 64u == 0) record_error(DEVERR_TIMEOUT);
+        return;
+    }
+#ifdef ATT_DEBUG
+    const int64_t st = __hip_atomic_load(&bar->state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t ph = __hip_atomic_load(&bar->phase, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (threadIdx.x == 0 && (st != ((int64_t)bar->expected << 32) || ph != 1u)) record_error(DEVERR_PHASE);
+#else
+    (void)bar;
+#endif
+}
+
+#ifdef ATT_DEBUG
+// Debug builds poison an LDS image before it is loaded (a consumer that
+// reads before the copies land then sees the pattern, not stale data) and
+// add up the bytes the waves issued, which must equal the box bytes.
+constexpr uint32_t kPoison = 0xDBDBDBDBu;
+__device__ __forceinline__ void poison_image(uint8_t* img, uint32_t bytes) {
+    for (uint32_t i = threadIdx.x; i < bytes / 16u; i += blockDim.x)
+        reinterpret_cast<u32x4*>(img)[i] = u32x4{kPoison, kPoison, kPoison, kPoison};
+}
+#endif
+
 __device__ __forceinline__ void read_coords(const TmapImpl& m, const int32_t* __restrict__ coords,
                                             uint32_t b, int32_t c[5]) {
 #pragma unroll
@@ -34,14 +74,28 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load(tmap_t map, const i
     const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
     int32_t c[5];
     read_coords(m, coords, b, c);
+#ifdef ATT_DEBUG
+    uint32_t* issued = reinterpret_cast<uint32_t*>(smem + bar_off + sizeof(TxBar));
+    poison_image(smem, m.box_bytes);
+    if (tid == 0) *issued = 0;
+#endif
     if (tid == 0) {
         txbar_init(bar, 1);
         txbar_arrive_expect_tx(bar, (int32_t)tile_box_bytes(map));   // expect before any copy is issued
     }
     __syncthreads();
-    const uint32_t bytes = tile_load_async(map, c, smem, wave, nwaves);
-    tile_load_arrive(bar, bytes);
-    txbar_wait(bar, 0);
+    // the barrier form: each wave's share completes on `bar` once landed
+    const uint32_t bytes = tile_load_async(map, c, smem, bar, wave, nwaves);
+#ifdef ATT_DEBUG
+    if (lane_id() == 0) atomicAdd(issued, bytes);
+#endif
+    check_consumed(bar, txbar_wait(bar, 0));
+#ifdef ATT_DEBUG
+    __syncthreads();
+    if (tid == 0 && *issued != m.box_bytes) record_error(DEVERR_BYTES);
+#else
+    (void)bytes;
+#endif
     const uint32_t nchunk = m.box_bytes >> 4;
     uint8_t* dst = out + (size_t)b * m.box_bytes;
     for (uint32_t i = tid; i < nchunk; i += blockDim.x)
@@ -67,6 +121,9 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load_im2col(tmap_t map, 
 #pragma unroll
     for (int s = 0; s < 3; ++s)
         if (s < S) off[s] = offsets[(size_t)b * S + s];
+#ifdef ATT_DEBUG
+    poison_image(smem, m.box_bytes);
+#endif
     if (tid == 0) {
         txbar_init(bar, 1);
         txbar_arrive_expect_tx(bar, (int32_t)m.box_bytes);
@@ -74,7 +131,7 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load_im2col(tmap_t map, 
     __syncthreads();
     const uint32_t bytes = tile_load_im2col_async(map, c, off, smem, wave, nwaves);
     tile_load_arrive(bar, bytes);
-    txbar_wait(bar, 0);
+    check_consumed(bar, txbar_wait(bar, 0));
     const uint32_t nchunk = m.box_bytes >> 4;
     uint8_t* dst = out + (size_t)b * m.box_bytes;
     for (uint32_t i = tid; i < nchunk; i += blockDim.x)
@@ -112,7 +169,8 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_store(tmap_t map, const 
 __global__ __launch_bounds__(kBatchThreads) void k_txbar_selftest(tmap_t map, const int32_t* __restrict__ coords,
                                                                  uint32_t ntile, int32_t* __restrict__ trace,
                                                                  uint8_t* __restrict__ out, uint32_t img_stride,
-                                                                 uint32_t bar_off) {
+                                                                 uint32_t bar_off, uint32_t extra_bytes,
+                                                                 uint32_t max_polls) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     TxBar* bar = reinterpret_cast<TxBar*>(smem + bar_off);
     uint32_t* counter = reinterpret_cast<uint32_t*>(smem + bar_off + sizeof(TxBar));
@@ -121,7 +179,7 @@ __global__ __launch_bounds__(kBatchThreads) void k_txbar_selftest(tmap_t map, co
     if (tid == 0) {
         txbar_init(bar, 1);
         trace[0] = -1; trace[1] = bar->expected; trace[2] = 0; trace[3] = 0;
-        const TxState s = txbar_arrive_expect_tx(bar, (int32_t)(tile_box_bytes(map) * ntile));
+        const TxState s = txbar_arrive_expect_tx(bar, (int32_t)(tile_box_bytes(map) * ntile + extra_bytes));
         trace[4] = -2; trace[5] = s.arrivals_left; trace[6] = s.pending; trace[7] = (int32_t)s.phase;
         *counter = 0;
     }
@@ -143,7 +201,9 @@ __global__ __launch_bounds__(kBatchThreads) void k_txbar_selftest(tmap_t map, co
             trace[slot * 4 + 3] = (int32_t)s.phase;
         }
     }
-    txbar_wait(bar, 0);
+    const bool ok = txbar_wait(bar, 0, max_polls);
+    if (extra_bytes == 0) check_consumed(bar, ok);
+    else if (!ok && tid == 0) record_error(DEVERR_TIMEOUT);
     for (uint32_t t = 0; t < ntile; ++t) {
         const uint32_t nchunk = m.box_bytes >> 4;
         for (uint32_t i = tid; i < nchunk; i += blockDim.x)
@@ -323,8 +383,9 @@ extern "C" tmap_status tile_load_im2col(const tmap_t* m, const int32_t* d_coords
     return check_launch("tile_load_im2col");
 }
 
-extern "C" tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, uint32_t ntile,
-                                      int32_t* d_trace, void* d_lds_image_out, void* stream) {
+extern "C" tmap_status txbar_selftest_ex(const tmap_t* m, const int32_t* d_coords, uint32_t ntile,
+                                         uint32_t extra_bytes, uint32_t max_polls, int32_t* d_trace,
+                                         void* d_lds_image_out, void* stream) {
     if (!m || !d_coords || !d_trace || !d_lds_image_out) return TMAP_ERR_NULL;
     if (ntile < 1 || ntile > 8) return TMAP_ERR_UNSUPPORTED;
     const TmapImpl t = load_map(m);
@@ -335,9 +396,28 @@ extern "C" tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, 
     const uint32_t lds = bar_off + 64u;
     tmap_status st = prepare_dynamic_lds((const void*)k_txbar_selftest, lds);
     if (st) return st;
+    if (extra_bytes >= (1u << 30) || max_polls == 0) return TMAP_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(k_txbar_selftest, dim3(1), dim3(kBatchThreads), lds, as_stream(stream), map_value(m), d_coords, ntile,
-                       d_trace, static_cast<uint8_t*>(d_lds_image_out), img_stride, bar_off);
+                       d_trace, static_cast<uint8_t*>(d_lds_image_out), img_stride, bar_off, extra_bytes, max_polls);
     return check_launch("txbar_selftest");
+}
+
+extern "C" tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, uint32_t ntile,
+                                      int32_t* d_trace, void* d_lds_image_out, void* stream) {
+    return txbar_selftest_ex(m, d_coords, ntile, 0u, 1u << 22, d_trace, d_lds_image_out, stream);
+}
+
+extern "C" tmap_status tile_device_status(void* stream) {
+    hipError_t e = hipStreamSynchronize(as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    uint32_t bits = 0;
+    e = hipMemcpyFromSymbol(&bits, HIP_SYMBOL(g_dev_error), sizeof(bits), 0, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyFromSymbol");
+    if (bits == 0) return TMAP_OK;
+    const uint32_t zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_dev_error), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyToSymbol");
+    return (bits & DEVERR_TIMEOUT) ? TMAP_ERR_TIMEOUT : TMAP_ERR_DEVICE_CHECK;
 }
 
 extern "C" tmap_status lds_bank_probe(int32_t layout, uint32_t iters, int32_t* d_hist, void* stream) {

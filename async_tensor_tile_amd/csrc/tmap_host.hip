@@ -255,6 +255,8 @@ extern "C" const char* tmap_strerror(tmap_status s) {
     case TMAP_ERR_LDS_CAPACITY: return "box image exceeds the LDS of one workgroup";
     case TMAP_ERR_UNSUPPORTED: return "unsupported argument for this call";
     case TMAP_ERR_HIP: return "HIP runtime error";
+    case TMAP_ERR_TIMEOUT: return "a bounded barrier wait in a kernel gave up; the box it guarded is not valid";
+    case TMAP_ERR_DEVICE_CHECK: return "a device-side check of the debug build failed";
     default: return "unknown status";
     }
 }

@@ -96,6 +96,19 @@ __device__ __forceinline__ ChunkLoc chunk_locate(const TmapImpl& m, const int32_
     return r;
 }
 
+// chunk_locate for maps of rank 1 or 2 (dims 2..4 of extent 1, coordinate 0):
+// the row of the LDS image is the box coordinate in dim 1.
+__device__ __forceinline__ ChunkLoc chunk_locate_2d(const TmapImpl& m, const int32_t c[5], uint32_t q) {
+    const uint32_t row = fdiv(q, m.magic_cpr);
+    const uint32_t j = q - row * m.cpr;
+    ChunkLoc r;
+    r.g0 = (int64_t)c[0] + (int64_t)(j * (16u / m.esize)) * m.es[0];
+    const int64_t g1 = (int64_t)c[1] + (int64_t)row * m.es[1];
+    r.rest_in = g1 >= 0 && g1 < m.dim[1];
+    r.rest_off = g1 * (int64_t)m.stride[0];
+    return r;
+}
+
 // Gather one 16-byte chunk element by element (element stride in dim 0,
 // unaligned origin, or a chunk cut by the tensor edge).  Out-of-range
 // elements take the fill pattern and are never read.
@@ -546,10 +559,14 @@ __device__ __forceinline__ uint64_t chunk_element(const u32x4 v, uint32_t off, u
 // Lane l of group grp handles logical chunk grp*64 + l so that global writes
 // are in address order; it reads the chunk's physical LDS slot.  Elements
 // outside the tensor are skipped; OP (ST_STORE, ST_ADD, ST_MIN, ST_MAX)
-// stores, or combines atomically with what global memory holds.
-template <int OP>
-__device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_t c[5], const uint8_t* lds,
-                                                 uint32_t wave, uint32_t nwaves) {
+// stores, or combines atomically with what global memory holds; NT makes
+// the 16-byte stores non-temporal.  Returns a lower bound of the vector-
+// memory instructions this wave issued (the whole-chunk stores; reductions
+// and element stores count 0), which store groups use to bound vmcnt.  Every
+// LDS read of the call has completed when it returns.
+template <int OP, bool NT = false>
+__device__ __forceinline__ uint32_t tile_store_issue(const TmapImpl& m, const int32_t c[5], const uint8_t* lds,
+                                                     uint32_t wave, uint32_t nwaves) {
     const uint32_t lane = lane_id();
     const uint32_t nchunk = m.box_bytes >> 4;
     if constexpr (OP != ST_STORE) {
@@ -578,7 +595,8 @@ __device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_
                 if constexpr (OP == ST_ADD) reduce_add_element(m.dtype, dst, bits);
                 else reduce_minmax_element<OP == ST_MAX>(m.dtype, dst, bits);
             }
-            return;
+            wait_lgkm0();
+            return 0;
         }
         if (m.es[0] == 1) {
             // 8- and 16-bit elements: lane l takes one aligned 32-bit word of
@@ -637,42 +655,101 @@ __device__ __forceinline__ void tile_store_issue(const TmapImpl& m, const int32_
                 }
                 reduce_word<OP>(m.dtype, esz, wp, vw, inb);
             }
-            return;
+            wait_lgkm0();
+            return 0;
         }
     }
+    // Chunk-major: SB of this wave's 64-chunk groups per step, their LDS
+    // reads issued together ahead of the writes.
     const bool fast = (m.es[0] == 1) && ((((int64_t)c[0] * m.esize) & 15) == 0);
+    const bool two_d = m.rank <= 2;
     const int64_t n_el = 16 / m.esize;
-    for (uint32_t grp = wave; grp * 64u < nchunk; grp += nwaves) {
-        const uint32_t q = grp * 64u + lane;
-        if (q >= nchunk) continue;
-        const uint32_t p = swz_chunk(q, m.swizzle);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + p * 16u);
-        const ChunkLoc L = chunk_locate(m, c, q);
-        if (!L.rest_in) continue;
-        gbyte* rowp = gptr(m.base + (uint64_t)L.rest_off);
-        if (OP == ST_STORE && fast && L.g0 >= 0 && L.g0 + n_el <= m.dim[0]) {
-            *(ATT_GLOBAL u32x4*)(rowp + L.g0 * m.esize) = v;
-            continue;
+    constexpr uint32_t SB = 4;
+    uint32_t issued = 0;
+    for (uint32_t g0 = wave; g0 * 64u < nchunk; g0 += SB * nwaves) {
+        u32x4 v[SB];
+#pragma unroll
+        for (uint32_t b = 0; b < SB; ++b) {
+            const uint32_t q = (g0 + b * nwaves) * 64u + lane;
+            v[b] = q < nchunk ? *reinterpret_cast<const u32x4*>(lds + swz_chunk(q, m.swizzle) * 16u) : u32x4{};
         }
-        for (int64_t e = 0; e < n_el; ++e) {
-            const int64_t g = L.g0 + e * m.es[0];
-            if (g < 0 || g >= m.dim[0]) continue;
-            gbyte* dst = rowp + g * m.esize;
-            const uint64_t bits = chunk_element(v, (uint32_t)e * m.esize, m.esize);
-            if constexpr (OP == ST_ADD) {
-                reduce_add_element(m.dtype, dst, bits);
-            } else if constexpr (OP == ST_MIN || OP == ST_MAX) {
-                reduce_minmax_element<OP == ST_MAX>(m.dtype, dst, bits);
-            } else {
-                switch (m.esize) {
-                case 1: *dst = (uint8_t)bits; break;
-                case 2: *(ATT_GLOBAL uint16_t*)dst = (uint16_t)bits; break;
-                case 4: *(ATT_GLOBAL uint32_t*)dst = (uint32_t)bits; break;
-                default: *(ATT_GLOBAL uint64_t*)dst = bits; break;
+#pragma unroll
+        for (uint32_t b = 0; b < SB; ++b) {
+            const uint32_t q = (g0 + b * nwaves) * 64u + lane;
+            bool whole = false;
+            if (q < nchunk) {
+                const ChunkLoc L = two_d ? chunk_locate_2d(m, c, q) : chunk_locate(m, c, q);
+                if (L.rest_in) {
+                    gbyte* rowp = gptr(m.base + (uint64_t)L.rest_off);
+                    whole = OP == ST_STORE && fast && L.g0 >= 0 && L.g0 + n_el <= m.dim[0];
+                    if (whole) {
+                        ATT_GLOBAL u32x4* dst = (ATT_GLOBAL u32x4*)(rowp + L.g0 * m.esize);
+                        if constexpr (NT) __builtin_nontemporal_store(v[b], dst);
+                        else *dst = v[b];
+                    } else {
+                        for (int64_t e = 0; e < n_el; ++e) {
+                            const int64_t g = L.g0 + e * m.es[0];
+                            if (g < 0 || g >= m.dim[0]) continue;
+                            gbyte* dst = rowp + g * m.esize;
+                            const uint64_t bits = chunk_element(v[b], (uint32_t)e * m.esize, m.esize);
+                            if constexpr (OP == ST_ADD) {
+                                reduce_add_element(m.dtype, dst, bits);
+                            } else if constexpr (OP == ST_MIN || OP == ST_MAX) {
+                                reduce_minmax_element<OP == ST_MAX>(m.dtype, dst, bits);
+                            } else {
+                                switch (m.esize) {
+                                case 1: *dst = (uint8_t)bits; break;
+                                case 2: *(ATT_GLOBAL uint16_t*)dst = (uint16_t)bits; break;
+                                case 4: *(ATT_GLOBAL uint32_t*)dst = (uint32_t)bits; break;
+                                default: *(ATT_GLOBAL uint64_t*)dst = bits; break;
+                                }
+                            }
+                        }
+                    }
                 }
             }
+            // one 16-byte store instruction ran if any lane took it
+            if constexpr (OP == ST_STORE) issued += __ballot(whole) != 0 ? 1u : 0u;
         }
     }
+    wait_lgkm0();
+    return issued;
+}
+
+// ---- store groups --------------------------------------------------------
+// Wait until at most x of this wave's vector-memory instructions are
+// outstanding (x clamped to the counter's 63, which only waits longer).
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vmcnt_range(uint32_t x) {
+    if constexpr (LO == HI) {
+        wait_vmcnt<LO>();
+    } else {
+        constexpr int MID = (LO + HI + 1) / 2;
+        if (x >= (uint32_t)MID) wait_vmcnt_range<MID, HI>(x);
+        else wait_vmcnt_range<LO, MID - 1>(x);
+    }
+}
+
+__device__ __forceinline__ void wait_vmcnt_le(uint32_t x) { wait_vmcnt_range<0, 63>(x < 63u ? x : 63u); }
+
+// A wave's committed store groups ([HPC] "TMA store": commit_group, then
+// wait_group N; [MLC] "waiting for a TMA store").  Held per wave in scalar
+// registers: the stores issued since the last commit (`open`) and, newest
+// first, the sizes of the last kDepth committed groups, each a lower bound
+// of the vector-memory instructions the group issued.  A group's stores have
+// completed once the wave has at most as many instructions outstanding as
+// it issued after them; stores complete in issue order, and loads issued in
+// between only make the wait longer.
+struct StoreGroups {
+    static constexpr int kDepth = 4;
+    uint32_t open;
+    uint32_t cnt[kDepth];
+};
+
+__device__ __forceinline__ void store_groups_init(StoreGroups& g) {
+    g.open = 0;
+#pragma unroll
+    for (int i = 0; i < StoreGroups::kDepth; ++i) g.cnt[i] = 0;
 }
 
 // ---- byte-counted LDS barrier -----------------------------------------------

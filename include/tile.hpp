@@ -79,6 +79,13 @@ __device__ __forceinline__ const Im2colImpl& tmap_im2col(const tmap_t& map) {
     return *reinterpret_cast<const Im2colImpl*>(&map);
 }
 
+// The box origin as the address generator takes it: entries past the map's
+// rank become 0 (the caller's values there are ignored).
+__device__ __forceinline__ void clip_coords(const TmapImpl& m, const int32_t (&c)[5], int32_t (&out)[5]) {
+#pragma unroll
+    for (int d = 0; d < 5; ++d) out[d] = d < (int)m.rank ? c[d] : 0;
+}
+
 // Bytes of one box's LDS image: the expect_tx amount of a whole load, for
 // boxes inside, across or wholly outside the tensor alike ([HPC] async
 // completion arms the barrier with the full tile size).
@@ -92,7 +99,9 @@ __device__ __forceinline__ uint32_t tile_box_bytes(const tmap_t& map) { return t
 // they are (no float conversion); the swizzle is applied on the source side.
 __device__ __forceinline__ uint32_t tile_load_async(const tmap_t& map, const int32_t (&c)[5], void* lds,
                                                     uint32_t wave, uint32_t nwaves) {
-    return tile_load_issue(tmap_tiled(map), c, static_cast<uint8_t*>(lds), wave, nwaves);
+    int32_t cc[5];
+    clip_coords(tmap_tiled(map), c, cc);
+    return tile_load_issue(tmap_tiled(map), cc, static_cast<uint8_t*>(lds), wave, nwaves);
 }
 
 // Im2col-mode load ([HPC] closing paragraph names im2col-mode maps): the
@@ -103,7 +112,13 @@ __device__ __forceinline__ uint32_t tile_load_async(const tmap_t& map, const int
 __device__ __forceinline__ uint32_t tile_load_im2col_async(const tmap_t& map, const int32_t (&c)[5],
                                                            const int32_t (&off)[3], void* lds, uint32_t wave,
                                                            uint32_t nwaves) {
-    return tile_load_im2col_issue(tmap_im2col(map), c, off, static_cast<uint8_t*>(lds), wave, nwaves);
+    const Im2colImpl& m = tmap_im2col(map);
+    int32_t cc[5], oo[3];
+#pragma unroll
+    for (int d = 0; d < 5; ++d) cc[d] = d < (int)m.rank ? c[d] : 0;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) oo[s] = s + 2 < (int)m.rank ? off[s] : 0;
+    return tile_load_im2col_issue(m, cc, oo, static_cast<uint8_t*>(lds), wave, nwaves);
 }
 
 // Completion of a load ([MLC] "waiting for a TMA load": the copy reports the
@@ -117,16 +132,44 @@ __device__ __forceinline__ void tile_load_arrive(TxBar* bar, uint32_t bytes) {
     if (lane_id() == 0 && bytes) txbar_complete_tx(bar, (int32_t)bytes);
 }
 
+// The pages' form of the load, with the barrier as an argument ([HPC]
+// single-tile load: LDS destination, map, coordinates, barrier): this wave's
+// share of box `c` is issued and, once it has landed, its bytes are applied
+// to `bar` as complete_tx.  gfx950 has no engine to report the bytes later,
+// so the wave itself waits for its copies before returning; the two-step
+// form (tile_load_async, independent work, tile_load_arrive) keeps the wave
+// free in between.  Returns the bytes this wave's share wrote.
+__device__ __forceinline__ uint32_t tile_load_async(const tmap_t& map, const int32_t (&c)[5], void* lds, TxBar* bar,
+                                                    uint32_t wave, uint32_t nwaves) {
+    const uint32_t bytes = tile_load_async(map, c, lds, wave, nwaves);
+    tile_load_arrive(bar, bytes);
+    return bytes;
+}
+
 // Store, LDS -> global, with the inverse swizzle ([HPC] "TMA store").  Writes
 // this wave's share of the LDS image at `lds` to box `c`; elements outside
 // the tensor are not written.  The image must be complete in LDS (all its
 // writers past a workgroup barrier).  When the call returns this wave's LDS
-// reads have completed, so the image may be reused once every storing wave
-// has returned (the pages' commit-group / wait-group-read collapses to
-// that); the global writes are in flight until tile_store_wait.
+// reads have completed; the global writes are in flight.  Completion goes
+// through store groups: pass the wave's StoreGroups to add these stores to
+// its open group, then store_commit / store_wait<N> as on the pages
+// (tile_store_wait waits for everything).  `streaming` makes the 16-byte
+// stores non-temporal (for output not read again soon).
 __device__ __forceinline__ void tile_store_async(const tmap_t& map, const int32_t (&c)[5], const void* lds,
                                                  uint32_t wave, uint32_t nwaves) {
-    tile_store_issue<ST_STORE>(tmap_tiled(map), c, static_cast<const uint8_t*>(lds), wave, nwaves);
+    int32_t cc[5];
+    clip_coords(tmap_tiled(map), c, cc);
+    tile_store_issue<ST_STORE>(tmap_tiled(map), cc, static_cast<const uint8_t*>(lds), wave, nwaves);
+}
+
+__device__ __forceinline__ void tile_store_async(const tmap_t& map, const int32_t (&c)[5], const void* lds,
+                                                 uint32_t wave, uint32_t nwaves, StoreGroups& groups,
+                                                 bool streaming = false) {
+    int32_t cc[5];
+    clip_coords(tmap_tiled(map), c, cc);
+    const uint8_t* img = static_cast<const uint8_t*>(lds);
+    groups.open += streaming ? tile_store_issue<ST_STORE, true>(tmap_tiled(map), cc, img, wave, nwaves)
+                             : tile_store_issue<ST_STORE, false>(tmap_tiled(map), cc, img, wave, nwaves);
 }
 
 // Reduce store ([HPC] "TMA reduce": element-wise add, min or max on write
@@ -143,7 +186,17 @@ __device__ __forceinline__ void tile_reduce_async(const tmap_t& map, const int32
                                                   uint32_t wave, uint32_t nwaves) {
     static_assert(OP == TMAP_REDUCE_ADD || OP == TMAP_REDUCE_MIN || OP == TMAP_REDUCE_MAX, "reduce op");
     constexpr int ST = OP == TMAP_REDUCE_ADD ? ST_ADD : (OP == TMAP_REDUCE_MIN ? ST_MIN : ST_MAX);
-    tile_store_issue<ST>(tmap_tiled(map), c, static_cast<const uint8_t*>(lds), wave, nwaves);
+    int32_t cc[5];
+    clip_coords(tmap_tiled(map), c, cc);
+    tile_store_issue<ST>(tmap_tiled(map), cc, static_cast<const uint8_t*>(lds), wave, nwaves);
+}
+
+// The same reduction as part of the wave's open store group.
+template <int OP>
+__device__ __forceinline__ void tile_reduce_async(const tmap_t& map, const int32_t (&c)[5], const void* lds,
+                                                  uint32_t wave, uint32_t nwaves, StoreGroups& groups) {
+    tile_reduce_async<OP>(map, c, lds, wave, nwaves);
+    (void)groups;   // atomics add nothing to the group's lower bound
 }
 
 // Wait until this wave's global writes (stores and reductions) have
@@ -151,6 +204,52 @@ __device__ __forceinline__ void tile_reduce_async(const tmap_t& map, const int32
 // for this wave's outstanding loads.
 __device__ __forceinline__ void tile_store_wait() {
     wait_vmcnt<0>();
+    wait_lgkm0();
+}
+
+// ---- store groups ([HPC] "TMA store": commit_group / wait_group N; [MLC]
+// "waiting for a TMA store": the source tile may be overwritten only after
+// the group that stores it has completed) ------------------------------------
+//
+//     att::StoreGroups sg;
+//     att::store_groups_init(sg);
+//     att::tile_store_async(map, c0, stage0, w, nw, sg);  att::store_commit(sg);
+//     att::tile_store_async(map, c1, stage1, w, nw, sg);  att::store_commit(sg);
+//     att::store_wait<1>(sg);        // the first group's writes are done
+//     ... every storing wave waits, then a workgroup barrier; stage0 is free
+//
+// Groups are per wave, like the pages' per-thread groups: a stage stored by
+// several waves is free once each of them has waited and the workgroup has
+// passed a barrier.
+
+// Close the open group: the stores issued since the last commit.
+__device__ __forceinline__ void store_commit(StoreGroups& g) {
+#pragma unroll
+    for (int i = StoreGroups::kDepth - 1; i > 0; --i) g.cnt[i] = g.cnt[i - 1];
+    g.cnt[0] = g.open;
+    g.open = 0;
+}
+
+// Wait until every committed group except the N most recent has completed
+// (its global writes performed), as the pages' wait_group N.  Stores still
+// open count as newer than every committed group.
+template <int N>
+__device__ __forceinline__ void store_wait(StoreGroups& g) {
+    static_assert(N >= 0 && N < StoreGroups::kDepth, "store_wait depth");
+    uint32_t newer = g.open;
+#pragma unroll
+    for (int i = 0; i < N; ++i) newer += g.cnt[i];
+    wait_vmcnt_le(newer);
+}
+
+// The pages' wait_group.read N: the LDS sources of every committed group
+// except the N most recent may be overwritten.  On gfx950 a store call's
+// LDS reads have completed when it returns, so this only makes sure of that
+// (lgkmcnt); the global writes may still be in flight.
+template <int N>
+__device__ __forceinline__ void store_wait_read(StoreGroups& g) {
+    static_assert(N >= 0 && N < StoreGroups::kDepth, "store_wait depth");
+    (void)g;
     wait_lgkm0();
 }
 

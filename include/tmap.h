@@ -92,7 +92,12 @@ enum {
     TMAP_ERR_OOB_FILL_DTYPE = 10, /* NaN fill requested for an integer type   */
     TMAP_ERR_LDS_CAPACITY = 11,   /* box image larger than one workgroup's LDS*/
     TMAP_ERR_UNSUPPORTED = 12,    /* enum value or shape this call cannot do  */
-    TMAP_ERR_HIP = 13             /* HIP runtime error; see tmap_last_error() */
+    TMAP_ERR_HIP = 13,            /* HIP runtime error; see tmap_last_error() */
+    TMAP_ERR_TIMEOUT = 14,        /* a bounded barrier wait inside a kernel
+                                     gave up: the box it guarded is not valid
+                                     (reported by tile_device_status)        */
+    TMAP_ERR_DEVICE_CHECK = 15    /* a check of a debug build failed on the
+                                     device (tile_device_status)             */
 };
 
 /* Largest box image (bytes) a map may describe: the 160 KiB of LDS per CU
@@ -273,6 +278,29 @@ tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32_t stages,
  * fit LDS together.  Errors: NULL, UNSUPPORTED, LDS_CAPACITY, HIP. */
 tmap_status txbar_selftest(const tmap_t* m, const int32_t* d_coords, uint32_t ntile,
                            int32_t* d_trace, void* d_lds_image_out, void* stream);
+
+/* txbar_selftest with two more inputs: the barrier expects `extra_bytes`
+ * beyond the tiles' bytes (0 in txbar_selftest), and its final wait gives up
+ * after `max_polls` polls (each about a 64-cycle sleep; txbar_selftest uses
+ * 2^22).  With extra_bytes > 0 the phase never completes, so the wait times
+ * out and the kernel records TMAP_ERR_TIMEOUT for tile_device_status while
+ * still exiting normally: the host-forced failure path of the bounded wait.
+ * extra_bytes < 2^30, max_polls >= 1, else UNSUPPORTED; other errors as
+ * txbar_selftest. */
+tmap_status txbar_selftest_ex(const tmap_t* m, const int32_t* d_coords, uint32_t ntile,
+                              uint32_t extra_bytes, uint32_t max_polls, int32_t* d_trace,
+                              void* d_lds_image_out, void* stream);
+
+/* Device-side status of the batch calls (tile_load, tile_load_im2col,
+ * txbar_selftest[_ex]): their kernels never trap; a barrier wait that gives
+ * up (a box whose bytes never all arrived) or, in a debug build (ATT_DEBUG),
+ * a failed device check is recorded in a per-device error word instead.
+ * This call synchronises `stream`, reads that word on the current device
+ * and clears it: TMAP_OK if nothing was recorded since the last call,
+ * TMAP_ERR_TIMEOUT if a wait gave up, TMAP_ERR_DEVICE_CHECK for a debug
+ * check, TMAP_ERR_HIP on a runtime error.  Not for use under graph
+ * capture (it synchronises). */
+tmap_status tile_device_status(void* stream);
 
 /* LDS bank-sector probe ([MLC] "128-byte swizzle grouping requirement").
  * For a 16 x 256-byte sector grid laid out in LDS either grouped (two

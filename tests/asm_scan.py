@@ -40,7 +40,7 @@ def valu_sgpr_writes(text: str) -> set:
     out = set()
     if ops:
         out |= sregs(ops[0])
-    if len(ops) > 1 and re.search(r"_co_|_co$|addc|subb|div_scale", mnem):
+    if len(ops) > 1 and re.search(r"_co_|_co$|addc|subb|div_scale|mad_u64|mad_i64", mnem):
         out |= sregs(ops[1])
     if mnem.startswith("v_cmp") and mnem.endswith("_e32"):
         out.add("vcc")
@@ -120,3 +120,11 @@ def scan(asm: str, need: int = 5):
                 left -= wait_states(text)
                 j -= 1
     return count, violations
+
+
+def sgpr_spills(asm: str) -> dict:
+    """Kernel symbol -> .sgpr_spill_count from the code-object metadata."""
+    out = {}
+    for m in re.finditer(r"\.name:\s+(\S+)\s*\n(?:.*\n)*?\s+\.sgpr_spill_count:\s+(\d+)", asm):
+        out[m.group(1)] = int(m.group(2))
+    return out

@@ -28,6 +28,10 @@ def test_scanner_finds_planted_hazards():
                       "global_load_lds_dwordx4 v0, s[6:7]", "s_cbranch_scc1 .LBB0_1", "s_endpgm"])
     n, v = asm_scan.scan(loop)
     assert n == 1 and len(v) == 1
+    # the carry output of a 64-bit multiply-add is an SGPR write
+    mad = "\n".join(["k:", "v_mad_u64_u32 v[2:3], s[0:1], v4, v5, v[6:7]", "s_nop 0",
+                      "global_load_lds_dwordx4 v0, s[0:1]", "s_endpgm"])
+    assert len(asm_scan.scan(mad)[1]) == 1
     # unrelated SGPRs and SALU writes are not hazards
     ok = "\n".join(["k:", "v_readfirstlane_b32 s9, v3", "s_mov_b32 s0, s9", "s_nop 0",
                     "global_load_lds_dwordx4 v0, s[0:1]", "s_endpgm"])
@@ -46,6 +50,12 @@ def test_gemm_sgpr_base_dma_wait_states(tmp_path):
                            "-Wno-unused-command-line-argument", "--cuda-device-only", "-S",
                            os.path.join(ROOT, "async_tensor_tile_amd", "csrc", "kernel_gemm.hip"), "-o", str(out)],
                           stderr=subprocess.DEVNULL)
-    n, v = asm_scan.scan(out.read_text())
+    asm = out.read_text()
+    n, v = asm_scan.scan(asm)
     assert n > 0, "no SGPR-base LDS-DMA copies found"
     assert v == [], v[:5]
+    # the operand ring's copies rely on scalar-only bases: no SGPR spills
+    # (a spill restore is a VALU write of an SGPR)
+    spills = asm_scan.sgpr_spills(asm)
+    ring = {k: c for k, c in spills.items() if "k_gemm_bf16_ring5" in k}
+    assert len(ring) == 4 and all(c == 0 for c in ring.values()), ring

@@ -110,3 +110,61 @@ def test_bf16_disjoint_boxes(swizzle):
     assert landed.all()
     np.testing.assert_array_equal(dst, want_dst)
     np.testing.assert_array_equal(accg, want_acc)
+
+
+def staged_lib():
+    L = ctypes.CDLL(USER_LIB)
+    tp = ctypes.POINTER(att.tmap_t)
+    L.user_staged_copy_launch.argtypes = [tp, tp, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                          ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.user_staged_copy_launch.restype = ctypes.c_int
+    return L
+
+
+def whole_chunk_groups(dims, box, c, wave=0, nwaves=4):
+    """Lower bound a wave's store of box c reports for its group: its 64-chunk
+    groups (bf16, 128-byte rows: 8 rows each) holding at least one 16-byte
+    chunk wholly inside the tensor."""
+    rows, cols = box[1], box[0]
+    n = 0
+    for g in range(wave, rows * cols * 2 // 16 // 64, nwaves):
+        whole = False
+        for r in range(8 * g, 8 * g + 8):
+            for j in range(8):
+                x0, y = c[0] + 8 * j, c[1] + r
+                whole |= 0 <= y < dims[1] and x0 >= 0 and x0 + 8 <= dims[0]
+        n += whole
+    return n
+
+
+@pytest.mark.parametrize("stages,wait_n", [(1, 0), (2, 1)])
+def test_store_groups_reuse_stages(stages, wait_n):
+    """[HPC] "TMA store" commit / wait groups, [MLC] "waiting for a TMA
+    store": boxes copied through one LDS stage reused after store_wait<0>,
+    or two stages each reused after store_wait<1>, every load in the
+    barrier form; the destination bit-exact against the oracle (sentinel
+    outside the boxes), the group sizes equal to the whole-chunk groups of
+    each box, every wave's barrier waits completed."""
+    L = staged_lib()
+    dims, strides, box = (512, 256), (1024,), (64, 128)
+    src = synthgen.u16_bits(81, (256, 512))
+    sentinel = np.full((256, 512), 0xBEEF, dtype=np.uint16)
+    coords = np.array([[0, 0], [64, 0], [128, 128], [320, 0], [192, 128], [384, 128], [-100, -300],
+                       [480, 200], [256, 64 - 128], [0, 128]], dtype=np.int32)
+    sd, dd = to_dev(src), to_dev(sentinel)
+    ms = encode(sd, "bf16", dims, strides, box, None, "128b")
+    md = encode(dd, "bf16", dims, strides, box, None, "128b")
+    cd = to_dev(coords)
+    sizes = torch.full((len(coords),), -1, dtype=torch.int32, device="cuda")
+    landed = torch.zeros(4, dtype=torch.int32, device="cuda")
+    say("store groups", stages, wait_n)
+    rc = L.user_staged_copy_launch(ctypes.byref(ms), ctypes.byref(md), cd.data_ptr(), 2, len(coords), stages,
+                                   att.tmap_box_bytes(ms), sizes.data_ptr(), landed.data_ptr(), stream())
+    assert rc == 0, rc
+    got = to_host(dd).view(np.uint16).reshape(256, 512)
+    om = oracle.Map("bf16", dims, strides, box, swizzle="128b")
+    want = sentinel.copy()
+    om.store(want, coords, om.load(src, coords))
+    np.testing.assert_array_equal(got, want)
+    assert (to_host(landed) == 1).all()
+    assert to_host(sizes).tolist() == [whole_chunk_groups(dims, box, c) for c in coords.tolist()]

@@ -184,6 +184,36 @@ def test_txbar_several_tiles(ntile):
     np.testing.assert_array_equal(to_host(out).reshape(ntile, 2048), om.load(src, coords))
 
 
+def test_txbar_timeout_is_reported():
+    """A barrier expecting 16 bytes more than its copies deliver never
+    completes; its bounded wait gives up after a host-chosen 64 polls, the
+    kernel exits normally, and tile_device_status reports ERR_TIMEOUT once
+    (the record is cleared by reading it).  The copies themselves land."""
+    att.tile_device_status(stream())                    # nothing recorded yet
+    src = synthgen.u16_bits(9, (64, 64))
+    sd = to_dev(src)
+    m = encode(sd, "bf16", (64, 64), (128,), (64, 16), swizzle="128b")
+    coords = np.array([[0, 0], [0, 16]], dtype=np.int32)
+    trace = empty_dev(4 * 4 * 4, 0xFF)
+    out = empty_dev(2 * 2048, 0)
+    att.txbar_selftest_ex(m, to_dev(coords), 2, 16, 64, trace, out, stream())
+    with pytest.raises(att.TmapError) as ei:
+        att.tile_device_status(stream())
+    assert ei.value.name == "ERR_TIMEOUT"
+    att.tile_device_status(stream())                    # cleared
+    tr = to_host(trace).view(np.int32).reshape(4, 4)
+    assert tuple(tr[1]) == (-2, 0, 4096 + 16, 0)
+    assert sorted(int(r[2]) for r in tr[2:]) == [16, 2064] and (tr[2:, 3] == 0).all()
+    om = oracle.Map("bf16", (64, 64), (128,), (64, 16), swizzle="128b")
+    np.testing.assert_array_equal(to_host(out).reshape(2, 2048), om.load(src, coords))
+    # a good run afterwards records nothing
+    att.txbar_selftest(m, to_dev(coords), 2, trace, out, stream())
+    att.tile_device_status(stream())
+    with pytest.raises(att.TmapError) as ei:
+        att.txbar_selftest_ex(m, to_dev(coords), 2, 0, 0, trace, out, stream())
+    assert ei.value.name == "ERR_UNSUPPORTED"
+
+
 # --------------------------- brute force, tiny ------------------------------
 
 @pytest.mark.parametrize("seed", range(40))
