@@ -15,7 +15,10 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libatt_amd.so")
+# ATT_DEBUG=1 in the environment selects the debug build (LDS poisoning and
+# device-side checks, reported by tile_device_status).
+DEBUG = os.environ.get("ATT_DEBUG", "") not in ("", "0")
+LIB_PATH = os.path.join(HERE, "libatt_amd_debug.so" if DEBUG else "libatt_amd.so")
 
 DTYPE = {"u8": 0, "u16": 1, "u32": 2, "i32": 3, "u64": 4, "i64": 5,
          "f16": 6, "bf16": 7, "f32": 8, "f64": 9}
@@ -69,7 +72,8 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise NativeLibraryMissing(
                 f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                "(hipcc --offload-arch=gfx950) first")
+                "(hipcc --offload-arch=gfx950; the debug build with "
+                "async_tensor_tile_amd/_build.py --debug) first")
         L = ctypes.CDLL(LIB_PATH)
         tp = _P(tmap_t)
         L.tmap_encode.argtypes = [tp, _I32, _U32, _V, _P(ctypes.c_uint64), _P(ctypes.c_uint64),
@@ -97,13 +101,15 @@ def lib():
         L.tile_device_status.argtypes = [_V]
         L.lds_bank_probe.argtypes = [_I32, _U32, _V, _V]
         L.hbm_probe.argtypes = [_I32, _V, _V, ctypes.c_uint64, _V]
+        L.hbm_probe_copy_ex.argtypes = [_V, _V, ctypes.c_uint64, _U32, _U32, _V]
+        L.hbm_probe_box_copy.argtypes = [_V, _V, _U32, _U32, _U32, _U32, _V]
         L.gemm_bf16.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
         L.gemm_bf16_ex.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _V]
         L.gemm_bf16_f32.argtypes = [tp, tp, _V, _U32, _U32, _U32, _U32, _U32, _V]
         for name in ("tmap_encode", "tmap_replace_address", "tmap_query", "tile_load", "tile_store",
                      "tile_reduce_add", "tile_reduce", "tmap_encode_im2col", "tile_load_im2col", "tile_copy", "tile_copy_ex",
                      "txbar_selftest", "txbar_selftest_ex", "tile_device_status",
-                     "lds_bank_probe", "hbm_probe", "gemm_bf16", "gemm_bf16_ex", "gemm_bf16_f32"):
+                     "lds_bank_probe", "hbm_probe", "hbm_probe_copy_ex", "hbm_probe_box_copy", "gemm_bf16", "gemm_bf16_ex", "gemm_bf16_f32"):
             getattr(L, name).restype = _I32
         _lib = L
     return _lib
@@ -246,6 +252,18 @@ def hbm_probe(kind, d_src, d_dst, nbytes: int, stream=0) -> None:
     """Streaming HBM probe: kind "read" (0), "write" (1) or "copy" (2)."""
     k = {"read": 0, "write": 1, "copy": 2}.get(kind, kind)
     _check(lib().hbm_probe(int(k), _addr(d_src), _addr(d_dst), int(nbytes), _addr(stream)), "hbm_probe")
+
+
+def hbm_probe_copy_ex(d_src, d_dst, nbytes: int, variant: int, wg_per_cu: int, stream=0) -> None:
+    """The probe's copy in another launch shape (see tmap.h)."""
+    _check(lib().hbm_probe_copy_ex(_addr(d_src), _addr(d_dst), int(nbytes), int(variant), int(wg_per_cu),
+                                   _addr(stream)), "hbm_probe_copy_ex")
+
+
+def hbm_probe_box_copy(d_src, d_dst, width: int, height: int, boxes_per_wg: int, variant: int, stream=0) -> None:
+    """Box-shaped register copy with the tile copy's access shape (see tmap.h)."""
+    _check(lib().hbm_probe_box_copy(_addr(d_src), _addr(d_dst), int(width), int(height), int(boxes_per_wg),
+                                    int(variant), _addr(stream)), "hbm_probe_box_copy")
 
 
 def lds_bank_probe(layout: int, iters: int, d_hist, stream=0) -> None:

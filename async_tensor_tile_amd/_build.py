@@ -16,6 +16,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(HERE, "libatt_amd.so")
+# The debug build (ATT_DEBUG): LDS images and ring stages are poisoned before
+# they are loaded, the bytes a box's waves issue are checked against the box
+# bytes and a barrier's state against its completed phase when its box is
+# consumed; failures are recorded for tile_device_status.
+OBJ_DEBUG = os.path.join(ROOT, "_build", "obj_debug")
+LIB_DEBUG = os.path.join(HERE, "libatt_amd_debug.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -29,26 +35,29 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    subprocess.check_call([HIPCC, *FLAGS, "-c", src, "-o", obj])
+def _compile(src: str, debug: bool) -> str:
+    obj = os.path.join(OBJ_DEBUG if debug else OBJ, os.path.basename(src) + ".o")
+    subprocess.check_call([HIPCC, *FLAGS, *(["-DATT_DEBUG"] if debug else []), "-c", src, "-o", obj])
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libatt_amd.so; returns its path."""
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile every HIP source and link libatt_amd.so (libatt_amd_debug.so
+    with debug=True); returns its path."""
+    os.makedirs(OBJ_DEBUG if debug else OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     workers = max(1, min(len(srcs), 8))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda f: _compile(f, debug), srcs))
+    lib = LIB_DEBUG if debug else LIB
+    tmp = lib + ".tmp%d" % os.getpid()
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import sys
+    build(verbose=True, debug="--debug" in sys.argv[1:])

@@ -31,7 +31,10 @@ struct CopyArgs {
 
 // Copy variant flags (tile_copy_ex `variant`).
 // Bits 4..5 select how many consecutive boxes share one ring stage (1, 2, 4, 8).
-enum : uint32_t { CV_NT_STORE = 1u, CV_GENERIC = 2u, CV_CHUNKED = 4u, CV_XCD = 8u, CV_NB_SHIFT = 4u };
+enum : uint32_t {
+    CV_NT_STORE = 1u, CV_GENERIC = 2u, CV_CHUNKED = 4u, CV_XCD = 8u, CV_NB_SHIFT = 4u, CV_BATCH = 64u, CV_ROWMAJOR = 128u,
+    CV_REGLOAD = 256u
+};
 constexpr uint32_t kNumXcd = 8;
 
 constexpr uint32_t kCopyWaves = 4;
@@ -39,6 +42,17 @@ constexpr uint32_t kCopyWaves = 4;
 // Byte offsets of tile t's origin in src and dst (tiles innermost first).
 __device__ __forceinline__ void tile_origin(const CopyArgs& a, uint32_t t, uint64_t& so, uint64_t& dof,
                                             int32_t c[5]) {
+    if (a.src.rank <= 2) {
+        // one division instead of five (the short-lived workgroups pay this
+        // per box)
+        const uint32_t t1 = t / a.nt[0], t0 = t - t1 * a.nt[0];
+        c[0] = (int32_t)(t0 * (a.src.box_m1[0] + 1u));
+        c[1] = (int32_t)(t1 * (a.src.box_m1[1] + 1u));
+        c[2] = c[3] = c[4] = 0;
+        so = (uint64_t)c[0] * a.src.esize + (uint64_t)c[1] * a.src.stride[0];
+        dof = (uint64_t)c[0] * a.dst.esize + (uint64_t)c[1] * a.dst.stride[0];
+        return;
+    }
     so = 0;
     dof = 0;
 #pragma unroll
@@ -83,6 +97,35 @@ __device__ __forceinline__ void lds_read_group<8>(const uint32_t (&a)[8], u32x4 
                    "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]) : "memory");
 }
 
+// Per-lane constants of a wave's GPW groups, identical for every box: where
+// the chunk this lane loads comes from (its logical chunk swz(p)), where the
+// chunk it stores goes (logical chunk p) and the LDS address of the slot
+// holding the latter.  Maps of rank 1 or 2 take a few integer operations per
+// chunk (box row = chunk / chunks-per-row) instead of the general rank-5
+// address generator.
+template <int GPW>
+__device__ __forceinline__ void copy_lane_offsets(const CopyArgs& a, uint32_t wave, uint32_t lane, uint32_t lds0,
+                                                  uint64_t (&ld_off)[GPW], uint64_t (&st_off)[GPW], uint32_t (&rd)[GPW]) {
+    const uint32_t sw = a.src.swizzle;
+    const int32_t zero[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        const uint32_t p = (wave * GPW + j) * 64u + lane;
+        const uint32_t q = swz_chunk(p, sw);
+        rd[j] = lds0 + q * 16u;
+        if (a.src.rank <= 2) {
+            const uint32_t rq = fdiv(q, a.src.magic_cpr), rp = fdiv(p, a.src.magic_cpr);
+            ld_off[j] = (uint64_t)rq * a.src.stride[0] + (q - rq * a.src.cpr) * 16u;
+            st_off[j] = (uint64_t)rp * a.dst.stride[0] + (p - rp * a.src.cpr) * 16u;
+        } else {
+            const ChunkLoc ls = chunk_locate(a.src, zero, q);
+            ld_off[j] = (uint64_t)(ls.g0 * a.src.esize + ls.rest_off);
+            const ChunkLoc ld = chunk_locate(a.dst, zero, p);
+            st_off[j] = (uint64_t)(ld.g0 * a.dst.esize + ld.rest_off);
+        }
+    }
+}
+
 // One stage holds NB consecutive boxes (each its own dense LDS image).  The
 // wave issues its DMA instructions row-group major, box minor, so that
 // back-to-back requests cover NB neighbouring 128-byte segments of the same
@@ -93,25 +136,10 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a, 
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t lane = lane_id();
     const uint32_t B = a.src.box_bytes;
-    const uint32_t sw = a.src.swizzle;
-
-    // Per-lane constants, identical for every box: where the chunk this lane
-    // loads comes from, where the chunk it stores goes, and which LDS slot
-    // holds the latter.
     uint64_t ld_off[GPW], st_off[GPW];
     uint32_t rd[GPW];
-    const int32_t zero[5] = {0, 0, 0, 0, 0};
     const uint32_t lds0 = lds_addr_of(smem);
-#pragma unroll
-    for (int j = 0; j < GPW; ++j) {
-        const uint32_t grp = wave * GPW + j;
-        const uint32_t p = grp * 64u + lane;
-        const ChunkLoc ls = chunk_locate(a.src, zero, swz_chunk(p, sw));
-        ld_off[j] = (uint64_t)(ls.g0 * a.src.esize + ls.rest_off);
-        const ChunkLoc ld = chunk_locate(a.dst, zero, p);
-        st_off[j] = (uint64_t)(ld.g0 * a.dst.esize + ld.rest_off);
-        rd[j] = lds0 + swz_chunk(p, sw) * 16u;
-    }
+    copy_lane_offsets<GPW>(a, wave, lane, lds0, ld_off, st_off, rd);
 
     // Units of NB boxes.  Workgroups are dispatched round-robin over the
     // XCDs; with `xcd` the ones sharing an XCD get neighbouring unit ranges.
@@ -135,6 +163,17 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a, 
             tile_origin(a, t0 + x, so, dof, c);
             sb[x] = a.src.base + so;
         }
+#ifdef ATT_DEBUG
+        // debug builds poison the wave's groups of the stage before refilling
+        // them, so a read ahead of its copies sees the pattern
+#pragma unroll
+        for (int j = 0; j < GPW; ++j)
+#pragma unroll
+            for (int x = 0; x < NB; ++x)
+                *reinterpret_cast<u32x4*>(stage + x * B + (wave * GPW + j) * 1024u + lane * 16u) =
+                    u32x4{0xDBDBDBDBu, 0xDBDBDBDBu, 0xDBDBDBDBu, 0xDBDBDBDBu};
+        wait_lgkm0();
+#endif
 #pragma unroll
         for (int j = 0; j < GPW; ++j)
 #pragma unroll
@@ -173,6 +212,87 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a, 
     }
 }
 
+// Batch round trip: workgroup b owns NBOX consecutive boxes and gives each
+// its own LDS stage.  Every wave issues all its copies up front, then takes
+// the stages in order -- waiting only for that stage's copies (loads
+// complete in issue order; no store has been issued yet, so vmcnt counts
+// copies alone) and reading its chunks into registers -- and stores all of
+// them at the end.  No wait ever covers a store, so the end of one box's
+// stores is never on the path to the next box, and the workgroup retires as
+// soon as its stores are issued.
+template <int GPW, int NBOX, bool ROWMAJOR, bool REGLOAD>
+__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_batch(CopyArgs a, uint32_t nt_store) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t lane = lane_id();
+    const uint32_t B = a.src.box_bytes;
+    const uint32_t G = gridDim.x;
+    const uint32_t b = a.xcd ? (blockIdx.x % kNumXcd) * (G / kNumXcd) + blockIdx.x / kNumXcd : blockIdx.x;
+    const uint32_t t0 = b * NBOX;
+    if (t0 >= a.ntiles) return;
+    const uint32_t lds0 = lds_addr_of(smem);
+    uint64_t ld_off[GPW], st_off[GPW];
+    uint32_t rd[GPW];
+    copy_lane_offsets<GPW>(a, wave, lane, lds0, ld_off, st_off, rd);
+    uint64_t sof[NBOX], dof[NBOX];
+#pragma unroll
+    for (int x = 0; x < NBOX; ++x) {
+        int32_t c[5];
+        tile_origin(a, t0 + x, sof[x], dof[x], c);
+#ifdef ATT_DEBUG
+#pragma unroll
+        for (int j = 0; j < GPW; ++j)
+            *reinterpret_cast<u32x4*>(smem + x * B + (wave * GPW + j) * 1024u + lane * 16u) =
+                u32x4{0xDBDBDBDBu, 0xDBDBDBDBu, 0xDBDBDBDBu, 0xDBDBDBDBu};
+#endif
+    }
+#ifdef ATT_DEBUG
+    wait_lgkm0();
+#endif
+    // ROWMAJOR: copy j of every box, then copy j+1 (the boxes sit side by
+    // side, so back-to-back requests cover the same rows NBOX x 128 bytes
+    // wide); else box by box.
+    u32x4 v[NBOX][GPW];
+    if constexpr (REGLOAD) {
+        // the loads go to registers and each lane writes its chunk to the
+        // slot the copy engine form would (the same LDS image); the wave
+        // reads back only chunks it wrote itself, so LDS order suffices
+#pragma unroll
+        for (int o = 0; o < NBOX * GPW; ++o) {
+            const int x = ROWMAJOR ? o % NBOX : o / GPW, j = ROWMAJOR ? o / NBOX : o % GPW;
+            v[x][j] = *(const ATT_GLOBAL u32x4*)gptr(a.src.base + sof[x] + ld_off[j]);
+        }
+#pragma unroll
+        for (int o = 0; o < NBOX * GPW; ++o) {
+            const int x = ROWMAJOR ? o % NBOX : o / GPW, j = ROWMAJOR ? o / NBOX : o % GPW;
+            *reinterpret_cast<u32x4*>(smem + x * B + (wave * GPW + j) * 1024u + lane * 16u) = v[x][j];
+        }
+    } else {
+#pragma unroll
+        for (int o = 0; o < NBOX * GPW; ++o) {
+            const int x = ROWMAJOR ? o % NBOX : o / GPW, j = ROWMAJOR ? o / NBOX : o % GPW;
+            dma16((const void*)(uintptr_t)(a.src.base + sof[x] + ld_off[j]), smem + x * B + (wave * GPW + j) * 1024u);
+        }
+        // every copy of the workgroup's boxes has landed (the wave only
+        // reads chunks it copied itself)
+        wait_vmcnt<0>();
+    }
+    // all stages read with ordinary LDS loads (one wait for all of them),
+    // then every chunk stored, in the order the loads went out
+#pragma unroll
+    for (int x = 0; x < NBOX; ++x)
+#pragma unroll
+        for (int j = 0; j < GPW; ++j)
+            v[x][j] = *reinterpret_cast<const u32x4*>(smem + x * B + (rd[j] - lds0));
+#pragma unroll
+    for (int o = 0; o < NBOX * GPW; ++o) {
+        const int x = ROWMAJOR ? o % NBOX : o / GPW, j = ROWMAJOR ? o / NBOX : o % GPW;
+        ATT_GLOBAL u32x4* p = (ATT_GLOBAL u32x4*)(gptr(a.dst.base + dof[x]) + st_off[j]);
+        if (nt_store) __builtin_nontemporal_store(v[x][j], p);
+        else *p = v[x][j];
+    }
+}
+
 // Generic round trip: one workgroup per tile, any geometry.
 __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_generic(CopyArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -185,6 +305,42 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_generic(CopyArgs 
     wait_lgkm0();
     __syncthreads();
     tile_store_issue<ST_STORE>(a.dst, c, smem, wave, nwaves);
+}
+
+template <int GPW, int NBOX, bool ROWMAJOR, bool REGLOAD>
+static tmap_status launch_batch(const CopyArgs& a, uint32_t nt, hipStream_t st) {
+    if constexpr (GPW * (NBOX - 1) > 63 || GPW * NBOX > 32) {
+        return TMAP_ERR_UNSUPPORTED;           // vmcnt range; registers for every chunk
+    } else {
+        const uint32_t lds = (uint32_t)NBOX * a.src.box_bytes;
+        hipError_t e = hipFuncSetAttribute((const void*)k_tile_copy_batch<GPW, NBOX, ROWMAJOR, REGLOAD>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+        const uint32_t grid = a.ntiles / NBOX;
+        hipLaunchKernelGGL((k_tile_copy_batch<GPW, NBOX, ROWMAJOR, REGLOAD>), dim3(grid), dim3(kCopyWaves * 64), lds, st,
+                           a, nt);
+        return check_launch("tile_copy");
+    }
+}
+
+template <int GPW, bool REGLOAD>
+static tmap_status launch_batch_n(const CopyArgs& a, uint32_t nbox, bool rowmajor, uint32_t nt, hipStream_t st) {
+    switch (nbox * 2 + (rowmajor ? 1 : 0)) {
+    case 4: return launch_batch<GPW, 2, false, REGLOAD>(a, nt, st);
+    case 5: return launch_batch<GPW, 2, true, REGLOAD>(a, nt, st);
+    case 6: return launch_batch<GPW, 3, false, REGLOAD>(a, nt, st);
+    case 7: return launch_batch<GPW, 3, true, REGLOAD>(a, nt, st);
+    case 8: return launch_batch<GPW, 4, false, REGLOAD>(a, nt, st);
+    case 9: return launch_batch<GPW, 4, true, REGLOAD>(a, nt, st);
+    default: return TMAP_ERR_UNSUPPORTED;
+    }
+}
+
+template <int GPW>
+static tmap_status launch_batch_r(const CopyArgs& a, uint32_t nbox, bool rowmajor, bool regload, uint32_t nt,
+                                  hipStream_t st) {
+    return regload ? launch_batch_n<GPW, true>(a, nbox, rowmajor, nt, st)
+                   : launch_batch_n<GPW, false>(a, nbox, rowmajor, nt, st);
 }
 
 template <int GPW, int S, int NB>
@@ -263,7 +419,7 @@ using namespace att;
 extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32_t stages, uint32_t grid,
                                     uint32_t variant, void* stream) {
     if (!src || !dst) return TMAP_ERR_NULL;
-    if (stages < 1 || stages > 8 || variant > 63) return TMAP_ERR_UNSUPPORTED;
+    if (stages < 1 || stages > 8 || variant > 511) return TMAP_ERR_UNSUPPORTED;
     CopyArgs a;
     a.src = load_map(src);
     a.dst = load_map(dst);
@@ -299,6 +455,22 @@ extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32
                          (gpw == 1 || gpw == 2 || gpw == 4 || gpw == 8) && stages * nb * B <= limit &&
                          gpw * nb * (stages - 1) <= 63 && stages != 5 && stages != 7;
     hipStream_t s = as_stream(stream);
+    // batch mode: `stages` boxes per workgroup, one stage each
+    const bool batch_ok = (variant & CV_BATCH) && even && !(variant & CV_GENERIC) && gpw * kCopyWaves == groups &&
+                          (gpw == 1 || gpw == 2 || gpw == 4 || gpw == 8) && stages >= 2 && stages <= 4 &&
+                          stages * B <= limit && a.ntiles % stages == 0 && gpw * (stages - 1) <= 63;
+    if (batch_ok) {
+        const uint32_t g = a.ntiles / stages;
+        a.xcd = ((variant & CV_XCD) && g % kNumXcd == 0) ? 1u : 0u;
+        const uint32_t nt = (variant & CV_NT_STORE) ? 1u : 0u;
+        const bool rm = (variant & CV_ROWMAJOR) != 0, rl = (variant & CV_REGLOAD) != 0;
+        switch (gpw) {
+        case 1: return launch_batch_r<1>(a, stages, rm, rl, nt, s);
+        case 2: return launch_batch_r<2>(a, stages, rm, rl, nt, s);
+        case 4: return launch_batch_r<4>(a, stages, rm, rl, nt, s);
+        default: return launch_batch_r<8>(a, stages, rm, rl, nt, s);
+        }
+    }
     if (ring_ok) {
         const uint32_t units = a.ntiles / nb;
         const uint32_t g = grid ? grid : auto_grid(units, cus, stages * nb * B);

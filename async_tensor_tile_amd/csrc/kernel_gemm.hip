@@ -235,11 +235,21 @@ static_assert(waits_consistent<GemmSched<8, 8, 2, 4>>() && waits_consistent<Gemm
 // suite compiles this file to gfx950 assembly and checks both: no
 // SGPR-base DMA of any kernel here has a VALU write of its base or M0 within
 // five wait states on any path, and the ring kernels report no SGPR spills.
+// Debug builds poison the 1 KiB group before refilling it (a fragment read
+// ahead of its copy then sees the pattern) and keep the full wait states.
 __device__ __forceinline__ void dma16_sv_ring(uint64_t sbase, uint32_t voff, uint32_t lds_group_addr) {
+#ifdef ATT_DEBUG
+    typedef __attribute__((address_space(3))) u32x4 lds_u4_t;
+    *(lds_u4_t*)(uintptr_t)(lds_group_addr + lane_id() * 16u) =
+        u32x4{0xDBDBDBDBu, 0xDBDBDBDBu, 0xDBDBDBDBu, 0xDBDBDBDBu};
+    wait_lgkm0();
+    dma16_sv(sbase, voff, lds_group_addr);
+#else
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(sbase), "{m0}"(lds_group_addr)
                  : "memory");
+#endif
 }
 
 template <int N>

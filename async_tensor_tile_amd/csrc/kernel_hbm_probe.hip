@@ -66,9 +66,167 @@ __global__ __launch_bounds__(kProbeThreads) void k_hbm_copy(const u32x4* __restr
     }
 }
 
+// Variants for the ceiling sweep: U 16-byte vectors per thread and step,
+// non-temporal or ordinary stores, and grid-stride order or a contiguous
+// slice per workgroup.
+template <int U, bool NT, bool SLICE>
+__global__ __launch_bounds__(kProbeThreads) void k_hbm_copy_v(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                              uint64_t n16) {
+    const uint64_t chunk = (uint64_t)kProbeThreads * U;
+    uint64_t first = (uint64_t)blockIdx.x * chunk, step = (uint64_t)gridDim.x * chunk, end = n16;
+    if (SLICE) {
+        const uint64_t per = ((n16 + gridDim.x - 1) / gridDim.x + chunk - 1) / chunk * chunk;
+        first = (uint64_t)blockIdx.x * per;
+        step = chunk;
+        end = first + per < n16 ? first + per : n16;
+    }
+    for (uint64_t i = first + threadIdx.x; i < end; i += step) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t j = i + (uint64_t)u * kProbeThreads;
+            v[u] = j < end ? ((const ATT_GLOBAL u32x4*)src)[j] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t j = i + (uint64_t)u * kProbeThreads;
+            if (j < end) {
+                if (NT) __builtin_nontemporal_store(v[u], (ATT_GLOBAL u32x4*)dst + j);
+                else ((ATT_GLOBAL u32x4*)dst)[j] = v[u];
+            }
+        }
+    }
+}
+
+template <int U, bool NT>
+static void launch_copy_v(bool slice, uint32_t grid, hipStream_t s, const void* src, void* dst, uint64_t n16) {
+    if (slice)
+        hipLaunchKernelGGL((k_hbm_copy_v<U, NT, true>), dim3(grid), dim3(kProbeThreads), 0, s, (const u32x4*)src,
+                           (u32x4*)dst, n16);
+    else
+        hipLaunchKernelGGL((k_hbm_copy_v<U, NT, false>), dim3(grid), dim3(kProbeThreads), 0, s, (const u32x4*)src,
+                           (u32x4*)dst, n16);
+}
+
+// Box-shaped copy without LDS: a row-major byte matrix (rows of `width`
+// bytes) is copied in boxes of 128 rows x 128 bytes, NBX boxes side by side
+// per workgroup, with exactly the access shape of the tile copy -- one
+// 16-byte vector per lane, 64 lanes = 8 rows x 128 bytes of one box per
+// instruction -- but through registers: every load of the workgroup's boxes
+// first, then every store.  Row-group major issue (NBX boxes' rows 8g..8g+7
+// back to back), or box major.  Measures what the box shape itself costs.
+template <int NBX, bool NT, bool BOXMAJOR>
+__global__ __launch_bounds__(kProbeThreads) void k_hbm_box_copy(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                                uint32_t width, uint32_t boxes_per_row, uint32_t xcd) {
+    const uint32_t G = gridDim.x;
+    const uint32_t b = xcd ? (blockIdx.x % 8u) * (G / 8u) + blockIdx.x / 8u : blockIdx.x;
+    const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63u;
+    const uint32_t t0 = b * NBX;                       // first box of the workgroup (row-major box order)
+    const uint64_t band = t0 / boxes_per_row, col0 = t0 % boxes_per_row;
+    u32x4 v[4][NBX];
+#pragma unroll
+    for (int o = 0; o < 4 * NBX; ++o) {
+        const int g = BOXMAJOR ? o % 4 : o / NBX, x = BOXMAJOR ? o / 4 : o % NBX;
+        const uint64_t row = band * 128u + (wave * 4u + (uint32_t)g) * 8u + lane / 8u;
+        const uint64_t off = row * width + (col0 + (uint64_t)x) * 128u + (lane % 8u) * 16u;
+        v[g][x] = *(const ATT_GLOBAL u32x4*)gptr(src + off);
+    }
+#pragma unroll
+    for (int o = 0; o < 4 * NBX; ++o) {
+        const int g = BOXMAJOR ? o % 4 : o / NBX, x = BOXMAJOR ? o / 4 : o % NBX;
+        const uint64_t row = band * 128u + (wave * 4u + (uint32_t)g) * 8u + lane / 8u;
+        const uint64_t off = row * width + (col0 + (uint64_t)x) * 128u + (lane % 8u) * 16u;
+        if (NT) __builtin_nontemporal_store(v[g][x], (ATT_GLOBAL u32x4*)gptr(dst + off));
+        else *(ATT_GLOBAL u32x4*)gptr(dst + off) = v[g][x];
+    }
+}
+
+template <int NBX>
+static tmap_status launch_box_copy(uint32_t variant, uint32_t grid, hipStream_t s, const void* src, void* dst,
+                                   uint32_t width, uint32_t bpr) {
+    const uint32_t xcd = (variant >> 1) & 1u;
+    // bits 3..4: reserve as much LDS per workgroup as the tile copy's stages
+    // would take for NBX 16 KiB boxes (x1, x2 or x4 of 16 KiB), so that LDS,
+    // not registers, bounds the workgroups per CU as it does there
+    const uint32_t lds = ((variant >> 3) & 3u) ? (16384u << (((variant >> 3) & 3u) - 1u)) : 0u;
+    const uint8_t* a = (const uint8_t*)src;
+    uint8_t* d = (uint8_t*)dst;
+    const void* fn;
+    switch (variant & 5u) {
+    case 0: fn = (const void*)k_hbm_box_copy<NBX, false, false>; break;
+    case 1: fn = (const void*)k_hbm_box_copy<NBX, true, false>; break;
+    case 4: fn = (const void*)k_hbm_box_copy<NBX, false, true>; break;
+    default: fn = (const void*)k_hbm_box_copy<NBX, true, true>; break;
+    }
+    if (lds) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+    }
+    switch (variant & 5u) {
+    case 0: hipLaunchKernelGGL((k_hbm_box_copy<NBX, false, false>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, xcd); break;
+    case 1: hipLaunchKernelGGL((k_hbm_box_copy<NBX, true, false>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, xcd); break;
+    case 4: hipLaunchKernelGGL((k_hbm_box_copy<NBX, false, true>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, xcd); break;
+    default: hipLaunchKernelGGL((k_hbm_box_copy<NBX, true, true>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, xcd); break;
+    }
+    return TMAP_OK;
+}
+
 }  // namespace att
 
 using namespace att;
+
+extern "C" tmap_status hbm_probe_box_copy(const void* d_src, void* d_dst, uint32_t width, uint32_t height,
+                                          uint32_t boxes_per_wg, uint32_t variant, void* stream) {
+    if (!d_src || !d_dst) return TMAP_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(d_src) | reinterpret_cast<uintptr_t>(d_dst)) & 15u) return TMAP_ERR_ALIGN;
+    if (variant > 31 || width == 0 || height == 0 || width % 128u || height % 128u) return TMAP_ERR_UNSUPPORTED;
+    const uint32_t bpr = width / 128u;
+    const uint64_t nbox = (uint64_t)bpr * (height / 128u);
+    if (!(boxes_per_wg == 1 || boxes_per_wg == 2 || boxes_per_wg == 4 || boxes_per_wg == 8) || bpr % boxes_per_wg ||
+        nbox / boxes_per_wg > 0x7FFFFFFFull)
+        return TMAP_ERR_UNSUPPORTED;
+    const uint32_t grid = (uint32_t)(nbox / boxes_per_wg);
+    if (((variant >> 1) & 1u) && grid % 8u) return TMAP_ERR_UNSUPPORTED;
+    hipStream_t s = as_stream(stream);
+    tmap_status st = TMAP_OK;
+    switch (boxes_per_wg) {
+    case 1: st = launch_box_copy<1>(variant, grid, s, d_src, d_dst, width, bpr); break;
+    case 2: st = launch_box_copy<2>(variant, grid, s, d_src, d_dst, width, bpr); break;
+    case 4: st = launch_box_copy<4>(variant, grid, s, d_src, d_dst, width, bpr); break;
+    default: st = launch_box_copy<8>(variant, grid, s, d_src, d_dst, width, bpr); break;
+    }
+    if (st) return st;
+    return check_launch("hbm_probe_box_copy");
+}
+
+extern "C" tmap_status hbm_probe_copy_ex(const void* d_src, void* d_dst, uint64_t bytes, uint32_t variant,
+                                         uint32_t wg_per_cu, void* stream) {
+    if ((bytes & 15u) || variant > 15 || wg_per_cu < 1 || wg_per_cu > 32) return TMAP_ERR_UNSUPPORTED;
+    if (bytes == 0) return TMAP_OK;
+    if (!d_src || !d_dst) return TMAP_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(d_src) | reinterpret_cast<uintptr_t>(d_dst)) & 15u) return TMAP_ERR_ALIGN;
+    uint32_t cus = 0;
+    tmap_status st = device_cu_count(&cus);
+    if (st) return st;
+    const uint64_t n16 = bytes / 16u;
+    const uint32_t u = 1u << (variant & 3u);
+    const bool nt = (variant >> 2) & 1u, slice = (variant >> 3) & 1u;
+    uint64_t grid = (uint64_t)cus * wg_per_cu;
+    const uint64_t need = (n16 + (uint64_t)kProbeThreads * u - 1) / ((uint64_t)kProbeThreads * u);
+    if (grid > need) grid = need;
+    hipStream_t s = as_stream(stream);
+    switch (u * 2 + (nt ? 1 : 0)) {
+    case 2: launch_copy_v<1, false>(slice, (uint32_t)grid, s, d_src, d_dst, n16); break;
+    case 3: launch_copy_v<1, true>(slice, (uint32_t)grid, s, d_src, d_dst, n16); break;
+    case 4: launch_copy_v<2, false>(slice, (uint32_t)grid, s, d_src, d_dst, n16); break;
+    case 5: launch_copy_v<2, true>(slice, (uint32_t)grid, s, d_src, d_dst, n16); break;
+    case 8: launch_copy_v<4, false>(slice, (uint32_t)grid, s, d_src, d_dst, n16); break;
+    case 9: launch_copy_v<4, true>(slice, (uint32_t)grid, s, d_src, d_dst, n16); break;
+    case 16: launch_copy_v<8, false>(slice, (uint32_t)grid, s, d_src, d_dst, n16); break;
+    default: launch_copy_v<8, true>(slice, (uint32_t)grid, s, d_src, d_dst, n16); break;
+    }
+    return check_launch("hbm_probe_copy_ex");
+}
 
 extern "C" tmap_status hbm_probe(int32_t kind, const void* d_src, void* d_dst, uint64_t bytes, void* stream) {
     if (kind < 0 || kind > 2 || (bytes & 15u)) return TMAP_ERR_UNSUPPORTED;

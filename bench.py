@@ -64,39 +64,96 @@ def gemm_traffic():
     return c.get("hbm_bytes_per_launch") if c else None
 
 
-def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 8):
-    """The oracle (single-threaded C) doing the same round trip on the host:
-    every box loaded into an LDS image and stored back, full passes over the
-    8192-box grid until min_seconds have elapsed."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
+    except OSError:
+        return "unknown"
+
+
+def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 8, max_threads: int = 16):
+    """The oracle (plain single-threaded C, as it stands) doing the same work
+    on the host, timed beside the GPU:
+
+    - the round trip: every box of the 8192-box grid loaded into an LDS image
+      and stored back, full passes until min_seconds have elapsed, first on
+      one thread, then split by boxes over the host's cores (threads calling
+      the oracle on disjoint box ranges; the C calls release the GIL);
+    - the GEMM sample: 4096 sampled outputs of the 8192^3 bf16 product as
+      float64 dot products (2 * 4096 * 8192 flop), on one thread and split by
+      samples over the same threads; the full product's CPU time is only
+      extrapolated from that rate."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import oracle
     import synthgen
+    from synthgen import workloads as W
 
     src = synthgen.u16_bits(2, (8192, 8192))
     dst = np.zeros_like(src)
     m = oracle.Map("bf16", (8192, 8192), (16384,), (64, 128), swizzle="128b")
     coords = np.array([[64 * (t % 128), 128 * (t // 128)] for t in range(8192)], dtype=np.int32)
+
+    def boxes(b0, b1):
+        for a in range(b0, b1, 256):
+            e = min(b1, a + 256)
+            m.store(dst, coords[a:e], m.load(src, coords[a:e]))
+
     passes, t0 = 0, time.perf_counter()
     while passes < max_passes:
-        for b0 in range(0, 8192, 512):
-            img = m.load(src, coords[b0:b0 + 512])
-            m.store(dst, coords[b0:b0 + 512], img)
+        boxes(0, 8192)
         passes += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
-    dt = time.perf_counter() - t0
+    dt1 = time.perf_counter() - t0
     ok = bool(np.array_equal(dst, src))
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
-    except OSError:
-        pass
-    return {"value": round(passes * BYTES_PER_STEP / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "verified": ok, "cpu_model": cpu,
+
+    avail = len(os.sched_getaffinity(0))
+    threads = max(1, min(avail, max_threads))
+    dst[...] = 0
+    per = (8192 + threads - 1) // threads
+    passes_mt, t0 = 0, time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        while passes_mt < 4 * max_passes:
+            list(ex.map(lambda w: boxes(w * per, min(8192, (w + 1) * per)), range(threads)))
+            passes_mt += 1
+            if time.perf_counter() - t0 >= min_seconds / 2:
+                break
+    dtm = time.perf_counter() - t0
+    ok = ok and bool(np.array_equal(dst, src))
+
+    ex_g = W.GEMM_8192
+    M, N, K = ex_g["M"], ex_g["N"], ex_g["K"]
+    A = synthgen.normal_bf16_bits(ex_g["seed"] * 1000 + 1, (M, K))
+    Bt = synthgen.normal_bf16_bits(ex_g["seed"] * 1000 + 2, (N, K))
+    rows, cols = synthgen.sample_pairs(ex_g["seed"] * 1000 + 3, ex_g["nsample"], M, N)
+    flop = 2.0 * len(rows) * K
+    t0 = time.perf_counter()
+    ref1 = oracle.gemm_bf16_sample(A, Bt, K, rows, cols)
+    g1 = time.perf_counter() - t0
+    parts = np.array_split(np.arange(len(rows)), threads)
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        refs = list(ex.map(lambda ix: oracle.gemm_bf16_sample(A, Bt, K, rows[ix], cols[ix]), parts))
+    gm = time.perf_counter() - t0
+    ok = ok and bool(np.array_equal(np.concatenate(refs), ref1))
+    gflops_mt = flop / gm / 1e9
+    return {"value": round(passes * BYTES_PER_STEP / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "verified": ok, "cpu_model": cpu_model(),
             "sample": f"{passes} full pass(es) of the 8192-box bf16 8192x8192 round trip "
-                      f"(load to LDS image + store), {dt:.1f} s on one host thread"}
+                      f"(load to LDS image + store), {dt1:.1f} s on one host thread",
+            "all_cores": {"value": round(passes_mt * BYTES_PER_STEP / dtm / 1e9, 4), "unit": "GB/s",
+                          "cores": threads, "cores_available": avail,
+                          "sample": f"{passes_mt} full pass(es) of the same round trip, boxes split over "
+                                    f"{threads} threads, {dtm:.1f} s"},
+            "gemm_sample": {"what": "4096 sampled outputs of the bf16 8192^3 GEMM as float64 dot products "
+                                    "(the oracle's GEMM check)",
+                            "GFLOPs_1_thread": round(flop / g1 / 1e9, 3),
+                            "GFLOPs_all_cores": round(gflops_mt, 3), "cores": threads,
+                            "full_gemm_seconds_extrapolated": round(2.0 * M * N * K / (gflops_mt * 1e9), 1)}}
 
 
 def run_extra(att, torch, stream, reps: int):
@@ -297,7 +354,7 @@ def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int 
     return out
 
 
-def hbm_ceiling(att, torch, stream, reps: int = 100):
+def hbm_ceiling(att, torch, stream, reps: int = 100, sweep: bool = True):
     """What plain streaming kernels (the library's hbm_probe: coalesced
     16-byte loads, non-temporal 16-byte stores) reach on this GPU's HBM with
     the same 128 MiB working sets, 4 rotating buffers so the last-level cache
@@ -323,9 +380,31 @@ def hbm_ceiling(att, torch, stream, reps: int = 100):
     w = timed(lambda k: att.hbm_probe("write", None, outs[k % 4], n, stream))
     c = timed(lambda k: att.hbm_probe("copy", bufs[k % 4], outs[k % 4], n, stream))
     ok = all(torch.equal(a, b) for a, b in zip(bufs, outs))
-    return {"read_only_GBps": round(n / r / 1e6, 1), "write_only_GBps": round(n / w / 1e6, 1),
-            "copy_GBps": round(2 * n / c / 1e6, 1), "copy_verified": ok, "bytes_per_buffer": n,
-            "what": "hbm_probe read / write / copy over 4 rotating 128 MiB buffers"}
+    out = {"read_only_GBps": round(n / r / 1e6, 1), "write_only_GBps": round(n / w / 1e6, 1),
+           "copy_GBps": round(2 * n / c / 1e6, 1), "copy_verified": ok, "bytes_per_buffer": n,
+           "what": "hbm_probe read / write / copy over 4 rotating 128 MiB buffers"}
+    if sweep:
+        # the best plain copy this GPU runs: every launch shape of
+        # hbm_probe_copy_ex (vectors per thread, store kind, order) at 1 to
+        # 16 workgroups per CU; the best is checked for correctness
+        best = None
+        for variant in range(16):
+            for wpc in (1, 2, 4, 8, 16):
+                t = timed(lambda k, v=variant, g=wpc: att.hbm_probe_copy_ex(bufs[k % 4], outs[k % 4], n, v, g,
+                                                                            stream))
+                if best is None or t < best[0]:
+                    best = (t, variant, wpc)
+        for o in outs:
+            o.zero_()
+        for k in range(4):
+            att.hbm_probe_copy_ex(bufs[k], outs[k], n, best[1], best[2], stream)
+        ok2 = all(torch.equal(a, b) for a, b in zip(bufs, outs))
+        u = 1 << (best[1] & 3)
+        out["copy_sweep_best"] = {"GBps": round(2 * n / best[0] / 1e6, 1), "verified": ok2,
+                                  "vectors_per_thread": u, "nontemporal_stores": bool(best[1] & 4),
+                                  "order": "slice per workgroup" if best[1] & 8 else "grid-stride",
+                                  "workgroups_per_cu": best[2], "configs": 80}
+    return out
 
 
 def main():
@@ -495,6 +574,8 @@ def main():
         ceil = hbm_ceiling(att, torch, stream)
         result["hbm_ceiling"] = ceil
         result["frac_of_linear_copy"] = round(gbs / ceil["copy_GBps"], 4)
+        best_copy = max(ceil["copy_GBps"], ceil.get("copy_sweep_best", {}).get("GBps", 0.0))
+        result["frac_of_best_plain_copy"] = round(gbs / best_copy, 4)
     if not args.no_extra:
         result["extra"] = run_extra(att, torch, stream, 20)
     if not args.no_cpu_baseline:

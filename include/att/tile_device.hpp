@@ -614,27 +614,52 @@ __device__ __forceinline__ uint32_t tile_store_issue(const TmapImpl& m, const in
             const uint32_t cpr = m.cpr;                                         // chunks per box row
             const uint32_t nrow = nchunk / cpr;
             const uint32_t nwd = nrow * wpr;
-            for (uint32_t w0 = wave * 64u; w0 < nwd; w0 += nwaves * 64u) {
-                const uint32_t W = w0 + lane;
-                if (W >= nwd) continue;
-                const uint32_t row = W / wpr, wi = W % wpr;
-                const uint32_t q_row = row * cpr;
-                const ChunkLoc L = chunk_locate(m, c, q_row);
-                if (!L.rest_in) continue;
-                const int64_t g = (w_first + (int64_t)wi) * (int64_t)epw;      // first element of the word
-                uint32_t inb = 0, vw = 0;
-                for (uint32_t h = 0; h < epw; ++h) {
-                    const int64_t gg = g + (int64_t)h;
-                    const int64_t e = gg - c0;                                 // box element in the row
-                    if (e < 0 || e >= (int64_t)L0 || gg < 0 || gg >= m.dim[0]) continue;
-                    const uint32_t eb = (uint32_t)e * esz;
-                    const uint8_t* src = lds + swz_chunk(q_row + (eb >> 4), m.swizzle) * 16u + (eb & 15u);
-                    const uint32_t v = esz == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(src) : (uint32_t)*src;
-                    vw |= v << (h * esz * 8u);
-                    inb |= 1u << h;
+            // WB words per lane per step: their LDS reads, then their atomics,
+            // are in flight together (the packed adds return the old value,
+            // which is only looked at after all of them have been issued).
+            // With a word-aligned origin a word's elements sit in one 16-byte
+            // chunk and are read from LDS as one 32-bit word.
+            constexpr uint32_t WB = 4;
+            const bool two_d = m.rank <= 2;
+            for (uint32_t w0 = wave * 64u * WB; w0 < nwd; w0 += nwaves * 64u * WB) {
+                ATT_GLOBAL uint32_t* wp[WB];
+                uint32_t vw[WB], inb[WB];
+#pragma unroll
+                for (uint32_t b = 0; b < WB; ++b) {
+                    const uint32_t W = w0 + b * 64u + lane;
+                    wp[b] = nullptr;
+                    vw[b] = 0;
+                    inb[b] = 0;
+                    if (W >= nwd) continue;
+                    const uint32_t row = W / wpr, wi = W - row * wpr;
+                    const uint32_t q_row = row * cpr;
+                    const ChunkLoc L = two_d ? chunk_locate_2d(m, c, q_row) : chunk_locate(m, c, q_row);
+                    if (!L.rest_in) continue;
+                    const int64_t g = (w_first + (int64_t)wi) * (int64_t)epw;  // first element of the word
+                    uint32_t whole = 0;
+                    if (head == 0) {
+                        const uint32_t eb = (uint32_t)(g - c0) * esz;
+                        whole = *reinterpret_cast<const uint32_t*>(lds + swz_chunk(q_row + (eb >> 4), m.swizzle) * 16u +
+                                                                   (eb & 15u));
+                    }
+                    for (uint32_t h = 0; h < epw; ++h) {
+                        const int64_t gg = g + (int64_t)h;
+                        const int64_t e = gg - c0;                             // box element in the row
+                        if (e < 0 || e >= (int64_t)L0 || gg < 0 || gg >= m.dim[0]) continue;
+                        uint32_t v;
+                        if (head == 0) {
+                            v = (whole >> (h * esz * 8u)) & (esz == 2 ? 0xFFFFu : 0xFFu);
+                        } else {
+                            const uint32_t eb = (uint32_t)e * esz;
+                            const uint8_t* src = lds + swz_chunk(q_row + (eb >> 4), m.swizzle) * 16u + (eb & 15u);
+                            v = esz == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(src) : (uint32_t)*src;
+                        }
+                        vw[b] |= v << (h * esz * 8u);
+                        inb[b] |= 1u << h;
+                    }
+                    if (inb[b])
+                        wp[b] = (ATT_GLOBAL uint32_t*)(gptr(m.base + (uint64_t)L.rest_off) + g * (int64_t)esz);
                 }
-                if (!inb) continue;
-                ATT_GLOBAL uint32_t* wp = (ATT_GLOBAL uint32_t*)(gptr(m.base + (uint64_t)L.rest_off) + g * (int64_t)esz);
                 if constexpr (OP == ST_ADD) {
                     // both halves inside: the packed hardware add, which
                     // rounds the exact sum once to nearest even like the
@@ -643,17 +668,33 @@ __device__ __forceinline__ uint32_t tile_store_issue(const TmapImpl& m, const in
                     // or gets a sign there; the old value it returns tells
                     // when that happened, and the word's NaN halves are then
                     // set to the canonical NaN.
-                    if (inb == 3u && (m.dtype == TMAP_BF16 || m.dtype == TMAP_F16)) {
+                    if (m.dtype == TMAP_BF16 || m.dtype == TMAP_F16) {
                         const bool bf = m.dtype == TMAP_BF16;
-                        const uint32_t old = bf ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2bf16(
-                                                                                  (ATT_GLOBAL bf16x2_t*)wp, __builtin_bit_cast(bf16x2_t, vw)))
-                                                : __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2f16(
-                                                                                  (ATT_GLOBAL f16x2_t*)wp, __builtin_bit_cast(f16x2_t, vw)));
-                        if (half_sum_nan(bf, old, vw) || half_sum_nan(bf, old >> 16, vw >> 16)) canon_nan_word(bf, wp);
+                        uint32_t old[WB];
+#pragma unroll
+                        for (uint32_t b = 0; b < WB; ++b) {
+                            old[b] = 0;
+                            if (inb[b] != 3u) continue;
+                            old[b] = bf ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2bf16(
+                                                                           (ATT_GLOBAL bf16x2_t*)wp[b], __builtin_bit_cast(bf16x2_t, vw[b])))
+                                        : __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2f16(
+                                                                           (ATT_GLOBAL f16x2_t*)wp[b], __builtin_bit_cast(f16x2_t, vw[b])));
+                        }
+#pragma unroll
+                        for (uint32_t b = 0; b < WB; ++b) {
+                            if (inb[b] == 3u) {
+                                if (half_sum_nan(bf, old[b], vw[b]) || half_sum_nan(bf, old[b] >> 16, vw[b] >> 16))
+                                    canon_nan_word(bf, wp[b]);
+                            } else if (inb[b]) {
+                                reduce_word<OP>(m.dtype, esz, wp[b], vw[b], inb[b]);
+                            }
+                        }
                         continue;
                     }
                 }
-                reduce_word<OP>(m.dtype, esz, wp, vw, inb);
+#pragma unroll
+                for (uint32_t b = 0; b < WB; ++b)
+                    if (inb[b]) reduce_word<OP>(m.dtype, esz, wp[b], vw[b], inb[b]);
             }
             wait_lgkm0();
             return 0;

@@ -261,8 +261,15 @@ tmap_status tile_copy(const tmap_t* src, const tmap_t* dst, uint32_t stages, voi
  * variant bits, for tuning sweeps: 1 non-temporal stores, 2 force the
  * generic one-workgroup-per-box path, 4 workgroups own contiguous box
  * ranges (else strided), 8 XCD-aware workgroup numbering, bits 4..5 boxes
- * per ring stage (1, 2, 4, 8).  tile_copy uses 1|4 with two boxes per
- * workgroup.  Ring depths 5 and 7 take the generic path. */
+ * per ring stage (1, 2, 4, 8), 64 batch mode: each workgroup owns `stages`
+ * (2..4) consecutive boxes, one LDS stage each, loads all of them, reads
+ * each stage once its copies have landed and stores them all at the end
+ * (grid ignored; the box count must divide by `stages`), 128 with 64: the
+ * workgroup's boxes are neighbours in dim 0 and each wave issues its first
+ * copy of every box, then its second, ... (back-to-back requests cover the
+ * same rows several boxes wide).  tile_copy uses
+ * 1|4 with two boxes per workgroup.  Ring depths 5 and 7 take the generic
+ * path. */
 tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32_t stages,
                          uint32_t grid, uint32_t variant, void* stream);
 
@@ -334,6 +341,32 @@ tmap_status lds_bank_probe(int32_t layout, uint32_t iters, int32_t* d_hist, void
  * Errors: NULL, ALIGN, UNSUPPORTED (kind, bytes not a multiple of 16), HIP.
  * bytes == 0 is a no-op. */
 tmap_status hbm_probe(int32_t kind, const void* d_src, void* d_dst, uint64_t bytes, void* stream);
+
+/* The copy of hbm_probe in other launch shapes, for a sweep that finds the
+ * best plain copy this GPU runs (the measured ceiling reported beside the
+ * tile copy): variant bits 0..1 select 1, 2, 4 or 8 16-byte vectors per
+ * thread and step, bit 2 non-temporal stores, bit 3 one contiguous slice per
+ * workgroup (else grid-stride order); wg_per_cu 1..32 workgroups of 256
+ * threads per CU (fewer if the data needs fewer).  Pointers and errors as
+ * hbm_probe (kind 2); variant > 15 or wg_per_cu outside 1..32 is
+ * UNSUPPORTED. */
+tmap_status hbm_probe_copy_ex(const void* d_src, void* d_dst, uint64_t bytes, uint32_t variant,
+                              uint32_t wg_per_cu, void* stream);
+
+/* Box-shaped copy without LDS (a measurement aid): copies a row-major byte
+ * matrix of `height` rows of `width` bytes (both multiples of 128) in boxes
+ * of 128 rows x 128 bytes with the tile copy's access shape -- each wave
+ * instruction moves 8 rows x 128 bytes of one box -- through registers,
+ * `boxes_per_wg` (1, 2, 4, 8; dividing width / 128) neighbouring boxes per
+ * 256-thread workgroup, all loads of a workgroup before its stores.  variant
+ * bit 0 non-temporal stores, bit 1 XCD-contiguous workgroup numbering (the
+ * workgroup count must divide by 8), bit 2 box-major instead of row-group-
+ * major issue, bits 3..4 = k > 0: reserve 16 KiB << (k - 1) of LDS per
+ * workgroup (unused; it bounds the workgroups per CU as the tile copy's
+ * stages do).  Shows what the box shape costs apart from the LDS staging.
+ * Errors: NULL, ALIGN (16 bytes), UNSUPPORTED (shape, variant > 31), HIP. */
+tmap_status hbm_probe_box_copy(const void* d_src, void* d_dst, uint32_t width, uint32_t height,
+                               uint32_t boxes_per_wg, uint32_t variant, void* stream);
 
 /* Consumer: bf16 GEMM mainloop C = A * B ([MLC] overview and "TMA in a
  * pipeline"; [H200] section 02 result).  A is M x K row-major (map dims

@@ -29,3 +29,17 @@ def read_table(name):
 @pytest.fixture(scope="session")
 def table():
     return read_table
+
+
+@pytest.fixture(autouse=True)
+def _device_status_clean(request):
+    """After every GPU test: no batch kernel recorded a barrier wait that gave
+    up, nor (debug build) a failed device check.  Tests that force one read
+    and clear the record themselves."""
+    yield
+    if request.node.get_closest_marker("gpu") is None:
+        return
+    import async_tensor_tile_amd as att
+    if att._lib is None:
+        return
+    att.tile_device_status(0)

@@ -136,6 +136,18 @@ def test_launch_argument_errors_without_gpu():
     assert ei.value.name == "ERR_NULL"
     # hbm_probe: argument checks come before any HIP call
     att.hbm_probe("copy", BASE, BASE, 0)
+    att.hbm_probe_copy_ex(BASE, BASE, 0, 15, 1)
+    for args, name in (((BASE, BASE, 16, 16, 1), "ERR_UNSUPPORTED"), ((BASE, BASE, 16, 0, 0), "ERR_UNSUPPORTED"),
+                       ((BASE, BASE, 16, 0, 33), "ERR_UNSUPPORTED"), ((BASE, BASE, 24, 0, 1), "ERR_UNSUPPORTED"),
+                       ((0, BASE, 16, 0, 1), "ERR_NULL"), ((BASE, BASE + 8, 16, 0, 1), "ERR_ALIGN")):
+        with pytest.raises(att.TmapError) as ei:
+            att.hbm_probe_copy_ex(*args)
+        assert ei.value.name == name, args
+    # txbar_selftest_ex: poll bound and extra bytes are checked on the host
+    m = att.tmap_encode("bf16", 2, BASE, (64, 64), (128,), (64, 16), None, "128b")
+    with pytest.raises(att.TmapError) as ei:
+        att.txbar_selftest_ex(m, 0, 1, 0, 1, BASE, BASE)
+    assert ei.value.name == "ERR_NULL"
     for args, name in ((("copy", BASE, BASE, 17), "ERR_UNSUPPORTED"), ((3, BASE, BASE, 16), "ERR_UNSUPPORTED"),
                        (("copy", 0, BASE, 16), "ERR_NULL"), (("write", 0, 0, 16), "ERR_NULL"),
                        (("read", BASE, BASE + 8, 16), "ERR_ALIGN")):

@@ -42,7 +42,8 @@ def _copy_case(dims, box, swizzle, stages, variant=0, grid=0, seed=2):
     return src, sd, dd, ms, same
 
 
-@pytest.mark.parametrize("stages,variant", [(2, 0), (1, 0), (3, 0), (4, 0), (2, 1), (2, 2)])
+@pytest.mark.parametrize("stages,variant", [(2, 0), (1, 0), (3, 0), (4, 0), (2, 1), (2, 2), (2, 65), (3, 65), (4, 73),
+                                            (2, 64), (4, 201), (2, 193), (3, 193), (2, 321), (4, 457)])
 def test_copy_8192_round_trip(stages, variant):
     ex = W.COPY_8192
     say("copy 8192^2 stages", stages, "variant", variant)
@@ -106,6 +107,12 @@ def test_copy_random_maps(seed):
     stages = int(g.choice([1, 2, 3, 4, 5, 6, 8]))
     variant = int(g.integers(0, 64))
     grid = int(g.choice([0, 0, 1, 3, 64, 1000]))
+    if g.integers(0, 2):
+        variant |= 64                      # batch mode (where the box count and depth allow it)
+    if g.integers(0, 2):
+        variant |= 128                     # row-group-major issue in batch mode
+    if g.integers(0, 2):
+        variant |= 256                     # batch mode through registers instead of the LDS-DMA
     say("copy random", seed, c.dtype, c.dims, c.box, c.swizzle, stages, variant, grid)
     sd = to_dev(c.buf)
     dd = empty_dev(c.buf.size, 0x5A)

@@ -35,3 +35,34 @@ def test_probe_copy_write_read(nbytes):
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     att.hbm_probe("read", src, sink, nbytes, stream())
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 22) + 16 * 333])
+def test_probe_copy_variants(nbytes):
+    """Every launch shape of the ceiling sweep copies exactly the requested
+    bytes (ragged sizes, every vector count, store kind and order, 1 to 16
+    workgroups per CU)."""
+    print("hbm_probe_copy_ex", nbytes, flush=True)
+    rng = np.random.default_rng(nbytes + 1)
+    src = torch.from_numpy(rng.integers(0, 256, nbytes + 64, dtype=np.uint8)).cuda()
+    for variant in range(16):
+        for wpc in (1, 2, 16):
+            dst = torch.full((nbytes + 64,), 0xEE, dtype=torch.uint8, device="cuda")
+            att.hbm_probe_copy_ex(src, dst, nbytes, variant, wpc, stream())
+            torch.cuda.synchronize()
+            assert torch.equal(dst[:nbytes], src[:nbytes]), (variant, wpc)
+            assert (dst[nbytes:] == 0xEE).all(), (variant, wpc)
+
+
+def test_probe_box_copy_variants():
+    """The box-shaped register copy moves every byte of the matrix for every
+    boxes-per-workgroup count and variant."""
+    W_, H_ = 4096, 512
+    rng = np.random.default_rng(7)
+    src = torch.from_numpy(rng.integers(0, 256, W_ * H_, dtype=np.uint8)).cuda()
+    for nbx in (1, 2, 4, 8):
+        for variant in range(8):
+            dst = torch.zeros_like(src)
+            att.hbm_probe_box_copy(src, dst, W_, H_, nbx, variant, stream())
+            torch.cuda.synchronize()
+            assert torch.equal(dst, src), (nbx, variant)
