@@ -528,16 +528,38 @@ __device__ __forceinline__ bool half_sum_nan(bool bf, uint32_t a, uint32_t b) {
     return ma > inf || mb > inf || (ma == inf && mb == inf && ((a ^ b) & 0x8000u));
 }
 
-// Every NaN half of the word becomes the canonical quiet NaN (the other
-// half is left as it is, whatever concurrent updates do to it).
-__device__ __forceinline__ void canon_nan_word(bool bf, ATT_GLOBAL uint32_t* w) {
+// The halves of the word selected by `halves` (bit 0 low, bit 1 high) that
+// hold a NaN become the canonical quiet NaN; the rest of the word is left
+// as it is, whatever concurrent updates do to it.
+__device__ __forceinline__ void canon_nan_halves(bool bf, ATT_GLOBAL uint32_t* w, uint32_t halves) {
     const uint32_t inf = bf ? 0x7F80u : 0x7C00u, canon = bf ? 0x7FC0u : 0x7E00u;
     uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     while (true) {
         uint32_t nw = old;
-        if ((old & 0x7FFFu) > inf) nw = (nw & 0xFFFF0000u) | canon;
-        if (((old >> 16) & 0x7FFFu) > inf) nw = (nw & 0x0000FFFFu) | (canon << 16);
+        if ((halves & 1u) && (old & 0x7FFFu) > inf) nw = (nw & 0xFFFF0000u) | canon;
+        if ((halves & 2u) && ((old >> 16) & 0x7FFFu) > inf) nw = (nw & 0x0000FFFFu) | (canon << 16);
         if (nw == old) return;
+        if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return;
+    }
+}
+
+// The packed adds quiet a signalling NaN and return every other value of a
+// half they add -0 to unchanged.  A half outside the box that held a
+// signalling NaN `orig` is put back, unless it no longer holds the quieted
+// value (another reduction into that element has changed it since, and its
+// result stands).
+__device__ __forceinline__ bool half_is_snan(bool bf, uint32_t h) {
+    return bf ? ((h & 0x7F80u) == 0x7F80u && (h & 0x7Fu) != 0 && !(h & 0x40u))
+              : ((h & 0x7C00u) == 0x7C00u && (h & 0x3FFu) != 0 && !(h & 0x200u));
+}
+
+__device__ __forceinline__ void restore_half(bool bf, ATT_GLOBAL uint32_t* w, uint32_t shift, uint32_t orig) {
+    const uint32_t quieted = orig | (bf ? 0x40u : 0x200u);
+    uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (((old >> shift) & 0xFFFFu) == quieted) {
+        const uint32_t nw = (old & ~(0xFFFFu << shift)) | (orig << shift);
         if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT))
             return;
@@ -661,33 +683,37 @@ __device__ __forceinline__ uint32_t tile_store_issue(const TmapImpl& m, const in
                         wp[b] = (ATT_GLOBAL uint32_t*)(gptr(m.base + (uint64_t)L.rest_off) + g * (int64_t)esz);
                 }
                 if constexpr (OP == ST_ADD) {
-                    // both halves inside: the packed hardware add, which
-                    // rounds the exact sum once to nearest even like the
-                    // f32-then-round definition (f32 carries more than
-                    // 2p + 2 bits).  A NaN result keeps an operand's payload
-                    // or gets a sign there; the old value it returns tells
-                    // when that happened, and the word's NaN halves are then
-                    // set to the canonical NaN.
+                    // The packed hardware add, which rounds the exact sum
+                    // once to nearest even like the f32-then-round
+                    // definition (f32 carries more than 2p + 2 bits); a half
+                    // outside the box (a word cut by the box row's ends)
+                    // gets -0 added, which leaves it as it was.  A NaN sum
+                    // keeps an operand's payload or sign there; the old
+                    // value the add returns tells when that happened, and
+                    // that half is then set to the canonical NaN.  It also
+                    // tells whether a half outside the box held a
+                    // signalling NaN (the add quiets it), to put it back.
                     if (m.dtype == TMAP_BF16 || m.dtype == TMAP_F16) {
                         const bool bf = m.dtype == TMAP_BF16;
                         uint32_t old[WB];
 #pragma unroll
                         for (uint32_t b = 0; b < WB; ++b) {
                             old[b] = 0;
-                            if (inb[b] != 3u) continue;
+                            if (!inb[b]) continue;
+                            const uint32_t v = vw[b] | ((inb[b] & 1u) ? 0u : 0x8000u) | ((inb[b] & 2u) ? 0u : 0x80000000u);
                             old[b] = bf ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2bf16(
-                                                                           (ATT_GLOBAL bf16x2_t*)wp[b], __builtin_bit_cast(bf16x2_t, vw[b])))
+                                                                           (ATT_GLOBAL bf16x2_t*)wp[b], __builtin_bit_cast(bf16x2_t, v)))
                                         : __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2f16(
-                                                                           (ATT_GLOBAL f16x2_t*)wp[b], __builtin_bit_cast(f16x2_t, vw[b])));
+                                                                           (ATT_GLOBAL f16x2_t*)wp[b], __builtin_bit_cast(f16x2_t, v)));
                         }
 #pragma unroll
                         for (uint32_t b = 0; b < WB; ++b) {
-                            if (inb[b] == 3u) {
-                                if (half_sum_nan(bf, old[b], vw[b]) || half_sum_nan(bf, old[b] >> 16, vw[b] >> 16))
-                                    canon_nan_word(bf, wp[b]);
-                            } else if (inb[b]) {
-                                reduce_word<OP>(m.dtype, esz, wp[b], vw[b], inb[b]);
-                            }
+                            if (!inb[b]) continue;
+                            const uint32_t nan = ((inb[b] & 1u) && half_sum_nan(bf, old[b], vw[b]) ? 1u : 0u) |
+                                                 ((inb[b] & 2u) && half_sum_nan(bf, old[b] >> 16, vw[b] >> 16) ? 2u : 0u);
+                            if (nan) canon_nan_halves(bf, wp[b], nan);
+                            if (inb[b] == 1u && half_is_snan(bf, old[b] >> 16)) restore_half(bf, wp[b], 16u, old[b] >> 16);
+                            if (inb[b] == 2u && half_is_snan(bf, old[b] & 0xFFFFu)) restore_half(bf, wp[b], 0u, old[b] & 0xFFFFu);
                         }
                         continue;
                     }

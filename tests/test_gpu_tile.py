@@ -311,6 +311,29 @@ def test_half_reduce_special_values_exact(dtype, layout):
     np.testing.assert_array_equal(to_host(acc), hw)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_half_reduce_odd_origins_keep_neighbours(dtype):
+    """16-bit reduce-add at odd origins: the words at each box row's ends
+    take the packed add with -0 in the half outside the box.  Every element
+    outside the boxes holds a signalling NaN, a quiet non-canonical NaN, -0
+    or a subnormal, and must keep its bits; inside, bit-exact against the
+    oracle."""
+    dims, strides, box = (133, 16), (288,), (32, 8)
+    g = synthgen.rng(43)
+    snan, qnan = (0x7F81, 0xFFC3) if dtype == "bf16" else (0x7C01, 0xFE03)
+    pats = np.array([snan, qnan, 0x8000, 0x0001], dtype=np.uint16)
+    dst0 = pats[g.integers(0, 4, strides[0] * dims[1] // 2)]
+    imgs = synthgen.normal_bf16_bits(44, (8, 32 * 8)) if dtype == "bf16" else \
+        g.standard_normal((8, 32 * 8)).astype(np.float16).view(np.uint16)
+    coords = np.array([[1, 0], [35, 0], [69, 0], [101, 0], [-3, 8], [33, 8], [67, 8], [103, 8]], dtype=np.int32)
+    acc = to_dev(dst0)
+    m = encode(acc, dtype, dims, strides, box)
+    att.tile_reduce_add(m, to_dev(coords), 8, to_dev(imgs), stream())
+    hw = dst0.view(np.uint8).copy()
+    oracle.Map(dtype, dims, strides, box).reduce_add(hw, coords, imgs.view(np.uint8))
+    np.testing.assert_array_equal(to_host(acc).view(np.uint16), hw.view(np.uint16))
+
+
 def _float_class_mix(dtype, n, seed):
     """n f32 / f64 bit patterns, each drawn from one of thirteen classes
     picked uniformly: random bits, +0, -0, subnormals, the smallest normal,
