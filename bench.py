@@ -404,6 +404,110 @@ def hbm_ceiling(att, torch, stream, reps: int = 100, sweep: bool = True):
                                   "vectors_per_thread": u, "nontemporal_stores": bool(best[1] & 4),
                                   "order": "slice per workgroup" if best[1] & 8 else "grid-stride",
                                   "workgroups_per_cu": best[2], "configs": 80}
+        # the same bytes in the tile copy's access shape (8 rows x 128 bytes
+        # of one 128 x 128-byte box per wave instruction) through registers:
+        # what the box shape itself allows, apart from the LDS staging
+        bbest = None
+        for nbx in (1, 2, 4, 8):
+            for variant in range(8):
+                t = timed(lambda k, v=variant, b=nbx: att.hbm_probe_box_copy(bufs[k % 4], outs[k % 4], 16384, 8192, b,
+                                                                             v, stream))
+                if bbest is None or t < bbest[0]:
+                    bbest = (t, nbx, variant)
+        for o in outs:
+            o.zero_()
+        for k in range(4):
+            att.hbm_probe_box_copy(bufs[k], outs[k], 16384, 8192, bbest[1], bbest[2], stream)
+        ok3 = all(torch.equal(a, b) for a, b in zip(bufs, outs))
+        out["box_copy_sweep_best"] = {"GBps": round(2 * n / bbest[0] / 1e6, 1), "verified": ok3,
+                                      "boxes_per_workgroup": bbest[1], "nontemporal_stores": bool(bbest[2] & 1),
+                                      "xcd_contiguous": bool(bbest[2] & 2),
+                                      "issue": "box-major" if bbest[2] & 4 else "row-group-major", "configs": 32,
+                                      "what": "register copy with the tile copy's access shape: one 16-byte "
+                                              "vector per lane, 8 rows x 128 bytes of a 128 x 128-byte box "
+                                              "per wave instruction"}
+    return out
+
+
+def run_copy_compare(att, torch, stream, reps: int = 20, rounds: int = 3):
+    """The tile copy beside the plain copies it is measured against, on the
+    same four rotating 128 MiB pairs, for counter runs: per round, `reps`
+    dispatches each of the default tile copy, the best plain copy of the
+    sweep (16-byte vectors, non-temporal stores, grid-stride, 4 workgroups
+    per CU), the register copy in the tile copy's access shape (2 boxes per
+    workgroup, non-temporal stores) and the default hbm_probe copy, in that
+    order.  Returns the median GB/s of each over the rounds."""
+    import numpy as np
+
+    import synthgen
+    from synthgen import workloads as W
+
+    ex = W.COPY_8192
+    n = 8192 * 8192 * 2
+    src_host = torch.from_numpy(synthgen.u16_bits(ex["seed"], (8192, 8192)).view(np.uint8).reshape(-1))
+    pairs = []
+    for _ in range(4):
+        a = src_host.to("cuda")
+        b = torch.empty_like(a)
+        ma = att.tmap_encode("bf16", 2, a.data_ptr(), ex["dims"], ex["strides"], ex["box"], None, ex["swizzle"])
+        mb = att.tmap_encode("bf16", 2, b.data_ptr(), ex["dims"], ex["strides"], ex["box"], None, ex["swizzle"])
+        pairs.append((a, b, ma, mb))
+    kinds = {
+        "tile_copy": lambda a, b, ma, mb: att.tile_copy(ma, mb, 2, stream),
+        "plain_copy_best": lambda a, b, ma, mb: att.hbm_probe_copy_ex(a, b, n, 4, 4, stream),
+        "box_shaped_register_copy": lambda a, b, ma, mb: att.hbm_probe_box_copy(a, b, 16384, 8192, 2, 1, stream),
+        "hbm_probe_copy": lambda a, b, ma, mb: att.hbm_probe("copy", a, b, n, stream),
+    }
+    times = {k: [] for k in kinds}
+    for _ in range(rounds):
+        for key, fn in kinds.items():
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for k in range(reps):
+                fn(*pairs[k % 4])
+            e.record()
+            torch.cuda.synchronize()
+            times[key].append(s.elapsed_time(e) / reps)
+    ok = all(torch.equal(a, b) for a, b, _, _ in pairs)
+    return {"order": list(kinds), "rounds": rounds, "dispatches_per_kind_and_round": reps, "verified": ok,
+            "GBps_median": {k: round(2 * n / sorted(t)[len(t) // 2] / 1e6, 1) for k, t in times.items()}}
+
+
+def run_reduce_compare(att, torch, stream, reps: int = 10):
+    """The reduce-add pass of 1024 boxes of 64 x 64 into a 4096 x 4096
+    destination in int32 and then in bf16, `reps` dispatches each (in that
+    order, for counter runs); algorithmic bytes 3 x box bytes per box."""
+    import numpy as np
+
+    import synthgen
+    from synthgen import workloads as W
+
+    ex = W.REDUCE_4096
+    rc = torch.from_numpy(synthgen.uniform_coords(ex["seed"] * 1000 + 10, ex["nbox"], (0, 0), (4032, 4032))).cuda()
+    dst = torch.from_numpy(synthgen.int32_range(ex["seed"], (4096, 4096), -(1 << 20), 1 << 20)).cuda()
+    src = torch.from_numpy(synthgen.int32_range(ex["seed"] * 1000 + 20, (ex["nbox"], 64, 64), -(1 << 20),
+                                                1 << 20)).cuda()
+    mi = att.tmap_encode("i32", 2, dst.data_ptr(), ex["dims"], ex["strides"], ex["box"], None, "none")
+    d16 = torch.from_numpy(synthgen.normal_bf16_bits(ex["seed"], (4096, 4096)).view(np.int16)).cuda()
+    s16 = torch.from_numpy(synthgen.normal_bf16_bits(ex["seed"] * 1000 + 21, (ex["nbox"], 64, 64))
+                           .view(np.int16)).cuda()
+    mb = att.tmap_encode("bf16", 2, d16.data_ptr(), ex["dims"], (8192,), ex["box"], None, "none")
+    out = {}
+    for key, fn, box_bytes in (("int32", lambda: att.tile_reduce_add(mi, rc.data_ptr(), ex["nbox"], src.data_ptr(),
+                                                                      stream), 16384),
+                               ("bf16", lambda: att.tile_reduce(mb, "add", rc.data_ptr(), ex["nbox"], s16.data_ptr(),
+                                                                stream), 8192)):
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        out[key] = {"us": round(ms * 1e3, 2), "GBps_algorithmic": round(ex["nbox"] * box_bytes * 3 / ms / 1e6, 1)}
+    out["bf16_per_byte_vs_int32"] = round(out["int32"]["GBps_algorithmic"] / out["bf16"]["GBps_algorithmic"], 3)
     return out
 
 
@@ -419,9 +523,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (rank-5 load, reduce-add pass, GEMM 8192^3)")
-    ap.add_argument("--only", choices=["copy", "gemm", "gemm-raster", "lds-probe"], default="copy",
+    ap.add_argument("--only", choices=["copy", "gemm", "gemm-raster", "lds-probe", "copy-compare", "reduce"],
+                    default="copy",
                     help="gemm: time only the GEMM mainloop; gemm-raster: the default GEMM under each tile "
-                         "rasterisation; lds-probe: run the LDS bank probe layouts (profiling runs)")
+                         "rasterisation; lds-probe: run the LDS bank probe layouts; copy-compare: the tile copy "
+                         "beside the plain and box-shaped copies; reduce: the int32 and bf16 reduce-add passes "
+                         "(profiling runs)")
     ap.add_argument("--gemm-variant", default="all",
                     help="bk,stages[,k256][,mfma] e.g. 32,4,k256 or 64,2,k256,32 (with --only gemm)")
     ap.add_argument("--gemm-c-f32", action="store_true",
@@ -458,6 +565,12 @@ def main():
             att.lds_bank_probe(layout, 1000, h.data_ptr(), stream)
         torch.cuda.synchronize()
         print(json.dumps({"lds_probe_layouts": 7, "iters": 1000}), flush=True)
+        return
+    if args.only == "copy-compare":
+        print(json.dumps({"copy_compare": run_copy_compare(att, torch, stream)}), flush=True)
+        return
+    if args.only == "reduce":
+        print(json.dumps({"reduce_compare": run_reduce_compare(att, torch, stream)}), flush=True)
         return
     if args.only == "gemm-raster":
         print(json.dumps({"gemm_raster": run_gemm_raster(att, torch, stream, args.steps),
@@ -576,6 +689,8 @@ def main():
         result["frac_of_linear_copy"] = round(gbs / ceil["copy_GBps"], 4)
         best_copy = max(ceil["copy_GBps"], ceil.get("copy_sweep_best", {}).get("GBps", 0.0))
         result["frac_of_best_plain_copy"] = round(gbs / best_copy, 4)
+        if "box_copy_sweep_best" in ceil:
+            result["frac_of_box_shaped_copy"] = round(gbs / ceil["box_copy_sweep_best"]["GBps"], 4)
     if not args.no_extra:
         result["extra"] = run_extra(att, torch, stream, 20)
     if not args.no_cpu_baseline:
