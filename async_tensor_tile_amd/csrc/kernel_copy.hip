@@ -44,8 +44,15 @@ __device__ __forceinline__ void tile_origin(const CopyArgs& a, uint32_t t, uint6
                                             int32_t c[5]) {
     if (a.src.rank <= 2) {
         // one division instead of five (the short-lived workgroups pay this
-        // per box)
-        const uint32_t t1 = t / a.nt[0], t0 = t - t1 * a.nt[0];
+        // per box).  Box row t1 is walked starting t1 boxes along dim 0 (a
+        // rotation of each row, so every box is still visited once): the
+        // workgroups in flight together, which straddle neighbouring box
+        // rows, then sit at different dim-0 offsets.  Measured on the bf16
+        // 8192^2 round trip in 128 x 64 boxes: 2 % faster than the plain
+        // row-major walk (and as fast as an XOR of the row into the column).
+        const uint32_t t1 = t / a.nt[0];
+        uint32_t t0 = t - t1 * a.nt[0] + t1 % a.nt[0];
+        if (t0 >= a.nt[0]) t0 -= a.nt[0];
         c[0] = (int32_t)(t0 * (a.src.box_m1[0] + 1u));
         c[1] = (int32_t)(t1 * (a.src.box_m1[1] + 1u));
         c[2] = c[3] = c[4] = 0;

@@ -126,6 +126,25 @@ def test_copy_random_maps(seed):
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("dims", [(8192, 8192), (8192, 640), (1984, 1408)])
+def test_copy_default_entry(dims):
+    """tile_copy, the launch the benchmark times (non-temporal stores, two
+    boxes per workgroup, each box row walked from a rotated start), on the
+    full workload and on shapes whose box-row count is below, or not a
+    multiple of, the boxes per row."""
+    ex = W.COPY_8192
+    say("copy default entry", dims)
+    H, Wd = dims[1], dims[0]
+    src = synthgen.u16_bits(7, (H, Wd))
+    sd = to_dev(src)
+    dd = empty_dev(src.nbytes, 0x33)
+    ms = encode(sd, "bf16", dims, (Wd * 2,), ex["box"], swizzle=ex["swizzle"])
+    md = encode(dd, "bf16", dims, (Wd * 2,), ex["box"], swizzle=ex["swizzle"])
+    att.tile_copy(ms, md, 2, stream())
+    torch.cuda.synchronize()
+    assert torch.equal(sd, dd)
+
+
 def test_copy_grid_sweep_small():
     ex = W.COPY_8192
     for grid in (1, 255, 256, 1024, 4096):
