@@ -9,10 +9,16 @@
 // own S-deep ring without any workgroup barrier.  Completion of a stage is the
 // wave's s_waitcnt vmcnt, counted in DMA instructions issued after that stage;
 // LDS reads are inline-asm ds_read_b128 at the swizzled address and go out as
-// coalesced global_store_dwordx4 in logical order.  Edge tiles, element
-// strides or shapes that do not split evenly take the generic path: one
-// workgroup per box through tile_load_issue / tile_store_issue.
+// coalesced global_store_dwordx4 in logical order.  The producer / consumer
+// form (the default for two stages) splits the roles instead: one wave
+// issues every copy of the workgroup's boxes and four waves store them.
+// Edge tiles, element strides or shapes that do not split evenly take the
+// generic path: one workgroup per box through tile_load_issue /
+// tile_store_issue.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
 
 #include "host_util.hpp"
 #include "att/tile_device.hpp"
@@ -33,7 +39,7 @@ struct CopyArgs {
 // Bits 4..5 select how many consecutive boxes share one ring stage (1, 2, 4, 8).
 enum : uint32_t {
     CV_NT_STORE = 1u, CV_GENERIC = 2u, CV_CHUNKED = 4u, CV_XCD = 8u, CV_NB_SHIFT = 4u, CV_BATCH = 64u, CV_ROWMAJOR = 128u,
-    CV_REGLOAD = 256u
+    CV_REGLOAD = 256u, CV_PC = 512u
 };
 constexpr uint32_t kNumXcd = 8;
 
@@ -300,6 +306,120 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_batch(CopyArgs a,
     }
 }
 
+// Per-lane constants of group g of a box: the global offset of the logical
+// chunk its DMA lane copies (ld), the offset the chunk its store lane writes
+// goes to (st) and the LDS byte offset holding the latter (rd).
+__device__ __forceinline__ void group_lane_offsets(const CopyArgs& a, uint32_t g, uint32_t lane, uint64_t& ld,
+                                                   uint64_t& st, uint32_t& rd) {
+    const uint32_t p = g * 64u + lane;
+    const uint32_t q = swz_chunk(p, a.src.swizzle);
+    rd = q * 16u;
+    if (a.src.rank <= 2) {
+        const uint32_t rq = fdiv(q, a.src.magic_cpr), rp = fdiv(p, a.src.magic_cpr);
+        ld = (uint64_t)rq * a.src.stride[0] + (q - rq * a.src.cpr) * 16u;
+        st = (uint64_t)rp * a.dst.stride[0] + (p - rp * a.src.cpr) * 16u;
+    } else {
+        const int32_t zero[5] = {0, 0, 0, 0, 0};
+        const ChunkLoc ls = chunk_locate(a.src, zero, q);
+        ld = (uint64_t)(ls.g0 * a.src.esize + ls.rest_off);
+        const ChunkLoc ldst = chunk_locate(a.dst, zero, p);
+        st = (uint64_t)(ldst.g0 * a.dst.esize + ldst.rest_off);
+    }
+}
+
+// Producer / consumer round trip, the pages' division of labour between the
+// thread that issues the copies and the threads that consume the staged
+// tile: wave 0 of a workgroup issues every LDS-DMA copy of its NB boxes (G
+// 1 KiB groups each) and then, as the groups land in order, releases them
+// kPcCons at a time with a workgroup barrier; each of the kPcCons consumer
+// waves reads one released group from LDS and stores it.  The producer only
+// ever has copies outstanding, so its vmcnt waits are exact and follow the
+// copies one step at a time; the consumers never wait on their stores, so
+// a store is issued as soon as its group has landed.  Every wave passes the
+// same NB * G / kPcCons barriers.
+constexpr uint32_t kPcCons = 4;
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>)
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll_for(F&& f) {
+    unroll_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int G, int NB>
+__global__ __launch_bounds__((kPcCons + 1) * 64) void k_tile_copy_pc(CopyArgs a, uint32_t nt_store) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    constexpr int K = G * NB;                          // groups per workgroup
+    constexpr int STEPS = K / (int)kPcCons;
+    static_assert(K % (int)kPcCons == 0 && K <= 64, "whole steps; vmcnt range");
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t lane = lane_id();
+    const uint32_t B = a.src.box_bytes;
+    const uint32_t t0 = blockIdx.x * NB;
+    if (wave == 0) {
+        uint64_t ld[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            uint64_t st;
+            uint32_t rd;
+            group_lane_offsets(a, (uint32_t)g, lane, ld[g], st, rd);
+        }
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+            uint64_t so, dof;
+            int32_t c[5];
+            tile_origin(a, t0 + x, so, dof, c);
+#ifdef ATT_DEBUG
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                *reinterpret_cast<u32x4*>(smem + x * B + g * 1024u + lane * 16u) =
+                    u32x4{0xDBDBDBDBu, 0xDBDBDBDBu, 0xDBDBDBDBu, 0xDBDBDBDBu};
+            wait_lgkm0();
+#endif
+#pragma unroll
+            for (int g = 0; g < G; ++g) dma16((const void*)(uintptr_t)(a.src.base + so + ld[g]), smem + x * B + g * 1024u);
+        }
+        // step s releases groups [s * kPcCons, (s + 1) * kPcCons): they have
+        // landed once at most K - (s + 1) * kPcCons copies are outstanding
+        unroll_for<STEPS>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            wait_vmcnt<K - (s + 1) * (int)kPcCons>();
+            wg_barrier();
+        });
+    } else {
+        const uint32_t cw = wave - 1u;                 // consumer index: group cw of every step
+        uint64_t st[G / kPcCons], dof[NB];
+        uint32_t rd[G / kPcCons];
+#pragma unroll
+        for (int i = 0; i < G / (int)kPcCons; ++i) {
+            uint64_t ld;
+            group_lane_offsets(a, cw + (uint32_t)i * kPcCons, lane, ld, st[i], rd[i]);
+        }
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+            uint64_t so;
+            int32_t c[5];
+            tile_origin(a, t0 + x, so, dof[x], c);
+        }
+        const uint32_t lds0 = lds_addr_of(smem);
+        unroll_for<STEPS>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            constexpr int k0 = s * (int)kPcCons;       // first group of the step
+            constexpr int x = k0 / G, i = (k0 % G) / (int)kPcCons;
+            wg_barrier();
+            u32x4 v[1];
+            const uint32_t addr[1] = {lds0 + x * B + rd[i]};
+            lds_read_group<1>(addr, v);
+            ATT_GLOBAL u32x4* p = (ATT_GLOBAL u32x4*)(gptr(a.dst.base + dof[x]) + st[i]);
+            if (nt_store) __builtin_nontemporal_store(v[0], p);
+            else *p = v[0];
+        });
+    }
+}
+
 // Generic round trip: one workgroup per tile, any geometry.
 __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_generic(CopyArgs a) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -348,6 +468,30 @@ static tmap_status launch_batch_r(const CopyArgs& a, uint32_t nbox, bool rowmajo
                                   hipStream_t st) {
     return regload ? launch_batch_n<GPW, true>(a, nbox, rowmajor, nt, st)
                    : launch_batch_n<GPW, false>(a, nbox, rowmajor, nt, st);
+}
+
+template <int G, int NB>
+static tmap_status launch_pc(const CopyArgs& a, uint32_t nt, hipStream_t st) {
+    if constexpr (G * NB > 64 || (G * NB) % (int)kPcCons != 0 || G < (int)kPcCons) {
+        return TMAP_ERR_UNSUPPORTED;
+    } else {
+        const uint32_t lds = (uint32_t)NB * a.src.box_bytes;
+        hipError_t e = hipFuncSetAttribute((const void*)k_tile_copy_pc<G, NB>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+        hipLaunchKernelGGL((k_tile_copy_pc<G, NB>), dim3(a.ntiles / NB), dim3((kPcCons + 1) * 64), lds, st, a, nt);
+        return check_launch("tile_copy");
+    }
+}
+
+template <int G>
+static tmap_status launch_pc_nb(const CopyArgs& a, uint32_t nb, uint32_t nt, hipStream_t st) {
+    switch (nb) {
+    case 1: return launch_pc<G, 1>(a, nt, st);
+    case 2: return launch_pc<G, 2>(a, nt, st);
+    case 4: return launch_pc<G, 4>(a, nt, st);
+    default: return TMAP_ERR_UNSUPPORTED;
+    }
 }
 
 template <int GPW, int S, int NB>
@@ -426,7 +570,7 @@ using namespace att;
 extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32_t stages, uint32_t grid,
                                     uint32_t variant, void* stream) {
     if (!src || !dst) return TMAP_ERR_NULL;
-    if (stages < 1 || stages > 8 || variant > 511) return TMAP_ERR_UNSUPPORTED;
+    if (stages < 1 || stages > 8 || variant > 1023) return TMAP_ERR_UNSUPPORTED;
     CopyArgs a;
     a.src = load_map(src);
     a.dst = load_map(dst);
@@ -466,6 +610,20 @@ extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32
     const bool batch_ok = (variant & CV_BATCH) && even && !(variant & CV_GENERIC) && gpw * kCopyWaves == groups &&
                           (gpw == 1 || gpw == 2 || gpw == 4 || gpw == 8) && stages >= 2 && stages <= 4 &&
                           stages * B <= limit && a.ntiles % stages == 0 && gpw * (stages - 1) <= 63;
+    // producer / consumer mode: `stages` boxes per workgroup (1, 2 or 4),
+    // one stage each, boxes of 4, 8, 16 or 32 KiB
+    const bool pc_ok = (variant & CV_PC) && even && !(variant & CV_GENERIC) && B % 4096u == 0 && B <= 32768u &&
+                       (stages == 1 || stages == 2 || stages == 4) && stages * (B / 1024u) <= 64 &&
+                       a.ntiles % stages == 0 && stages * B <= limit;
+    if (pc_ok) {
+        const uint32_t nt = (variant & CV_NT_STORE) ? 1u : 0u;
+        switch (B / 1024u) {
+        case 4: return launch_pc_nb<4>(a, stages, nt, s);
+        case 8: return launch_pc_nb<8>(a, stages, nt, s);
+        case 16: return launch_pc_nb<16>(a, stages, nt, s);
+        default: return launch_pc_nb<32>(a, stages, nt, s);
+        }
+    }
     if (batch_ok) {
         const uint32_t g = a.ntiles / stages;
         a.xcd = ((variant & CV_XCD) && g % kNumXcd == 0) ? 1u : 0u;
@@ -495,7 +653,9 @@ extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32
 
 // Default launch: non-temporal stores, workgroups owning neighbouring boxes,
 // two ring stages' worth of boxes per workgroup so that LDS, not the grid,
-// bounds how many workgroups share a CU.
+// bounds how many workgroups share a CU.  With two stages the producer /
+// consumer form takes the two boxes where the box size allows it (measured
+// on the bf16 8192^2 round trip: 49.7-49.8 us against the ring's 50.1).
 extern "C" tmap_status tile_copy(const tmap_t* src, const tmap_t* dst, uint32_t stages, void* stream) {
     if (!src) return TMAP_ERR_NULL;
     const TmapImpl s = load_map(src);
@@ -505,5 +665,5 @@ extern "C" tmap_status tile_copy(const tmap_t* src, const tmap_t* dst, uint32_t 
         T *= ((uint64_t)s.dim[d] + bx - 1) / bx;
     }
     const uint32_t grid = T >= 2 ? (uint32_t)((T + 1) / 2) : 1u;
-    return tile_copy_ex(src, dst, stages, grid, CV_NT_STORE | CV_CHUNKED, stream);
+    return tile_copy_ex(src, dst, stages, grid, CV_NT_STORE | CV_CHUNKED | (stages == 2 ? CV_PC : 0u), stream);
 }

@@ -114,28 +114,31 @@ static void launch_copy_v(bool slice, uint32_t grid, hipStream_t s, const void* 
 // 16-byte vector per lane, 64 lanes = 8 rows x 128 bytes of one box per
 // instruction -- but through registers: every load of the workgroup's boxes
 // first, then every store.  Row-group major issue (NBX boxes' rows 8g..8g+7
-// back to back), or box major.  Measures what the box shape itself costs.
+// back to back), or box major.  flags bit 0: XCD-contiguous numbering;
+// bit 1: box row r is walked starting r boxes along (the tile copy's walk).
+// Measures what the box shape itself costs.
 template <int NBX, bool NT, bool BOXMAJOR>
 __global__ __launch_bounds__(kProbeThreads) void k_hbm_box_copy(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                                                uint32_t width, uint32_t boxes_per_row, uint32_t xcd) {
+                                                                uint32_t width, uint32_t boxes_per_row, uint32_t flags) {
     const uint32_t G = gridDim.x;
-    const uint32_t b = xcd ? (blockIdx.x % 8u) * (G / 8u) + blockIdx.x / 8u : blockIdx.x;
+    const uint32_t b = (flags & 1u) ? (blockIdx.x % 8u) * (G / 8u) + blockIdx.x / 8u : blockIdx.x;
     const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63u;
     const uint32_t t0 = b * NBX;                       // first box of the workgroup (row-major box order)
     const uint64_t band = t0 / boxes_per_row, col0 = t0 % boxes_per_row;
+    const uint64_t rot = (flags & 2u) ? band % boxes_per_row : 0u;
     u32x4 v[4][NBX];
 #pragma unroll
     for (int o = 0; o < 4 * NBX; ++o) {
         const int g = BOXMAJOR ? o % 4 : o / NBX, x = BOXMAJOR ? o / 4 : o % NBX;
         const uint64_t row = band * 128u + (wave * 4u + (uint32_t)g) * 8u + lane / 8u;
-        const uint64_t off = row * width + (col0 + (uint64_t)x) * 128u + (lane % 8u) * 16u;
+        const uint64_t off = row * width + ((col0 + (uint64_t)x + rot) % boxes_per_row) * 128u + (lane % 8u) * 16u;
         v[g][x] = *(const ATT_GLOBAL u32x4*)gptr(src + off);
     }
 #pragma unroll
     for (int o = 0; o < 4 * NBX; ++o) {
         const int g = BOXMAJOR ? o % 4 : o / NBX, x = BOXMAJOR ? o / 4 : o % NBX;
         const uint64_t row = band * 128u + (wave * 4u + (uint32_t)g) * 8u + lane / 8u;
-        const uint64_t off = row * width + (col0 + (uint64_t)x) * 128u + (lane % 8u) * 16u;
+        const uint64_t off = row * width + ((col0 + (uint64_t)x + rot) % boxes_per_row) * 128u + (lane % 8u) * 16u;
         if (NT) __builtin_nontemporal_store(v[g][x], (ATT_GLOBAL u32x4*)gptr(dst + off));
         else *(ATT_GLOBAL u32x4*)gptr(dst + off) = v[g][x];
     }
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_hbm_box_copy(const uint8_t* _
 template <int NBX>
 static tmap_status launch_box_copy(uint32_t variant, uint32_t grid, hipStream_t s, const void* src, void* dst,
                                    uint32_t width, uint32_t bpr) {
-    const uint32_t xcd = (variant >> 1) & 1u;
+    const uint32_t flags = ((variant >> 1) & 1u) | (((variant >> 5) & 1u) << 1);
     // bits 3..4: reserve as much LDS per workgroup as the tile copy's stages
     // would take for NBX 16 KiB boxes (x1, x2 or x4 of 16 KiB), so that LDS,
     // not registers, bounds the workgroups per CU as it does there
@@ -163,10 +166,10 @@ static tmap_status launch_box_copy(uint32_t variant, uint32_t grid, hipStream_t 
         if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
     }
     switch (variant & 5u) {
-    case 0: hipLaunchKernelGGL((k_hbm_box_copy<NBX, false, false>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, xcd); break;
-    case 1: hipLaunchKernelGGL((k_hbm_box_copy<NBX, true, false>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, xcd); break;
-    case 4: hipLaunchKernelGGL((k_hbm_box_copy<NBX, false, true>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, xcd); break;
-    default: hipLaunchKernelGGL((k_hbm_box_copy<NBX, true, true>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, xcd); break;
+    case 0: hipLaunchKernelGGL((k_hbm_box_copy<NBX, false, false>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, flags); break;
+    case 1: hipLaunchKernelGGL((k_hbm_box_copy<NBX, true, false>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, flags); break;
+    case 4: hipLaunchKernelGGL((k_hbm_box_copy<NBX, false, true>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, flags); break;
+    default: hipLaunchKernelGGL((k_hbm_box_copy<NBX, true, true>), dim3(grid), dim3(kProbeThreads), lds, s, a, d, width, bpr, flags); break;
     }
     return TMAP_OK;
 }
@@ -179,7 +182,7 @@ extern "C" tmap_status hbm_probe_box_copy(const void* d_src, void* d_dst, uint32
                                           uint32_t boxes_per_wg, uint32_t variant, void* stream) {
     if (!d_src || !d_dst) return TMAP_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(d_src) | reinterpret_cast<uintptr_t>(d_dst)) & 15u) return TMAP_ERR_ALIGN;
-    if (variant > 31 || width == 0 || height == 0 || width % 128u || height % 128u) return TMAP_ERR_UNSUPPORTED;
+    if (variant > 63 || width == 0 || height == 0 || width % 128u || height % 128u) return TMAP_ERR_UNSUPPORTED;
     const uint32_t bpr = width / 128u;
     const uint64_t nbox = (uint64_t)bpr * (height / 128u);
     if (!(boxes_per_wg == 1 || boxes_per_wg == 2 || boxes_per_wg == 4 || boxes_per_wg == 8) || bpr % boxes_per_wg ||

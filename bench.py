@@ -2,9 +2,10 @@
 """Benchmark: tiled box copy of a bf16 8192 x 8192 tensor through LDS.
 
 One step = one full-grid round trip (8192 boxes of 128 rows x 64 columns,
-128-byte swizzle, 2-stage LDS ring per wave): every box is loaded
-global -> LDS with the swizzle applied on write and stored LDS -> global
-through a second map.  Algorithmic bytes per step: 128 MiB read + 128 MiB
+128-byte swizzle, two LDS stages per workgroup: one wave issues the copies,
+four store each part as it lands): every box is loaded global -> LDS with
+the swizzle applied on write and stored LDS -> global through a second
+map.  Algorithmic bytes per step: 128 MiB read + 128 MiB
 written = 268,435,456 B.  Four source/destination pairs (1 GiB) rotate so
 the 256 MB last-level cache cannot serve the working set.
 
@@ -409,7 +410,7 @@ def hbm_ceiling(att, torch, stream, reps: int = 100, sweep: bool = True):
         # what the box shape itself allows, apart from the LDS staging
         bbest = None
         for nbx in (1, 2, 4, 8):
-            for variant in range(8):
+            for variant in list(range(8)) + [v | 32 for v in range(8)]:
                 t = timed(lambda k, v=variant, b=nbx: att.hbm_probe_box_copy(bufs[k % 4], outs[k % 4], 16384, 8192, b,
                                                                              v, stream))
                 if bbest is None or t < bbest[0]:
@@ -422,7 +423,8 @@ def hbm_ceiling(att, torch, stream, reps: int = 100, sweep: bool = True):
         out["box_copy_sweep_best"] = {"GBps": round(2 * n / bbest[0] / 1e6, 1), "verified": ok3,
                                       "boxes_per_workgroup": bbest[1], "nontemporal_stores": bool(bbest[2] & 1),
                                       "xcd_contiguous": bool(bbest[2] & 2),
-                                      "issue": "box-major" if bbest[2] & 4 else "row-group-major", "configs": 32,
+                                      "issue": "box-major" if bbest[2] & 4 else "row-group-major",
+                                      "rotated_row_walk": bool(bbest[2] & 32), "configs": 64,
                                       "what": "register copy with the tile copy's access shape: one 16-byte "
                                               "vector per lane, 8 rows x 128 bytes of a 128 x 128-byte box "
                                               "per wave instruction"}
@@ -435,8 +437,9 @@ def run_copy_compare(att, torch, stream, reps: int = 20, rounds: int = 3):
     dispatches each of the default tile copy, the best plain copy of the
     sweep (16-byte vectors, non-temporal stores, grid-stride, 4 workgroups
     per CU), the register copy in the tile copy's access shape (2 boxes per
-    workgroup, non-temporal stores) and the default hbm_probe copy, in that
-    order.  Returns the median GB/s of each over the rounds."""
+    workgroup, non-temporal stores, the tile copy's rotated row walk) and the
+    default hbm_probe copy, in that order.  Returns the median GB/s of each
+    over the rounds."""
     import numpy as np
 
     import synthgen
@@ -455,7 +458,7 @@ def run_copy_compare(att, torch, stream, reps: int = 20, rounds: int = 3):
     kinds = {
         "tile_copy": lambda a, b, ma, mb: att.tile_copy(ma, mb, 2, stream),
         "plain_copy_best": lambda a, b, ma, mb: att.hbm_probe_copy_ex(a, b, n, 4, 4, stream),
-        "box_shaped_register_copy": lambda a, b, ma, mb: att.hbm_probe_box_copy(a, b, 16384, 8192, 2, 1, stream),
+        "box_shaped_register_copy": lambda a, b, ma, mb: att.hbm_probe_box_copy(a, b, 16384, 8192, 2, 33, stream),
         "hbm_probe_copy": lambda a, b, ma, mb: att.hbm_probe("copy", a, b, n, stream),
     }
     times = {k: [] for k in kinds}
@@ -674,7 +677,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "bf16 8192x8192 tile round trip global->LDS->global, box 128x64, "
-                               "128B swizzle, 2-stage ring",
+                               "128B swizzle, 2 stages per workgroup (producer / consumer waves)",
                    "box": [64, 128], "tiles": 8192, "stages": args.stages, "variant": args.variant,
                    "grid": args.grid or "auto", "buffer_pairs": args.pairs},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),

@@ -251,7 +251,9 @@ tmap_status tile_reduce(const tmap_t* m, int32_t op, const int32_t* d_coords, ui
 /* Full-grid round trip: every box of the grid covering `src` (origins at
  * multiples of box[i]) is loaded global->LDS through `src` and stored
  * LDS->global through `dst`, with `stages` LDS buffers per workgroup
- * (producer/consumer ring, [MLC] "TMA in a pipeline").  src and dst must have
+ * ([MLC] "TMA in a pipeline": fill one stage while another is consumed;
+ * with two stages and boxes of 4 to 32 KiB one wave issues the copies and
+ * four others store each part as it lands).  src and dst must have
  * the same dtype, rank, dims, box and swizzle, all element strides 1, and
  * must not overlap.  stages in [1, 8].  Errors: NULL, UNSUPPORTED (geometry
  * mismatch, stages, element strides), LDS_CAPACITY, HIP. */
@@ -267,9 +269,15 @@ tmap_status tile_copy(const tmap_t* src, const tmap_t* dst, uint32_t stages, voi
  * (grid ignored; the box count must divide by `stages`), 128 with 64: the
  * workgroup's boxes are neighbours in dim 0 and each wave issues its first
  * copy of every box, then its second, ... (back-to-back requests cover the
- * same rows several boxes wide).  tile_copy uses
- * 1|4 with two boxes per workgroup.  Ring depths 5 and 7 take the generic
- * path. */
+ * same rows several boxes wide), 256 with 64: loads through registers and
+ * ds_write instead of the LDS-DMA, 512 producer / consumer form: each
+ * workgroup owns `stages` (1, 2 or 4) consecutive boxes of 4, 8, 16 or 32
+ * KiB (at most 64 KiB of copies), one stage each; one wave issues every
+ * copy and releases the landed 1 KiB groups four at a time with a barrier,
+ * four consumer waves read and store them (grid ignored; other shapes fall
+ * back to the modes above).  tile_copy uses 1|4|512 with two boxes per
+ * workgroup for stages = 2, 1|4 otherwise.  Ring depths 5 and 7 take the
+ * generic path. */
 tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32_t stages,
                          uint32_t grid, uint32_t variant, void* stream);
 
@@ -363,8 +371,9 @@ tmap_status hbm_probe_copy_ex(const void* d_src, void* d_dst, uint64_t bytes, ui
  * workgroup count must divide by 8), bit 2 box-major instead of row-group-
  * major issue, bits 3..4 = k > 0: reserve 16 KiB << (k - 1) of LDS per
  * workgroup (unused; it bounds the workgroups per CU as the tile copy's
- * stages do).  Shows what the box shape costs apart from the LDS staging.
- * Errors: NULL, ALIGN (16 bytes), UNSUPPORTED (shape, variant > 31), HIP. */
+ * stages do), bit 5 box row r walked starting r boxes along (as the tile
+ * copy walks it).  Shows what the box shape costs apart from the LDS staging.
+ * Errors: NULL, ALIGN (16 bytes), UNSUPPORTED (shape, variant > 63), HIP. */
 tmap_status hbm_probe_box_copy(const void* d_src, void* d_dst, uint32_t width, uint32_t height,
                                uint32_t boxes_per_wg, uint32_t variant, void* stream);
 

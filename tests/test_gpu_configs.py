@@ -43,7 +43,8 @@ def _copy_case(dims, box, swizzle, stages, variant=0, grid=0, seed=2):
 
 
 @pytest.mark.parametrize("stages,variant", [(2, 0), (1, 0), (3, 0), (4, 0), (2, 1), (2, 2), (2, 65), (3, 65), (4, 73),
-                                            (2, 64), (4, 201), (2, 193), (3, 193), (2, 321), (4, 457)])
+                                            (2, 64), (4, 201), (2, 193), (3, 193), (2, 321), (4, 457),
+                                            (1, 513), (2, 513), (4, 512)])
 def test_copy_8192_round_trip(stages, variant):
     ex = W.COPY_8192
     say("copy 8192^2 stages", stages, "variant", variant)
@@ -68,6 +69,10 @@ def test_copy_8192_round_trip(stages, variant):
 def test_copy_other_shapes(dims, box, swizzle):
     say("copy", dims, box, swizzle)
     src, sd, dd, ms, same = _copy_case(dims, box, swizzle, 2, seed=12)
+    assert same
+    # the producer / consumer form (two boxes per workgroup where the box
+    # size allows it, else the ring)
+    src, sd, dd, ms, same = _copy_case(dims, box, swizzle, 2, 513, seed=13)
     assert same
 
 
@@ -113,6 +118,8 @@ def test_copy_random_maps(seed):
         variant |= 128                     # row-group-major issue in batch mode
     if g.integers(0, 2):
         variant |= 256                     # batch mode through registers instead of the LDS-DMA
+    if g.integers(0, 3) == 0:
+        variant |= 512                     # producer / consumer form (where the box size allows it)
     say("copy random", seed, c.dtype, c.dims, c.box, c.swizzle, stages, variant, grid)
     sd = to_dev(c.buf)
     dd = empty_dev(c.buf.size, 0x5A)

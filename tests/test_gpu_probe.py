@@ -56,12 +56,13 @@ def test_probe_copy_variants(nbytes):
 
 def test_probe_box_copy_variants():
     """The box-shaped register copy moves every byte of the matrix for every
-    boxes-per-workgroup count and variant."""
-    W_, H_ = 4096, 512
+    boxes-per-workgroup count and variant (the rotated row walk on a matrix
+    with more box rows than boxes per row, so the rotation wraps)."""
+    W_, H_ = 4096, 5120
     rng = np.random.default_rng(7)
     src = torch.from_numpy(rng.integers(0, 256, W_ * H_, dtype=np.uint8)).cuda()
     for nbx in (1, 2, 4, 8):
-        for variant in range(8):
+        for variant in list(range(8)) + [32, 33, 35, 39]:
             dst = torch.zeros_like(src)
             att.hbm_probe_box_copy(src, dst, W_, H_, nbx, variant, stream())
             torch.cuda.synchronize()
