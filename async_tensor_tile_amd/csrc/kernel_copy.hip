@@ -33,6 +33,13 @@ struct CopyArgs {
     uint32_t nt[5];     // tiles per dimension
     uint32_t chunked;   // 1: workgroup b owns tiles [b*per, b*per + per); 0: tiles b + n*grid
     uint32_t xcd;       // 1: renumber workgroups so each XCD owns one contiguous range
+    // Maps of rank 1 or 2: what the fast paths read, each field 4- or
+    // 8-byte aligned so that it comes in through a scalar load.  Several
+    // descriptor fields are single bytes at offsets that are not multiples of
+    // four, which the compiler fetches with a vector-memory load at the start
+    // of every workgroup: a memory round trip before its first copy.
+    uint64_t r2_sbase, r2_dbase, r2_sstride, r2_dstride;
+    uint32_t r2_box0, r2_box1, r2_sesize, r2_desize, r2_swizzle, r2_cpr, r2_magic_cpr;
 };
 
 // Copy variant flags (tile_copy_ex `variant`).
@@ -44,6 +51,18 @@ enum : uint32_t {
 constexpr uint32_t kNumXcd = 8;
 
 constexpr uint32_t kCopyWaves = 4;
+
+// Box t of a rank 1 or 2 map from the aligned fields only: byte offsets of
+// its origin in src and dst.  Box row t1 is walked starting t1 boxes along
+// dim 0, as in tile_origin.
+__device__ __forceinline__ void tile_origin_r2(const CopyArgs& a, uint32_t t, uint64_t& so, uint64_t& dof) {
+    const uint32_t t1 = t / a.nt[0];
+    uint32_t t0 = t - t1 * a.nt[0] + t1 % a.nt[0];
+    if (t0 >= a.nt[0]) t0 -= a.nt[0];
+    const uint64_t c0 = (uint64_t)(t0 * a.r2_box0), c1 = (uint64_t)(t1 * a.r2_box1);
+    so = c0 * a.r2_sesize + c1 * a.r2_sstride;
+    dof = c0 * a.r2_desize + c1 * a.r2_dstride;
+}
 
 // Byte offsets of tile t's origin in src and dst (tiles innermost first).
 __device__ __forceinline__ void tile_origin(const CopyArgs& a, uint32_t t, uint64_t& so, uint64_t& dof,
@@ -144,7 +163,8 @@ __device__ __forceinline__ void copy_lane_offsets(const CopyArgs& a, uint32_t wa
 // back-to-back requests cover NB neighbouring 128-byte segments of the same
 // rows: with 128-byte-wide boxes that is what keeps HBM pages busy.
 template <int GPW, int S, int NB>
-__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a, uint32_t nt_store) {
+__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a_arg, uint32_t nt_store) {
+    const CopyArgs a = uniform_copy(a_arg);
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t lane = lane_id();
@@ -234,7 +254,8 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_ring(CopyArgs a, 
 // stores is never on the path to the next box, and the workgroup retires as
 // soon as its stores are issued.
 template <int GPW, int NBOX, bool ROWMAJOR, bool REGLOAD>
-__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_batch(CopyArgs a, uint32_t nt_store) {
+__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_batch(CopyArgs a_arg, uint32_t nt_store) {
+    const CopyArgs a = uniform_copy(a_arg);
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t lane = lane_id();
@@ -309,9 +330,18 @@ __global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_batch(CopyArgs a,
 // Per-lane constants of group g of a box: the global offset of the logical
 // chunk its DMA lane copies (ld), the offset the chunk its store lane writes
 // goes to (st) and the LDS byte offset holding the latter (rd).
+template <bool R2>
 __device__ __forceinline__ void group_lane_offsets(const CopyArgs& a, uint32_t g, uint32_t lane, uint64_t& ld,
                                                    uint64_t& st, uint32_t& rd) {
     const uint32_t p = g * 64u + lane;
+    if constexpr (R2) {
+        const uint32_t q = swz_chunk(p, a.r2_swizzle);
+        rd = q * 16u;
+        const uint32_t rq = fdiv(q, a.r2_magic_cpr), rp = fdiv(p, a.r2_magic_cpr);
+        ld = (uint64_t)rq * a.r2_sstride + (q - rq * a.r2_cpr) * 16u;
+        st = (uint64_t)rp * a.r2_dstride + (p - rp * a.r2_cpr) * 16u;
+        return;
+    }
     const uint32_t q = swz_chunk(p, a.src.swizzle);
     rd = q * 16u;
     if (a.src.rank <= 2) {
@@ -349,8 +379,9 @@ __device__ __forceinline__ void unroll_for(F&& f) {
     unroll_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int G, int NB>
-__global__ __launch_bounds__((kPcCons + 1) * 64) void k_tile_copy_pc(CopyArgs a, uint32_t nt_store) {
+template <int G, int NB, bool R2>
+__global__ __launch_bounds__((kPcCons + 1) * 64) void k_tile_copy_pc(CopyArgs a_arg, uint32_t nt_store) {
+    const CopyArgs a = uniform_copy(a_arg);
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     constexpr int K = G * NB;                          // groups per workgroup
     constexpr int STEPS = K / (int)kPcCons;
@@ -365,13 +396,18 @@ __global__ __launch_bounds__((kPcCons + 1) * 64) void k_tile_copy_pc(CopyArgs a,
         for (int g = 0; g < G; ++g) {
             uint64_t st;
             uint32_t rd;
-            group_lane_offsets(a, (uint32_t)g, lane, ld[g], st, rd);
+            group_lane_offsets<R2>(a, (uint32_t)g, lane, ld[g], st, rd);
         }
+        const uint64_t sbase = R2 ? a.r2_sbase : a.src.base;
 #pragma unroll
         for (int x = 0; x < NB; ++x) {
             uint64_t so, dof;
-            int32_t c[5];
-            tile_origin(a, t0 + x, so, dof, c);
+            if constexpr (R2) {
+                tile_origin_r2(a, t0 + x, so, dof);
+            } else {
+                int32_t c[5];
+                tile_origin(a, t0 + x, so, dof, c);
+            }
 #ifdef ATT_DEBUG
 #pragma unroll
             for (int g = 0; g < G; ++g)
@@ -380,7 +416,7 @@ __global__ __launch_bounds__((kPcCons + 1) * 64) void k_tile_copy_pc(CopyArgs a,
             wait_lgkm0();
 #endif
 #pragma unroll
-            for (int g = 0; g < G; ++g) dma16((const void*)(uintptr_t)(a.src.base + so + ld[g]), smem + x * B + g * 1024u);
+            for (int g = 0; g < G; ++g) dma16((const void*)(uintptr_t)(sbase + so + ld[g]), smem + x * B + g * 1024u);
         }
         // step s releases groups [s * kPcCons, (s + 1) * kPcCons): they have
         // landed once at most K - (s + 1) * kPcCons copies are outstanding
@@ -396,14 +432,19 @@ __global__ __launch_bounds__((kPcCons + 1) * 64) void k_tile_copy_pc(CopyArgs a,
 #pragma unroll
         for (int i = 0; i < G / (int)kPcCons; ++i) {
             uint64_t ld;
-            group_lane_offsets(a, cw + (uint32_t)i * kPcCons, lane, ld, st[i], rd[i]);
+            group_lane_offsets<R2>(a, cw + (uint32_t)i * kPcCons, lane, ld, st[i], rd[i]);
         }
 #pragma unroll
         for (int x = 0; x < NB; ++x) {
             uint64_t so;
-            int32_t c[5];
-            tile_origin(a, t0 + x, so, dof[x], c);
+            if constexpr (R2) {
+                tile_origin_r2(a, t0 + x, so, dof[x]);
+            } else {
+                int32_t c[5];
+                tile_origin(a, t0 + x, so, dof[x], c);
+            }
         }
+        const uint64_t dbase = R2 ? a.r2_dbase : a.dst.base;
         const uint32_t lds0 = lds_addr_of(smem);
         unroll_for<STEPS>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
@@ -413,7 +454,7 @@ __global__ __launch_bounds__((kPcCons + 1) * 64) void k_tile_copy_pc(CopyArgs a,
             u32x4 v[1];
             const uint32_t addr[1] = {lds0 + x * B + rd[i]};
             lds_read_group<1>(addr, v);
-            ATT_GLOBAL u32x4* p = (ATT_GLOBAL u32x4*)(gptr(a.dst.base + dof[x]) + st[i]);
+            ATT_GLOBAL u32x4* p = (ATT_GLOBAL u32x4*)(gptr(dbase + dof[x]) + st[i]);
             if (nt_store) __builtin_nontemporal_store(v[0], p);
             else *p = v[0];
         });
@@ -421,7 +462,8 @@ __global__ __launch_bounds__((kPcCons + 1) * 64) void k_tile_copy_pc(CopyArgs a,
 }
 
 // Generic round trip: one workgroup per tile, any geometry.
-__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_generic(CopyArgs a) {
+__global__ __launch_bounds__(kCopyWaves * 64) void k_tile_copy_generic(CopyArgs a_arg) {
+    const CopyArgs a = uniform_copy(a_arg);
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const uint32_t wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     uint64_t so, dof;
@@ -476,10 +518,13 @@ static tmap_status launch_pc(const CopyArgs& a, uint32_t nt, hipStream_t st) {
         return TMAP_ERR_UNSUPPORTED;
     } else {
         const uint32_t lds = (uint32_t)NB * a.src.box_bytes;
-        hipError_t e = hipFuncSetAttribute((const void*)k_tile_copy_pc<G, NB>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const void* fn = a.src.rank <= 2 ? (const void*)k_tile_copy_pc<G, NB, true> : (const void*)k_tile_copy_pc<G, NB, false>;
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-        hipLaunchKernelGGL((k_tile_copy_pc<G, NB>), dim3(a.ntiles / NB), dim3((kPcCons + 1) * 64), lds, st, a, nt);
+        if (a.src.rank <= 2)
+            hipLaunchKernelGGL((k_tile_copy_pc<G, NB, true>), dim3(a.ntiles / NB), dim3((kPcCons + 1) * 64), lds, st, a, nt);
+        else
+            hipLaunchKernelGGL((k_tile_copy_pc<G, NB, false>), dim3(a.ntiles / NB), dim3((kPcCons + 1) * 64), lds, st, a, nt);
         return check_launch("tile_copy");
     }
 }
@@ -592,6 +637,17 @@ extern "C" tmap_status tile_copy_ex(const tmap_t* src, const tmap_t* dst, uint32
     a.ntiles = (uint32_t)T;
     a.chunked = (variant & CV_CHUNKED) ? 1u : 0u;
     a.xcd = 0u;
+    a.r2_sbase = a.src.base;
+    a.r2_dbase = a.dst.base;
+    a.r2_sstride = a.src.rank >= 2 ? a.src.stride[0] : 0u;
+    a.r2_dstride = a.dst.rank >= 2 ? a.dst.stride[0] : 0u;
+    a.r2_box0 = (uint32_t)a.src.box_m1[0] + 1u;
+    a.r2_box1 = (uint32_t)a.src.box_m1[1] + 1u;
+    a.r2_sesize = a.src.esize;
+    a.r2_desize = a.dst.esize;
+    a.r2_swizzle = a.src.swizzle;
+    a.r2_cpr = a.src.cpr;
+    a.r2_magic_cpr = a.src.magic_cpr;
     uint32_t limit = 0, cus = 0;
     tmap_status st = device_lds_limit(&limit);
     if (st) return st;

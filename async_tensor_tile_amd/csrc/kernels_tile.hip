@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_load(tmap_t map, const i
                                                             uint8_t* __restrict__ out, uint32_t bar_off) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     TxBar* bar = reinterpret_cast<TxBar*>(smem + bar_off);
-    const TmapImpl& m = tmap_tiled(map);
+    const TmapImpl m = tmap_tiled_uniform(map);
     const uint32_t b = blockIdx.x;
     const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
     int32_t c[5];
@@ -143,7 +143,7 @@ template <int OP>
 __global__ __launch_bounds__(kBatchThreads) void k_tile_store(tmap_t map, const int32_t* __restrict__ coords,
                                                              const uint8_t* __restrict__ in) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    const TmapImpl& m = tmap_tiled(map);
+    const TmapImpl m = tmap_tiled_uniform(map);
     const uint32_t b = blockIdx.x;
     const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
     int32_t c[5];
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kBatchThreads) void k_txbar_selftest(tmap_t map, co
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     TxBar* bar = reinterpret_cast<TxBar*>(smem + bar_off);
     uint32_t* counter = reinterpret_cast<uint32_t*>(smem + bar_off + sizeof(TxBar));
-    const TmapImpl& m = tmap_tiled(map);
+    const TmapImpl m = tmap_tiled_uniform(map);
     const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
     if (tid == 0) {
         txbar_init(bar, 1);

@@ -45,6 +45,25 @@ static __device__ __attribute__((aligned(16))) const uint32_t g_fill_rows[5][4] 
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
+// A copy of a struct that is the same for the whole wave (a kernel
+// argument), read as aligned 32-bit words into scalar registers.  Reading
+// its one- and two-byte fields where they lie takes vector-memory loads
+// (there are no sub-word scalar loads): for a kernel argument, a memory
+// round trip at the start of every workgroup, before its first copy.  Words
+// the caller never uses are dropped by the compiler.
+template <typename T>
+__device__ __forceinline__ T uniform_copy(const T& x) {
+    static_assert(sizeof(T) % 4 == 0 && alignof(T) >= 4, "whole 32-bit words");
+    union {
+        uint32_t u[sizeof(T) / 4];
+        T t;
+    } r;
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&x);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) r.u[i] = __builtin_amdgcn_readfirstlane(w[i]);
+    return r.t;
+}
+
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, uint32_t magic) {
     return magic ? __umulhi(n, magic) : n;
 }

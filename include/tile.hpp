@@ -74,6 +74,13 @@ __device__ __forceinline__ const TmapImpl& tmap_tiled(const tmap_t& map) {
     return *reinterpret_cast<const TmapImpl*>(&map);
 }
 
+// A copy of a map that is the same for the whole wave (a kernel argument,
+// as the pages pass descriptors) in scalar registers, read as whole 32-bit
+// words: the map's one- and two-byte fields read where they lie would take
+// vector-memory loads, a memory round trip before the first copy of every
+// workgroup.  Kernels that take a map as an argument start from this.
+__device__ __forceinline__ TmapImpl tmap_tiled_uniform(const tmap_t& map) { return uniform_copy(tmap_tiled(map)); }
+
 // The 128 bytes of an im2col map as the device reads them.
 __device__ __forceinline__ const Im2colImpl& tmap_im2col(const tmap_t& map) {
     return *reinterpret_cast<const Im2colImpl*>(&map);
