@@ -59,3 +59,44 @@ def test_gemm_sgpr_base_dma_wait_states(tmp_path):
     spills = asm_scan.sgpr_spills(asm)
     ring = {k: c for k, c in spills.items() if "k_gemm_bf16_ring5" in k}
     assert len(ring) == 4 and all(c == 0 for c in ring.values()), ring
+
+
+def _kernel_bodies(asm: str) -> dict:
+    """Kernel name -> its assembly text, for every kernel of a listing."""
+    import re
+    out = {}
+    for m in re.finditer(r"^(_ZN3att\w+):", asm, re.M):
+        end = asm.find(".Lfunc_end", m.start())
+        out[m.group(1)] = asm[m.start():end]
+    return out
+
+
+def _argument_vector_loads(body: str) -> list:
+    """Vector-memory loads whose base is the kernel-argument pointer s[0:1]
+    (the kernels here have no scratch, so it is their first user SGPR pair)."""
+    import re
+    return re.findall(r"global_load_\w+\s+v\[?[\d:]+\]?,\s*v\d+,\s*s\[0:1\]", body)
+
+
+@pytest.mark.parametrize("src", ["kernel_copy.hip", "kernels_tile.hip"])
+def test_kernel_arguments_come_through_scalar_loads(tmp_path, src):
+    """The copy and the tile load / store / reduce kernels read their maps as
+    whole words (scalar loads); a byte field read in place would be a
+    vector-memory load of the argument, a memory round trip at the start of
+    every workgroup.  The scanner itself is checked on a planted line."""
+    assert len(_argument_vector_loads("k:\n\tglobal_load_ubyte v3, v1, s[0:1] offset:94\n")) == 1
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not installed")
+    out = tmp_path / (src + ".s")
+    subprocess.check_call([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17",
+                           "-I" + os.path.join(ROOT, "include"),
+                           "-I" + os.path.join(ROOT, "async_tensor_tile_amd", "csrc"),
+                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics",
+                           "-Wno-unused-command-line-argument", "--cuda-device-only", "-S",
+                           os.path.join(ROOT, "async_tensor_tile_amd", "csrc", src), "-o", str(out)],
+                          stderr=subprocess.DEVNULL)
+    bodies = _kernel_bodies(out.read_text())
+    assert len(bodies) > 3
+    bad = {k: len(_argument_vector_loads(b)) for k, b in bodies.items() if _argument_vector_loads(b)}
+    assert bad == {}, list(bad.items())[:5]
