@@ -32,7 +32,7 @@ KERNEL_SOURCES = ("async_tensor_tile_amd/csrc/kernel_copy.hip", "include/att/til
 
 
 GEMM_COUNTERS_FILE = os.path.join(PROFILE_DIR, "gemm_bf16_8192_counters.json")
-GEMM_SOURCES = ("async_tensor_tile_amd/csrc/kernel_gemm.hip", "include/att/tile_device.hpp",
+GEMM_SOURCES = ("async_tensor_tile_amd/csrc/kernel_gemm.hip", "include/att/tile_device.hpp", "include/tile.hpp",
                 "include/att/tmap_impl.hpp")
 
 
