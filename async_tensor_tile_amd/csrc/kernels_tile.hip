@@ -146,14 +146,16 @@ __global__ __launch_bounds__(kBatchThreads) void k_tile_store(tmap_t map, const 
     const TmapImpl m = tmap_tiled_uniform(map);
     const uint32_t b = blockIdx.x;
     const uint32_t tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
-    int32_t c[5];
-    read_coords(m, coords, b, c);
     const uint32_t nchunk = m.box_bytes >> 4;
     const uint8_t* src = in + (size_t)b * m.box_bytes;
     for (uint32_t grp = wave; grp * 64u < nchunk; grp += nwaves) {
         const uint32_t p = grp * 64u + lane_id();
         if (p < nchunk) dma16(src + p * 16u, smem + grp * 1024u);
     }
+    // the box origin is fetched once the image copies are in flight (its
+    // scalar load would otherwise hold them up)
+    int32_t c[5];
+    read_coords(m, coords, b, c);
     wait_vmcnt<0>();
     __syncthreads();
     if constexpr (OP == ST_STORE) tile_store_async(map, c, smem, wave, nwaves);
