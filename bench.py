@@ -516,6 +516,54 @@ def run_reduce_compare(att, torch, stream, reps: int = 10):
     return out
 
 
+def run_reduce_scale(att, torch, stream, reps: int = 10, rounds: int = 3):
+    """The reduce-add pass (64 x 64 boxes at uniform origins in [0, 4032]^2
+    of a 4096 x 4096 destination) at 128 to 8192 boxes, int32 and bf16
+    interleaved per round; the median per pass over `rounds` rounds of
+    `reps` dispatches.  Separates the pass's fixed latency (below about
+    1000 boxes every workgroup is resident at once) from its per-byte cost."""
+    import numpy as np
+
+    import synthgen
+    from synthgen import workloads as W
+
+    ex = W.REDUCE_4096
+    counts = (128, 256, 512, 1024, 2048, 4096, 8192)
+    nmax = counts[-1]
+    rc = torch.from_numpy(synthgen.uniform_coords(ex["seed"] * 1000 + 30, nmax, (0, 0), (4032, 4032))).cuda()
+    dst = torch.from_numpy(synthgen.int32_range(ex["seed"], (4096, 4096), -(1 << 20), 1 << 20)).cuda()
+    src = torch.from_numpy(synthgen.int32_range(ex["seed"] * 1000 + 31, (nmax, 64, 64), -(1 << 20), 1 << 20)).cuda()
+    mi = att.tmap_encode("i32", 2, dst.data_ptr(), ex["dims"], ex["strides"], ex["box"], None, "none")
+    d16 = torch.from_numpy(synthgen.normal_bf16_bits(ex["seed"], (4096, 4096)).view(np.int16)).cuda()
+    s16 = torch.from_numpy(synthgen.normal_bf16_bits(ex["seed"] * 1000 + 32, (nmax, 64, 64)).view(np.int16)).cuda()
+    mb = att.tmap_encode("bf16", 2, d16.data_ptr(), ex["dims"], (8192,), ex["box"], None, "none")
+    times = {}
+    for _ in range(rounds):
+        for n in counts:
+            for key, fn in (("int32", lambda n=n: att.tile_reduce_add(mi, rc.data_ptr(), n, src.data_ptr(), stream)),
+                            ("bf16", lambda n=n: att.tile_reduce(mb, "add", rc.data_ptr(), n, s16.data_ptr(),
+                                                                 stream))):
+                fn()
+                torch.cuda.synchronize()
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                for _ in range(reps):
+                    fn()
+                e.record()
+                torch.cuda.synchronize()
+                times.setdefault((key, n), []).append(s.elapsed_time(e) / reps)
+    out = []
+    for n in counts:
+        row = {"boxes": n}
+        for key, bb in (("int32", 16384), ("bf16", 8192)):
+            ms = sorted(times[(key, n)])[len(times[(key, n)]) // 2]
+            row[key + "_us"] = round(ms * 1e3, 2)
+            row[key + "_GBps"] = round(n * bb * 3 / ms / 1e6, 1)
+        row["bf16_per_byte_vs_int32"] = round(row["int32_GBps"] / row["bf16_GBps"], 3)
+        out.append(row)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -528,12 +576,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (rank-5 load, reduce-add pass, GEMM 8192^3)")
-    ap.add_argument("--only", choices=["copy", "gemm", "gemm-raster", "lds-probe", "copy-compare", "reduce"],
+    ap.add_argument("--only", choices=["copy", "gemm", "gemm-raster", "lds-probe", "copy-compare", "reduce",
+                                       "reduce-scale"],
                     default="copy",
                     help="gemm: time only the GEMM mainloop; gemm-raster: the default GEMM under each tile "
                          "rasterisation; lds-probe: run the LDS bank probe layouts; copy-compare: the tile copy "
                          "beside the plain and box-shaped copies; reduce: the int32 and bf16 reduce-add passes "
-                         "(profiling runs)")
+                         "(profiling runs); reduce-scale: those passes at 128 to 8192 boxes")
     ap.add_argument("--gemm-variant", default="all",
                     help="bk,stages[,k256][,mfma] e.g. 32,4,k256 or 64,2,k256,32 (with --only gemm)")
     ap.add_argument("--gemm-c-f32", action="store_true",
@@ -576,6 +625,9 @@ def main():
         return
     if args.only == "reduce":
         print(json.dumps({"reduce_compare": run_reduce_compare(att, torch, stream)}), flush=True)
+        return
+    if args.only == "reduce-scale":
+        print(json.dumps({"reduce_scale": run_reduce_scale(att, torch, stream)}), flush=True)
         return
     if args.only == "gemm-raster":
         print(json.dumps({"gemm_raster": run_gemm_raster(att, torch, stream, args.steps),
