@@ -59,7 +59,7 @@ __device__ __forceinline__ void tile_origin_r2(const CopyArgs& a, uint32_t t, ui
     const uint32_t t1 = t / a.nt[0];
     uint32_t t0 = t - t1 * a.nt[0] + t1 % a.nt[0];
     if (t0 >= a.nt[0]) t0 -= a.nt[0];
-    const uint64_t c0 = (uint64_t)(t0 * a.r2_box0), c1 = (uint64_t)(t1 * a.r2_box1);
+    const uint64_t c0 = (uint64_t)t0 * a.r2_box0, c1 = (uint64_t)t1 * a.r2_box1;
     so = c0 * a.r2_sesize + c1 * a.r2_sstride;
     dof = c0 * a.r2_desize + c1 * a.r2_dstride;
 }
