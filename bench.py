@@ -296,12 +296,16 @@ def run_gemm_raster(att, torch, stream, reps: int, rounds: int = 3):
     return out
 
 
-def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int = 10, vendor: bool = False,
-             rounds: int = 3, c_f32: bool = False):
+def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int = 40, warmup_ms: float = 100.0,
+             vendor: bool = False, rounds: int = 3, c_f32: bool = False):
     """bf16 GEMM mainloop, M = N = K = 8192, A row-major, B column-major,
     N(0,1) operands; 2*M*N*K flop per launch.  Each variant is timed in
     `rounds` interleaved rounds of `reps` launches (median reported), after
-    `warmup` launches so that clocks have settled under sustained MFMA load.
+    at least `warmup` launches of each and `warmup_ms` of host time, the
+    variants in turn: when MFMA work follows a memory-bound phase the
+    shader clock takes some 30-60 ms of sustained load to settle (the first
+    launches run 20-40 % slower, for the vendor kernel as for these), and
+    the figure wanted is the settled rate.
     With `vendor`, torch's A @ B^T on the same operands joins the rounds.
     With `c_f32`, C is written as the fp32 accumulators (gemm_bf16_f32, no
     LDS staging of C), for counters of the mainloop alone."""
@@ -330,10 +334,12 @@ def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int 
     if vendor:
         Bt = Bd.t()
         fns["vendor_gemm_torch_matmul"] = lambda: torch.matmul(Ad, Bt, out=Cd)
-    for fn in fns.values():
-        for _ in range(warmup):
+    warm, t_end = 0, time.perf_counter() + warmup_ms / 1e3
+    while warm < warmup or time.perf_counter() < t_end:
+        for fn in fns.values():
             fn()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        warm += 1
     times = {k: [] for k in fns}
     for _ in range(rounds):
         for key, fn in fns.items():
@@ -352,6 +358,7 @@ def run_gemm(att, torch, stream, reps: int, variants=GEMM_VARIANTS, warmup: int 
         if key.startswith("gemm_") and (best is None or tf > best[0]):
             best = (tf, key)
     out["gemm_best"] = best[1]
+    out["warmup_launches_each"] = warm
     return out
 
 
