@@ -597,6 +597,44 @@ __device__ __forceinline__ uint64_t chunk_element(const u32x4 v, uint32_t off, u
 }
 
 // Write one box from LDS image `lds` back through the map (inverse swizzle).
+// Every in-bounds element of a box image of 4- or 8-byte elements with
+// element stride 1 in dim 0, element-major: lane l of a wave takes element
+// l of each run of 64 consecutive box elements and passes its global
+// address and bits to f.  The rows of rank-1 and rank-2 maps are located
+// with one multiply-high per element.
+template <typename F>
+__device__ __forceinline__ void box_elements(const TmapImpl& m, const int32_t c[5], const uint8_t* lds, uint32_t nchunk,
+                                             uint32_t wave, uint32_t nwaves, F&& f) {
+    const uint32_t lane = lane_id();
+    const uint32_t sh = m.esize == 4 ? 2u : 1u;              // log2 of elements per chunk
+    const uint32_t nel = nchunk << sh;
+    const uint32_t rowel = m.cpr << sh;                       // elements per LDS row
+    const bool two_d = m.rank <= 2;
+    for (uint32_t e0 = wave * 64u; e0 < nel; e0 += nwaves * 64u) {
+        const uint32_t E = e0 + lane;
+        if (E >= nel) continue;
+        const uint32_t q = E >> sh, eo = E & ((1u << sh) - 1u);
+        int64_t g, rest_off;
+        if (two_d) {
+            const uint32_t row = fdiv(q, m.magic_cpr);
+            g = (int64_t)c[0] + (int64_t)(E - row * rowel);
+            const int64_t g1 = (int64_t)c[1] + (int64_t)row * m.es[1];
+            if (g1 < 0 || g1 >= m.dim[1]) continue;
+            rest_off = g1 * (int64_t)m.stride[0];
+        } else {
+            const ChunkLoc L = chunk_locate(m, c, q);
+            if (!L.rest_in) continue;
+            g = L.g0 + (int64_t)eo;
+            rest_off = L.rest_off;
+        }
+        if (g < 0 || g >= m.dim[0]) continue;
+        const uint8_t* src = lds + swz_chunk(q, m.swizzle) * 16u + (eo << (4u - sh));
+        const uint64_t bits = sh == 2u ? (uint64_t)*reinterpret_cast<const uint32_t*>(src)
+                                       : *reinterpret_cast<const uint64_t*>(src);
+        f(gptr(m.base + (uint64_t)rest_off) + g * m.esize, bits);
+    }
+}
+
 // Lane l of group grp handles logical chunk grp*64 + l so that global writes
 // are in address order; it reads the chunk's physical LDS slot.  Elements
 // outside the tensor are skipped; OP (ST_STORE, ST_ADD, ST_MIN, ST_MAX)
@@ -619,22 +657,57 @@ __device__ __forceinline__ uint32_t tile_store_issue(const TmapImpl& m, const in
             // bytes apart (the L2 then merges a line's atomics into one
             // request).  The result is the same: integer and min / max
             // updates commute, and float adds are unordered across boxes
-            // anyway.
-            const uint32_t epc = 16u / m.esize;
-            const uint32_t nel = nchunk * epc;
-            for (uint32_t e0 = wave * 64u; e0 < nel; e0 += nwaves * 64u) {
-                const uint32_t E = e0 + lane;
-                if (E >= nel) continue;
-                const uint32_t q = E / epc, eo = E % epc;
-                const ChunkLoc L = chunk_locate(m, c, q);
-                const int64_t g = L.g0 + (int64_t)eo;
-                if (!L.rest_in || g < 0 || g >= m.dim[0]) continue;
-                const uint8_t* src = lds + swz_chunk(q, m.swizzle) * 16u + eo * m.esize;
-                const uint64_t bits = m.esize == 4 ? (uint64_t)*reinterpret_cast<const uint32_t*>(src)
-                                                   : *reinterpret_cast<const uint64_t*>(src);
-                gbyte* dst = gptr(m.base + (uint64_t)L.rest_off) + g * m.esize;
-                if constexpr (OP == ST_ADD) reduce_add_element(m.dtype, dst, bits);
-                else reduce_minmax_element<OP == ST_MAX>(m.dtype, dst, bits);
+            // anyway.  Each element type gets a loop of its own: with
+            // nothing but non-returning atomics in it (integer add, min and
+            // max; float add outside its rare compare-and-swap cases), no
+            // iteration waits for the previous one's atomics to complete,
+            // as one loop holding every type's compare-and-swap paths did.
+            if constexpr (OP == ST_ADD) {
+                switch (m.dtype) {
+                case TMAP_U32: case TMAP_I32:
+                    box_elements(m, c, lds, nchunk, wave, nwaves,
+                                 [](gbyte* dst, uint64_t bits) { atomic_add_g<uint32_t>(dst, (uint32_t)bits); });
+                    break;
+                case TMAP_U64: case TMAP_I64:
+                    box_elements(m, c, lds, nchunk, wave, nwaves,
+                                 [](gbyte* dst, uint64_t bits) { atomic_add_g<uint64_t>(dst, bits); });
+                    break;
+                case TMAP_F32:
+                    box_elements(m, c, lds, nchunk, wave, nwaves, [](gbyte* dst, uint64_t bits) {
+                        float_add_atomic<float, uint32_t>(dst, (uint32_t)bits);
+                    });
+                    break;
+                default:
+                    box_elements(m, c, lds, nchunk, wave, nwaves, [](gbyte* dst, uint64_t bits) {
+                        float_add_atomic<double, uint64_t>(dst, bits);
+                    });
+                    break;
+                }
+            } else {
+                constexpr bool MX = OP == ST_MAX;
+                switch (m.dtype) {
+                case TMAP_I32:
+                    box_elements(m, c, lds, nchunk, wave, nwaves,
+                                 [](gbyte* dst, uint64_t bits) { reduce_minmax_element<MX>(TMAP_I32, dst, bits); });
+                    break;
+                case TMAP_U32:
+                    box_elements(m, c, lds, nchunk, wave, nwaves,
+                                 [](gbyte* dst, uint64_t bits) { reduce_minmax_element<MX>(TMAP_U32, dst, bits); });
+                    break;
+                case TMAP_I64:
+                    box_elements(m, c, lds, nchunk, wave, nwaves,
+                                 [](gbyte* dst, uint64_t bits) { reduce_minmax_element<MX>(TMAP_I64, dst, bits); });
+                    break;
+                case TMAP_U64:
+                    box_elements(m, c, lds, nchunk, wave, nwaves,
+                                 [](gbyte* dst, uint64_t bits) { reduce_minmax_element<MX>(TMAP_U64, dst, bits); });
+                    break;
+                default:
+                    box_elements(m, c, lds, nchunk, wave, nwaves, [&m](gbyte* dst, uint64_t bits) {
+                        reduce_minmax_element<MX>(m.dtype, dst, bits);
+                    });
+                    break;
+                }
             }
             wait_lgkm0();
             return 0;

@@ -100,3 +100,69 @@ def test_kernel_arguments_come_through_scalar_loads(tmp_path, src):
     assert len(bodies) > 3
     bad = {k: len(_argument_vector_loads(b)) for k, b in bodies.items() if _argument_vector_loads(b)}
     assert bad == {}, list(bad.items())[:5]
+
+
+def _loops(body: str) -> dict:
+    """Innermost-loop header -> the assembly lines of that loop's blocks,
+    from the compiler's loop annotations on block labels."""
+    import re
+    loops, header, lines = {}, None, []
+    for line in body.splitlines():
+        m = re.match(r"^\.L(BB\w+):\s*(?:;\s*(.*))?$", line)
+        if m:
+            if header is not None:
+                loops.setdefault(header, []).extend(lines)
+            ann = m.group(2) or ""
+            h = re.search(r"Header=(BB\w+)", ann)
+            header = m.group(1) if "Loop Header" in ann else (h.group(1) if h else None)
+            lines = []
+        else:
+            lines.append(line)
+    if header is not None:
+        loops.setdefault(header, []).extend(lines)
+    return loops
+
+
+def _atomic_loops_without_waits(body: str) -> tuple:
+    """(loops holding a non-returning integer atomic, those of them with no
+    vmcnt wait in any of their blocks)."""
+    import re
+    atom = re.compile(r"^\s*global_atomic_(add|smin|smax|umin|umax)(_x2)?\s")
+    with_atomic = [ls for ls in _loops(body).values() if any(atom.match(x) and " sc0" not in x for x in ls)]
+    free = [ls for ls in with_atomic if not any("s_waitcnt" in x and "vmcnt" in x for x in ls)]
+    return len(with_atomic), len(free)
+
+
+def test_reduce_element_loops_do_not_wait_on_atomics(tmp_path):
+    """No loop of the reduce kernels that issues non-returning integer
+    atomics (add, min, max) waits on vmcnt, so no iteration waits for the
+    previous one's atomics to complete (a loop that also held the other
+    types' compare-and-swap paths got such a wait, and a one-box int32 pass
+    took twice as long).  Checked on the gfx950 assembly, per reduce kernel,
+    after the loop scanner is checked on planted loops."""
+    waits = "\n".join(["k:", ".LBB0_1:  ; =>This Inner Loop Header: Depth=1", "\ts_waitcnt vmcnt(0)",
+                       "\tglobal_atomic_add v[2:3], v4, off", "\ts_cbranch_scc1 .LBB0_1", "\ts_endpgm"])
+    assert _atomic_loops_without_waits(waits) == (1, 0)
+    clean = waits.replace("\ts_waitcnt vmcnt(0)\n", "")
+    assert _atomic_loops_without_waits(clean) == (1, 1)
+    split = "\n".join(["k:", ".LBB0_1:  ; =>This Inner Loop Header: Depth=1", "\tv_add_u32 v1, v1, v2",
+                       ".LBB0_2:  ;   in Loop: Header=BB0_1 Depth=1", "\ts_waitcnt vmcnt(0)",
+                       "\tglobal_atomic_smax v[2:3], v4, off", "\ts_cbranch_scc1 .LBB0_1", "\ts_endpgm"])
+    assert _atomic_loops_without_waits(split) == (1, 0)
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not installed")
+    out = tmp_path / "kernels_tile.s"
+    subprocess.check_call([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17",
+                           "-I" + os.path.join(ROOT, "include"),
+                           "-I" + os.path.join(ROOT, "async_tensor_tile_amd", "csrc"),
+                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics",
+                           "-Wno-unused-command-line-argument", "--cuda-device-only", "-S",
+                           os.path.join(ROOT, "async_tensor_tile_amd", "csrc", "kernels_tile.hip"), "-o", str(out)],
+                          stderr=subprocess.DEVNULL)
+    bodies = _kernel_bodies(out.read_text())
+    for op in (1, 2, 3):   # add, min, max
+        name = f"_ZN3att12k_tile_storeILi{op}EEEv6tmap_tPKiPKh"
+        assert name in bodies, sorted(bodies)[:8]
+        n, free = _atomic_loops_without_waits(bodies[name])
+        assert n > 0 and free == n, (op, n, free)
