@@ -49,11 +49,17 @@ struct GemmArgs {
     uint32_t xcd;        // 0: plain order, 1: contiguous ranges per XCD, 2: a 2-D block of tiles per XCD
     uint32_t blk_m, blk_n;   // xcd == 2: tile rows / columns of each XCD's block
     uint32_t c_staged;       // 1: C written back through Cm (LDS image + tile store)
-    TmapImpl Cm;             // C map: dims {N, M}, box {64, 256}, 128B_K256 swizzle
+    TmapImpl Cm;             // C map: dims {N, M}, box {64, 256}, 128B swizzle
 };
 
+// Swizzle of the staged epilogue's C box images: the 128-byte mode, whose
+// key (row % 8) differs across any 8 consecutive rows, so the 16-byte writes
+// of 8 lanes holding one chunk column of 8 consecutive rows hit 8 distinct
+// bank groups.
+constexpr uint32_t kCSwizzle = TMAP_SWIZZLE_128B;
+
 // The C map of the staged epilogue: dims {N, M} with a row stride of
-// ld_bytes, box {64, 256}, bf16, 128B_K256 swizzle, zero fill -- exactly
+// ld_bytes, box {64, 256}, bf16, 128B swizzle, zero fill -- exactly
 // what tmap_encode makes of those arguments (the host compares the two
 // before choosing the staged epilogue).  Built here from constants but the
 // base, stride and dims, so the box store inlined into the epilogue folds
@@ -77,7 +83,7 @@ __host__ __device__ __forceinline__ TmapImpl gemm_c_box_map(uint64_t base, uint6
     t.rank = 2;
     t.dtype = TMAP_BF16;
     t.esize = 2;
-    t.swizzle = TMAP_SWIZZLE_128B_K256;
+    t.swizzle = kCSwizzle;
     t.oob = TMAP_OOB_ZERO;
     t.fill_idx = FILL_ZERO;
     t.cpr = 8;
@@ -347,8 +353,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI]
         // epilogue does ([MLC] "waiting for a TMA store": write the output
         // tile to shared memory, store it, wait on the store group, then
         // reuse the buffer).  The 256 x 256 tile is four 256 x 64 boxes of
-        // the C map (128-byte rows, 16-row XOR key: the 8-byte writes of rows
-        // r and r+1..r+15 land in distinct bank groups).  Two LDS stages of
+        // the C map (128-byte rows, 128-byte swizzle).  With 16 x 16 tiles
+        // a lane holds four consecutive columns of one row per tile; lanes
+        // l and l + 16 swap halves of two neighbouring tiles
+        // (v_permlane16_swap), so that each lane holds a whole 16-byte
+        // chunk (eight columns of one row) and writes it with one 16-byte
+        // LDS store: 8 lanes of a store cover one chunk column of 8
+        // consecutive rows, 8 distinct bank groups under the row % 8 key.
+        // (With 32 x 32 tiles the lanes write their 8-byte pieces.)  Two LDS stages of
         // one box each are used twice: in round r the waves of column half
         // wn write box 2*wn + r (their accumulator columns j*MI with
         // j in [r*NJ/2, (r+1)*NJ/2)) into stage wn, then every wave stores
@@ -359,6 +371,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI]
         // MFMAs).
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         typedef __attribute__((address_space(3))) u32x2 lds_u2_t;
+        typedef __attribute__((address_space(3))) u32x4 lds_u4_t;
         constexpr uint32_t kStage = 256u * 128u;      // one C box image
         const TmapImpl cm = gemm_c_box_map(g.Cm.base, g.Cm.stride[0], (uint32_t)g.Cm.dim[0], (uint32_t)g.Cm.dim[1]);
         const tmap_t& cmap = reinterpret_cast<const tmap_t&>(cm);
@@ -371,24 +384,59 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI]
                 store_wait_read<0>(sg);               // this wave's stores no longer read either stage
                 wg_barrier();                         // ... nor any other wave's
             }
+            if constexpr (MI == 16) {
+                static_assert(NQ == 1 && NJ % 4 == 0, "16 x 16 tiles, pairs of tiles per round half");
+                // Before the swap lane group lg = lane / 16 holds columns
+                // 4 lg .. 4 lg + 3 of tiles j0 and j0 + 1; the swap trades the
+                // odd groups' pieces of j0 for the even groups' pieces of
+                // j0 + 1, after which group lg holds columns 8 (lg >> 1) ..
+                // + 7 of tile j0 + (lg & 1): four from the first result (the
+                // even group's), four from the second (the odd group's).
+                const uint32_t lg = lane >> 4;
+                const uint32_t row = rloc;                       // + i * 16 below
+                const uint32_t tsel = lg & 1u, half = lg >> 1;
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
+                for (int i = 0; i < NI; ++i)
 #pragma unroll
-                for (int jj = 0; jj < NJ / 2; ++jj)
+                    for (int jp = 0; jp < NJ / 4; ++jp) {
+                        const int j0 = r * (NJ / 2) + 2 * jp;
+                        uint32_t t0[2], t1[2];
 #pragma unroll
-                    for (int q = 0; q < NQ; ++q) {
-                        const int j = r * (NJ / 2) + jj;
-                        const uint32_t row = rloc + (uint32_t)i * (uint32_t)MI;
-                        const uint32_t col = cloc + (uint32_t)j * (uint32_t)MI + (uint32_t)q * 8u;
-                        const uint32_t chunk = row * 8u + ((col & 63u) >> 3);
-                        const uint32_t addr = lds0 + wn * kStage + (swz_chunk(chunk, TMAP_SWIZZLE_128B_K256) << 4) +
-                                              (col & 7u) * 2u;
-                        const f32x2 lo = {acc[i][j][4 * q], acc[i][j][4 * q + 1]};
-                        const f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                        const u32x2 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
-                                         __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
-                        *(lds_u2_t*)(uintptr_t)addr = v;
+                        for (int h = 0; h < 2; ++h) {
+                            const f32x2 a = {acc[i][j0][2 * h], acc[i][j0][2 * h + 1]};
+                            const f32x2 b = {acc[i][j0 + 1][2 * h], acc[i][j0 + 1][2 * h + 1]};
+                            t0[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
+                            t1[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2));
+                        }
+                        const auto s0 = __builtin_amdgcn_permlane16_swap(t0[0], t1[0], false, false);
+                        const auto s1 = __builtin_amdgcn_permlane16_swap(t0[1], t1[1], false, false);
+                        const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+                        const uint32_t rr = row + (uint32_t)i * 16u;
+                        const uint32_t col = (uint32_t)(j0 + (int)tsel) * 16u + half * 8u;  // tile-local column
+                        const uint32_t chunk = rr * 8u + ((col & 63u) >> 3);
+                        const uint32_t addr = lds0 + wn * kStage + (swz_chunk(chunk, kCSwizzle) << 4);
+                        *(lds_u4_t*)(uintptr_t)addr = v;
                     }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < NJ / 2; ++jj)
+#pragma unroll
+                        for (int q = 0; q < NQ; ++q) {
+                            const int j = r * (NJ / 2) + jj;
+                            const uint32_t row = rloc + (uint32_t)i * (uint32_t)MI;
+                            const uint32_t col = cloc + (uint32_t)j * (uint32_t)MI + (uint32_t)q * 8u;
+                            const uint32_t chunk = row * 8u + ((col & 63u) >> 3);
+                            const uint32_t addr = lds0 + wn * kStage + (swz_chunk(chunk, kCSwizzle) << 4) +
+                                                  (col & 7u) * 2u;
+                            const f32x2 lo = {acc[i][j][4 * q], acc[i][j][4 * q + 1]};
+                            const f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                            const u32x2 v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                                             __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
+                            *(lds_u2_t*)(uintptr_t)addr = v;
+                        }
+            }
             wait_lgkm0();
             wg_barrier();                             // both box images complete
 #pragma unroll
@@ -978,7 +1026,7 @@ static tmap_status gemm_run(const tmap_t* A, const tmap_t* B, void* d_C, uint32_
         const uint64_t cdim[2] = {N, M};
         const uint64_t cstride[1] = {(uint64_t)ldc * 2u};
         const uint32_t cbox[2] = {64u, (uint32_t)kTM};
-        if (tmap_encode(&cm, TMAP_BF16, 2, d_C, cdim, cstride, cbox, nullptr, TMAP_SWIZZLE_128B_K256,
+        if (tmap_encode(&cm, TMAP_BF16, 2, d_C, cdim, cstride, cbox, nullptr, (tmap_swizzle)kCSwizzle,
                         TMAP_OOB_ZERO) == TMAP_OK) {
             g.Cm = load_map(&cm);
             const TmapImpl want = gemm_c_box_map(g.Cm.base, g.Cm.stride[0], N, M);
