@@ -635,6 +635,176 @@ __device__ __forceinline__ void box_elements(const TmapImpl& m, const int32_t c[
     }
 }
 
+// Reductions on 8- and 16-bit elements with element stride 1 in dim 0:
+// lane l takes one aligned 32-bit word of global memory, so that one atomic
+// updates all its elements.  A box row of L0 elements starting at c0 touches
+// words floor(c0 / EPW) .. floor((c0 + L0 - 1) / EPW); with an origin that is
+// not word-aligned a word's elements come from two neighbouring box
+// elements, read from LDS one by one.  Elements past either end of the box
+// row or of dim 0 are left alone.  For maps of rank 1 or 2 the rows and
+// elements inside the tensor are worked out once per box, so a word costs a
+// multiply-high and a few 32-bit operations; higher ranks locate each
+// word's row with chunk_locate.
+template <int OP, uint32_t ESZ, bool TWO_D>
+__device__ __forceinline__ void reduce_words(const TmapImpl& m, const int32_t c[5], const uint8_t* lds,
+                                             uint32_t nchunk, uint32_t wave, uint32_t nwaves) {
+    constexpr uint32_t EPW = 4u / ESZ;                          // elements per word
+    const uint32_t lane = lane_id();
+    const uint32_t L0 = m.L[0], cpr = m.cpr;
+    const int64_t c0 = c[0];
+    const int64_t w_first = c0 >= 0 ? c0 / EPW : -((-c0 + EPW - 1) / EPW);
+    const uint32_t head = (uint32_t)(c0 - w_first * (int64_t)EPW);     // 0 .. EPW-1
+    const uint32_t wpr = (head + L0 + EPW - 1u) / EPW;                 // words per box row
+    const uint32_t nrow = fdiv(nchunk, m.magic_cpr);
+    const uint32_t nwd = nrow * wpr;
+    // ceil(2^32 / wpr) for fdiv, from 32-bit arithmetic (a 64-bit division
+    // here is a long software routine run by every wave)
+    const uint32_t magic_wpr = wpr == 1u ? 0u : 0xFFFFFFFFu / wpr + 1u;
+    // box elements of a row inside dim 0: [e_lo, e_hi)
+    const int64_t elo = c0 < 0 ? (-c0 < (int64_t)L0 ? -c0 : (int64_t)L0) : 0;
+    int64_t ehi = m.dim[0] - c0;
+    if (ehi > (int64_t)L0) ehi = L0;
+    if (ehi < elo) ehi = elo;
+    const int32_t e_lo = (int32_t)elo, e_hi = (int32_t)ehi;
+    // rank <= 2: image rows inside dim 1, [r_lo, r_hi), and row r's address
+    uint32_t r_lo = 0, r_hi = nrow;
+    int64_t rb0 = 0, rstep = 0;
+    if constexpr (TWO_D) {
+        // row r is inside iff 0 <= c1 + r * es1 < dim1; 32-bit divisions
+        // only, the upper bound clamped to the image first
+        const int64_t c1 = c[1];
+        const uint32_t es1 = m.es[1];
+        const int64_t below = c1 < 0 ? -c1 : 0;                       // rows needed to reach 0
+        const uint64_t lo = below >= (int64_t)nrow * es1 ? nrow : ((uint32_t)below + es1 - 1u) / es1;
+        const int64_t avail = m.dim[1] - c1;                          // coordinates left in dim 1
+        const uint64_t hi = avail <= 0 ? 0u
+                          : (avail >= (int64_t)nrow * es1 ? nrow : ((uint32_t)avail + es1 - 1u) / es1);
+        r_hi = (uint32_t)hi;
+        r_lo = (uint32_t)(lo < hi ? lo : hi);
+        rb0 = (int64_t)m.base + c1 * (int64_t)m.stride[0] + w_first * 4;
+        rstep = (int64_t)es1 * (int64_t)m.stride[0];
+    }
+    // Word W of the box image (W < nwd): its address, its box elements
+    // packed into a word and which of them the box covers (inb bit h for
+    // element h); inb == 0 if none is inside.
+    auto word_at = [&](uint32_t W, ATT_GLOBAL uint32_t*& wp, uint32_t& vw, uint32_t& inb) {
+        if constexpr (TWO_D) {
+            // no branch on W: a word past the image or in a row outside the
+            // tensor is computed from clamped indices and gets inb == 0
+            const uint32_t Wc = W < nwd ? W : nwd - 1u;
+            const uint32_t row = fdiv(Wc, magic_wpr), wi = Wc - row * wpr;
+            const uint32_t q_row = row * cpr;
+            const int32_t e0 = (int32_t)(wi * EPW) - (int32_t)head;    // box element of the word's element 0
+            const int32_t lo = e_lo - e0 > 0 ? e_lo - e0 : 0;
+            const int32_t hi = e_hi - e0 < (int32_t)EPW ? (e_hi - e0 > 0 ? e_hi - e0 : 0) : (int32_t)EPW;
+            const uint32_t span = hi > lo ? ((1u << hi) - 1u) & ~((1u << lo) - 1u) : 0u;
+            inb = (W < nwd && row >= r_lo && row < r_hi) ? span : 0u;
+            uint32_t keep = 0;
+#pragma unroll
+            for (uint32_t h = 0; h < EPW; ++h) keep |= ((inb >> h) & 1u) * ((ESZ == 2 ? 0xFFFFu : 0xFFu) << (h * ESZ * 8u));
+            if (head == 0) {
+                // a word-aligned row: the word's elements sit in one 16-byte chunk
+                const uint32_t eb = (uint32_t)e0 * ESZ;
+                vw = *reinterpret_cast<const uint32_t*>(lds + swz_chunk(q_row + (eb >> 4), m.swizzle) * 16u + (eb & 15u)) &
+                     keep;
+            } else {
+                uint32_t v = 0;
+#pragma unroll
+                for (uint32_t h = 0; h < EPW; ++h) {
+                    int32_t e = e0 + (int32_t)h;
+                    e = e < 0 ? 0 : (e >= (int32_t)L0 ? (int32_t)L0 - 1 : e);
+                    const uint32_t eb = (uint32_t)e * ESZ;
+                    const uint8_t* src = lds + swz_chunk(q_row + (eb >> 4), m.swizzle) * 16u + (eb & 15u);
+                    v |= (ESZ == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(src) : (uint32_t)*src) << (h * ESZ * 8u);
+                }
+                vw = v & keep;
+            }
+            wp = (ATT_GLOBAL uint32_t*)gptr((uint64_t)(rb0 + (int64_t)row * rstep + (int64_t)wi * 4));
+        } else {
+            wp = nullptr;
+            vw = 0;
+            inb = 0;
+            if (W >= nwd) return;
+            const uint32_t row = fdiv(W, magic_wpr), wi = W - row * wpr;
+            const uint32_t q_row = row * cpr;
+            const int32_t e0 = (int32_t)(wi * EPW) - (int32_t)head;
+            const ChunkLoc L = chunk_locate(m, c, q_row);
+            if (!L.rest_in) return;
+#pragma unroll
+            for (uint32_t h = 0; h < EPW; ++h) {
+                const int32_t e = e0 + (int32_t)h;
+                if (e >= e_lo && e < e_hi) inb |= 1u << h;
+            }
+            if (!inb) return;
+#pragma unroll
+            for (uint32_t h = 0; h < EPW; ++h) {
+                if (!(inb & (1u << h))) continue;
+                const uint32_t eb = (uint32_t)(e0 + (int32_t)h) * ESZ;
+                const uint8_t* src = lds + swz_chunk(q_row + (eb >> 4), m.swizzle) * 16u + (eb & 15u);
+                const uint32_t v = ESZ == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(src) : (uint32_t)*src;
+                vw |= v << (h * ESZ * 8u);
+            }
+            wp = (ATT_GLOBAL uint32_t*)gptr((uint64_t)((int64_t)m.base + L.rest_off + (w_first + (int64_t)wi) * 4));
+        }
+    };
+    // WB words per lane per step: their LDS reads, then their atomics, are
+    // in flight together (the packed adds return the old value, which is
+    // only looked at after all of them have been issued).  Measured on the
+    // 4096^2 bf16 pass: two words per lane run 4-6 % faster than four and
+    // 20-50 % faster than 8-16 (the returning adds queue at the L2), at 1024
+    // to 8192 boxes.
+    constexpr uint32_t WB = 2;
+    if constexpr (OP == ST_ADD && ESZ == 2) {
+        if (m.dtype == TMAP_BF16 || m.dtype == TMAP_F16) {
+            // The packed hardware add, which rounds the exact sum once to
+            // nearest even like the f32-then-round definition (f32 carries
+            // more than 2p + 2 bits); a half outside the box (a word cut by
+            // the box row's ends) gets -0 added, which leaves it as it was.
+            // A NaN sum keeps an operand's payload or sign there; the old
+            // value the add returns tells when that happened, and that half
+            // is then set to the canonical NaN.  It also tells whether a half
+            // outside the box held a signalling NaN (the add quiets it), to
+            // put it back.
+            const bool bf = m.dtype == TMAP_BF16;
+            for (uint32_t w0 = wave * 64u * WB; w0 < nwd; w0 += nwaves * 64u * WB) {
+                ATT_GLOBAL uint32_t* wp[WB];
+                uint32_t vw[WB], inb[WB], old[WB];
+#pragma unroll
+                for (uint32_t b = 0; b < WB; ++b) word_at(w0 + b * 64u + lane, wp[b], vw[b], inb[b]);
+#pragma unroll
+                for (uint32_t b = 0; b < WB; ++b) {
+                    old[b] = 0;
+                    if (!inb[b]) continue;
+                    const uint32_t v = vw[b] | ((inb[b] & 1u) ? 0u : 0x8000u) | ((inb[b] & 2u) ? 0u : 0x80000000u);
+                    old[b] = bf ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2bf16(
+                                                                   (ATT_GLOBAL bf16x2_t*)wp[b], __builtin_bit_cast(bf16x2_t, v)))
+                                : __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2f16(
+                                                                   (ATT_GLOBAL f16x2_t*)wp[b], __builtin_bit_cast(f16x2_t, v)));
+                }
+#pragma unroll
+                for (uint32_t b = 0; b < WB; ++b) {
+                    if (!inb[b]) continue;
+                    const uint32_t nan = ((inb[b] & 1u) && half_sum_nan(bf, old[b], vw[b]) ? 1u : 0u) |
+                                         ((inb[b] & 2u) && half_sum_nan(bf, old[b] >> 16, vw[b] >> 16) ? 2u : 0u);
+                    if (nan) canon_nan_halves(bf, wp[b], nan);
+                    if (inb[b] == 1u && half_is_snan(bf, old[b] >> 16)) restore_half(bf, wp[b], 16u, old[b] >> 16);
+                    if (inb[b] == 2u && half_is_snan(bf, old[b] & 0xFFFFu)) restore_half(bf, wp[b], 0u, old[b] & 0xFFFFu);
+                }
+            }
+            return;
+        }
+    }
+    for (uint32_t w0 = wave * 64u * WB; w0 < nwd; w0 += nwaves * 64u * WB) {
+        ATT_GLOBAL uint32_t* wp[WB];
+        uint32_t vw[WB], inb[WB];
+#pragma unroll
+        for (uint32_t b = 0; b < WB; ++b) word_at(w0 + b * 64u + lane, wp[b], vw[b], inb[b]);
+#pragma unroll
+        for (uint32_t b = 0; b < WB; ++b)
+            if (inb[b]) reduce_word<OP>(m.dtype, ESZ, wp[b], vw[b], inb[b]);
+    }
+}
+
 // Lane l of group grp handles logical chunk grp*64 + l so that global writes
 // are in address order; it reads the chunk's physical LDS slot.  Elements
 // outside the tensor are skipped; OP (ST_STORE, ST_ADD, ST_MIN, ST_MAX)
@@ -713,109 +883,12 @@ __device__ __forceinline__ uint32_t tile_store_issue(const TmapImpl& m, const in
             return 0;
         }
         if (m.es[0] == 1) {
-            // 8- and 16-bit elements: lane l takes one aligned 32-bit word of
-            // global memory, so that one atomic updates all its elements.  A
-            // box row of L0 elements starting at c0 touches words
-            // floor(c0 / epw) .. floor((c0 + L0 - 1) / epw); with an origin
-            // that is not word-aligned a word's elements come from two
-            // neighbouring box elements, read from LDS one by one.  Elements
-            // past either end of the box row or of dim 0 are left alone.
-            const uint32_t esz = m.esize, epw = 4u / esz, L0 = m.L[0];
-            const int64_t c0 = c[0];
-            const int64_t w_first = c0 >= 0 ? c0 / epw : -((-c0 + epw - 1) / epw);
-            const uint32_t head = (uint32_t)(c0 - w_first * (int64_t)epw);     // 0 .. epw-1
-            const uint32_t wpr = (head + L0 + epw - 1u) / epw;                 // words per box row
-            const uint32_t cpr = m.cpr;                                         // chunks per box row
-            const uint32_t nrow = nchunk / cpr;
-            const uint32_t nwd = nrow * wpr;
-            // WB words per lane per step: their LDS reads, then their atomics,
-            // are in flight together (the packed adds return the old value,
-            // which is only looked at after all of them have been issued).
-            // Measured on the 4096^2 bf16 pass: two words per lane run 4-6 %
-            // faster than four and 20-50 % faster than 8-16 (the returning
-            // adds queue at the L2), at 1024 to 8192 boxes.  With a
-            // word-aligned origin a word's elements sit in one 16-byte chunk
-            // and are read from LDS as one 32-bit word.
-            constexpr uint32_t WB = 2;
-            const bool two_d = m.rank <= 2;
-            for (uint32_t w0 = wave * 64u * WB; w0 < nwd; w0 += nwaves * 64u * WB) {
-                ATT_GLOBAL uint32_t* wp[WB];
-                uint32_t vw[WB], inb[WB];
-#pragma unroll
-                for (uint32_t b = 0; b < WB; ++b) {
-                    const uint32_t W = w0 + b * 64u + lane;
-                    wp[b] = nullptr;
-                    vw[b] = 0;
-                    inb[b] = 0;
-                    if (W >= nwd) continue;
-                    const uint32_t row = W / wpr, wi = W - row * wpr;
-                    const uint32_t q_row = row * cpr;
-                    const ChunkLoc L = two_d ? chunk_locate_2d(m, c, q_row) : chunk_locate(m, c, q_row);
-                    if (!L.rest_in) continue;
-                    const int64_t g = (w_first + (int64_t)wi) * (int64_t)epw;  // first element of the word
-                    uint32_t whole = 0;
-                    if (head == 0) {
-                        const uint32_t eb = (uint32_t)(g - c0) * esz;
-                        whole = *reinterpret_cast<const uint32_t*>(lds + swz_chunk(q_row + (eb >> 4), m.swizzle) * 16u +
-                                                                   (eb & 15u));
-                    }
-                    for (uint32_t h = 0; h < epw; ++h) {
-                        const int64_t gg = g + (int64_t)h;
-                        const int64_t e = gg - c0;                             // box element in the row
-                        if (e < 0 || e >= (int64_t)L0 || gg < 0 || gg >= m.dim[0]) continue;
-                        uint32_t v;
-                        if (head == 0) {
-                            v = (whole >> (h * esz * 8u)) & (esz == 2 ? 0xFFFFu : 0xFFu);
-                        } else {
-                            const uint32_t eb = (uint32_t)e * esz;
-                            const uint8_t* src = lds + swz_chunk(q_row + (eb >> 4), m.swizzle) * 16u + (eb & 15u);
-                            v = esz == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(src) : (uint32_t)*src;
-                        }
-                        vw[b] |= v << (h * esz * 8u);
-                        inb[b] |= 1u << h;
-                    }
-                    if (inb[b])
-                        wp[b] = (ATT_GLOBAL uint32_t*)(gptr(m.base + (uint64_t)L.rest_off) + g * (int64_t)esz);
-                }
-                if constexpr (OP == ST_ADD) {
-                    // The packed hardware add, which rounds the exact sum
-                    // once to nearest even like the f32-then-round
-                    // definition (f32 carries more than 2p + 2 bits); a half
-                    // outside the box (a word cut by the box row's ends)
-                    // gets -0 added, which leaves it as it was.  A NaN sum
-                    // keeps an operand's payload or sign there; the old
-                    // value the add returns tells when that happened, and
-                    // that half is then set to the canonical NaN.  It also
-                    // tells whether a half outside the box held a
-                    // signalling NaN (the add quiets it), to put it back.
-                    if (m.dtype == TMAP_BF16 || m.dtype == TMAP_F16) {
-                        const bool bf = m.dtype == TMAP_BF16;
-                        uint32_t old[WB];
-#pragma unroll
-                        for (uint32_t b = 0; b < WB; ++b) {
-                            old[b] = 0;
-                            if (!inb[b]) continue;
-                            const uint32_t v = vw[b] | ((inb[b] & 1u) ? 0u : 0x8000u) | ((inb[b] & 2u) ? 0u : 0x80000000u);
-                            old[b] = bf ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2bf16(
-                                                                           (ATT_GLOBAL bf16x2_t*)wp[b], __builtin_bit_cast(bf16x2_t, v)))
-                                        : __builtin_bit_cast(uint32_t, __builtin_amdgcn_global_atomic_fadd_v2f16(
-                                                                           (ATT_GLOBAL f16x2_t*)wp[b], __builtin_bit_cast(f16x2_t, v)));
-                        }
-#pragma unroll
-                        for (uint32_t b = 0; b < WB; ++b) {
-                            if (!inb[b]) continue;
-                            const uint32_t nan = ((inb[b] & 1u) && half_sum_nan(bf, old[b], vw[b]) ? 1u : 0u) |
-                                                 ((inb[b] & 2u) && half_sum_nan(bf, old[b] >> 16, vw[b] >> 16) ? 2u : 0u);
-                            if (nan) canon_nan_halves(bf, wp[b], nan);
-                            if (inb[b] == 1u && half_is_snan(bf, old[b] >> 16)) restore_half(bf, wp[b], 16u, old[b] >> 16);
-                            if (inb[b] == 2u && half_is_snan(bf, old[b] & 0xFFFFu)) restore_half(bf, wp[b], 0u, old[b] & 0xFFFFu);
-                        }
-                        continue;
-                    }
-                }
-#pragma unroll
-                for (uint32_t b = 0; b < WB; ++b)
-                    if (inb[b]) reduce_word<OP>(m.dtype, esz, wp[b], vw[b], inb[b]);
+            if (m.esize == 2) {
+                if (m.rank <= 2) reduce_words<OP, 2, true>(m, c, lds, nchunk, wave, nwaves);
+                else reduce_words<OP, 2, false>(m, c, lds, nchunk, wave, nwaves);
+            } else {
+                if (m.rank <= 2) reduce_words<OP, 1, true>(m, c, lds, nchunk, wave, nwaves);
+                else reduce_words<OP, 1, false>(m, c, lds, nchunk, wave, nwaves);
             }
             wait_lgkm0();
             return 0;
