@@ -360,12 +360,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI]
         // chunk (eight columns of one row) and writes it with one 16-byte
         // LDS store: 8 lanes of a store cover one chunk column of 8
         // consecutive rows, 8 distinct bank groups under the row % 8 key.
-        // (With 32 x 32 tiles the lanes write their 8-byte pieces.)  Two LDS stages of
-        // one box each are used twice: in round r the waves of column half
-        // wn write box 2*wn + r (their accumulator columns j*MI with
-        // j in [r*NJ/2, (r+1)*NJ/2)) into stage wn, then every wave stores
-        // its share of both boxes as two store groups; round 1 refills the
-        // stages once those groups no longer read them.  The box store clips
+        // (With 32 x 32 tiles the lanes write their 8-byte pieces.)  Two
+        // LDS stages of one box each are used twice: in pass r the waves of
+        // column half wn write box 2*wn + r (their accumulator columns j*MI
+        // with j in [r*NJ/2, (r+1)*NJ/2)) into stage wn, then every wave
+        // stores its share of both boxes as two store groups; pass 1 refills
+        // the stages once those groups no longer read them.  The box store clips
         // at the M / N edges.  The ring is free once every wave has passed
         // the first barrier (all fragment reads completed before the last
         // MFMAs).
@@ -385,7 +385,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, AccT (&acc)[NI]
                 wg_barrier();                         // ... nor any other wave's
             }
             if constexpr (MI == 16) {
-                static_assert(NQ == 1 && NJ % 4 == 0, "16 x 16 tiles, pairs of tiles per round half");
+                static_assert(NQ == 1 && NJ % 4 == 0, "16 x 16 tiles, pairs of tiles per pass");
                 // Before the swap lane group lg = lane / 16 holds columns
                 // 4 lg .. 4 lg + 3 of tiles j0 and j0 + 1; the swap trades the
                 // odd groups' pieces of j0 for the even groups' pieces of
@@ -890,7 +890,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu
         wait_lgkm0();
         wg_barrier();
         // (the layout hints keep the common path free of taken branches:
-        // 0.5 % on the 8192^3 GEMM in interleaved rounds)
+        // 0.5 % on the 8192^3 GEMM, timed interleaved with the plain form)
         if (__builtin_expect(t + 1u == NT, 0)) {
             // Rows 4.. of the last sub-step, inside the body, where the
             // accumulators still sit; then drain (the clamped copies too)
