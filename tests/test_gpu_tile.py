@@ -259,6 +259,41 @@ def test_random_maps_load_store_reduce(seed):
         np.testing.assert_array_equal(to_host(acc)[: c.buf.size], hw, err_msg=op)
 
 
+@pytest.mark.parametrize("dtype", ["u8", "u16", "f16", "bf16"])
+@pytest.mark.parametrize("rank", [1, 2])
+@pytest.mark.parametrize("seed", range(6))
+def test_word_reduce_rank12_edges(dtype, rank, seed):
+    """8- and 16-bit reductions on rank-1 and rank-2 maps, the path that
+    works out a box's rows and elements inside the tensor once per box:
+    origins from fully below to fully above both dimensions, element strides
+    1-3 in dim 1, odd and even dim-0 origins (words cut by the box row's
+    ends).  Integer add, and min / max of every type (NaNs and signed zeros
+    among the random bit patterns), bit-exact against the oracle."""
+    g = synthgen.rng(30000 + 1000 * ["u8", "u16", "f16", "bf16"].index(dtype) + 100 * rank + seed)
+    while True:
+        c = random_case(g, dtype=dtype, rank=rank)
+        if c.estride[0] == 1:
+            break
+    coords = sweep_coords(g, c, 32)
+    say("case", dtype, rank, seed, c.dims, c.strides, c.box, c.estride, c.swizzle)
+    om = oracle.Map(c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle)
+    assert om.validate() == "OK"
+    probe = encode(to_dev(c.buf), c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, "zero")
+    bb = att.tmap_box_bytes(probe)
+    imgs = synthgen.random_bytes(seed + 40 * rank + 3, len(coords) * bb).reshape(len(coords), bb)
+    ops = (["add"] if dtype in ("u8", "u16") else []) + ["min", "max"]
+    for op in ops:
+        acc = to_dev(c.buf)
+        ma = encode(acc, c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, "zero")
+        att.tile_reduce(ma, op, to_dev(coords), len(coords), to_dev(imgs), stream())
+        hw = c.buf.copy()
+        if op == "add":
+            om.reduce_add(hw, coords, imgs)
+        else:
+            om.reduce(hw, coords, imgs, op)
+        np.testing.assert_array_equal(to_host(acc)[: c.buf.size], hw, err_msg=op)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32", "f64"])
 def test_float_reduce_single_contribution_exact(dtype):
     """Non-overlapping boxes: one IEEE addition per element, rounded once;
