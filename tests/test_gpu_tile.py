@@ -259,17 +259,20 @@ def test_random_maps_load_store_reduce(seed):
         np.testing.assert_array_equal(to_host(acc)[: c.buf.size], hw, err_msg=op)
 
 
-@pytest.mark.parametrize("dtype", ["u8", "u16", "f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["u8", "u16", "f16", "bf16", "u32", "i32", "f32", "u64", "i64", "f64"])
 @pytest.mark.parametrize("rank", [1, 2])
 @pytest.mark.parametrize("seed", range(6))
-def test_word_reduce_rank12_edges(dtype, rank, seed):
-    """8- and 16-bit reductions on rank-1 and rank-2 maps, the path that
-    works out a box's rows and elements inside the tensor once per box:
+def test_reduce_rank12_edges(dtype, rank, seed):
+    """Reductions on rank-1 and rank-2 maps with element stride 1 in dim 0,
+    the paths that locate a box's rows with one multiply-high (8- and 16-bit
+    elements also work out the elements inside the tensor once per box):
     origins from fully below to fully above both dimensions, element strides
-    1-3 in dim 1, odd and even dim-0 origins (words cut by the box row's
-    ends).  Integer add, and min / max of every type (NaNs and signed zeros
-    among the random bit patterns), bit-exact against the oracle."""
-    g = synthgen.rng(30000 + 1000 * ["u8", "u16", "f16", "bf16"].index(dtype) + 100 * rank + seed)
+    1-3 in dim 1, odd and even dim-0 origins (for 8- and 16-bit elements,
+    words cut by the box row's ends).  Integer add, and min / max of every
+    type (NaNs and signed zeros among the random bit patterns), bit-exact
+    against the oracle."""
+    types = ["u8", "u16", "f16", "bf16", "u32", "i32", "f32", "u64", "i64", "f64"]
+    g = synthgen.rng(30000 + 1000 * types.index(dtype) + 100 * rank + seed)
     while True:
         c = random_case(g, dtype=dtype, rank=rank)
         if c.estride[0] == 1:
@@ -281,7 +284,7 @@ def test_word_reduce_rank12_edges(dtype, rank, seed):
     probe = encode(to_dev(c.buf), c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, "zero")
     bb = att.tmap_box_bytes(probe)
     imgs = synthgen.random_bytes(seed + 40 * rank + 3, len(coords) * bb).reshape(len(coords), bb)
-    ops = (["add"] if dtype in ("u8", "u16") else []) + ["min", "max"]
+    ops = (["add"] if dtype not in ("f16", "bf16", "f32", "f64") else []) + ["min", "max"]
     for op in ops:
         acc = to_dev(c.buf)
         ma = encode(acc, c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, "zero")
