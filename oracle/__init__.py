@@ -9,9 +9,16 @@ The arithmetic lives in ``oracle.c`` (plain C, scalar loops written from the
 reference pages); this module only compiles it with gcc and marshals NumPy
 arrays through ctypes.
 
-Parity status (see the comments in ``oracle.c`` for the passages followed):
-32-byte and 64-byte swizzle patterns are "parity unpinned" by a printed
-example -- the pages only name those modes -- and are pinned by invariants.
+Parity status (see the comments in ``oracle.c`` for the passages followed;
+the pins are in ``tests/test_oracle_pins.py``): the 128-byte swizzle, the
+worked examples and the byte-counted barrier trace are pinned by the pages'
+printed tables; the 32-byte and 64-byte swizzles, for which the pages print
+no pattern, by the grouping section's bank-sector criterion and its
+128-byte-unit key (the rejected row-index reading fails both); the _K256
+modes, this library's addition for a 64-bank LDS, by their definition from
+the base modes (the key of row r is the base key of row r // 2) and the
+sixteen-sector criterion; loads, stores and reductions by NumPy slicing,
+torch ``unfold`` and library adds on tiny cases.
 """
 from __future__ import annotations
 

@@ -138,7 +138,7 @@ def test_store_roundtrip_covers_exactly_inbounds(seed):
 
 
 def test_swizzle_k256_invariants():
-    """The 256-byte-key modes (not on the pages; parity unpinned): a XOR
+    """The 256-byte-key modes (this library's addition, not on the pages): a XOR
     permutation of the 16-byte sectors of each row whose key is constant per
     row, 16 B granularity kept, involution, keys repeating with twice the
     period of the pages' modes; the key of row r is the pages' key of row
@@ -167,7 +167,7 @@ def test_swizzle_k256_invariants():
 
 
 def test_swizzle_invariants_all_modes():
-    """32B/64B carry no printed example (parity unpinned); pin invariants:
+    """32B/64B carry no printed example (pinned by the bank criterion below); invariants:
     XOR permutation of 16-byte sectors inside each N-byte row, key constant
     along a row, 8-row period, row 0 identity, involution, every key value of
     the span used equally often within one atom; 128B equals the page rule."""
