@@ -228,9 +228,13 @@ tmap_status tile_store(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
 
 /* Reduce-add store ([HPC] "TMA reduce"): like tile_store but every in-bounds
  * element is added to global memory atomically.  Integer types wrap modulo
- * 2^w; f32/f64 use IEEE addition (round to nearest even), f16/bf16 add in
- * f32 and round once to nearest even.  Overlapping boxes are applied in an
- * unspecified order (bit-exact for integers).  Errors as tile_load. */
+ * 2^w; f32/f64 use IEEE addition (round to nearest even; a NaN result's
+ * payload is not fixed), f16/bf16 add in f32 and round once to nearest
+ * even, a NaN result being the type's canonical quiet NaN (0x7E00 /
+ * 0x7FC0).  Elements outside the box that share a 32-bit word with a 16- or
+ * 8-bit element inside it are left as they were.  Overlapping boxes are
+ * applied in an unspecified order (bit-exact for integers).  Errors as
+ * tile_load. */
 tmap_status tile_reduce_add(const tmap_t* m, const int32_t* d_coords, uint32_t nbox,
                             const void* d_lds_image_in, void* stream);
 
