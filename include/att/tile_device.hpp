@@ -597,16 +597,17 @@ __device__ __forceinline__ uint64_t chunk_element(const u32x4 v, uint32_t off, u
 }
 
 // Write one box from LDS image `lds` back through the map (inverse swizzle).
-// Every in-bounds element of a box image of 4- or 8-byte elements with
-// element stride 1 in dim 0, element-major: lane l of a wave takes element
-// l of each run of 64 consecutive box elements and passes its global
-// address and bits to f.  The rows of rank-1 and rank-2 maps are located
-// with one multiply-high per element.
+// Every in-bounds element of a box image with element stride 1 in dim 0,
+// element-major: lane l of a wave takes element l of each run of 64
+// consecutive box elements and passes its global address and bits to f, so
+// that a wave's accesses to one row fall on consecutive addresses whatever
+// the row's alignment.  The rows of rank-1 and rank-2 maps are located with
+// one multiply-high per element.
 template <typename F>
 __device__ __forceinline__ void box_elements(const TmapImpl& m, const int32_t c[5], const uint8_t* lds, uint32_t nchunk,
                                              uint32_t wave, uint32_t nwaves, F&& f) {
     const uint32_t lane = lane_id();
-    const uint32_t sh = m.esize == 4 ? 2u : 1u;              // log2 of elements per chunk
+    const uint32_t sh = m.esize == 1 ? 4u : m.esize == 2 ? 3u : m.esize == 4 ? 2u : 1u;   // log2 of elements per chunk
     const uint32_t nel = nchunk << sh;
     const uint32_t rowel = m.cpr << sh;                       // elements per LDS row
     const bool two_d = m.rank <= 2;
@@ -629,7 +630,9 @@ __device__ __forceinline__ void box_elements(const TmapImpl& m, const int32_t c[
         }
         if (g < 0 || g >= m.dim[0]) continue;
         const uint8_t* src = lds + swz_chunk(q, m.swizzle) * 16u + (eo << (4u - sh));
-        const uint64_t bits = sh == 2u ? (uint64_t)*reinterpret_cast<const uint32_t*>(src)
+        const uint64_t bits = sh == 4u ? (uint64_t)*src
+                            : sh == 3u ? (uint64_t)*reinterpret_cast<const uint16_t*>(src)
+                            : sh == 2u ? (uint64_t)*reinterpret_cast<const uint32_t*>(src)
                                        : *reinterpret_cast<const uint64_t*>(src);
         f(gptr(m.base + (uint64_t)rest_off) + g * m.esize, bits);
     }
@@ -889,6 +892,21 @@ __device__ __forceinline__ uint32_t tile_store_issue(const TmapImpl& m, const in
             } else {
                 if (m.rank <= 2) reduce_words<OP, 1, true>(m, c, lds, nchunk, wave, nwaves);
                 else reduce_words<OP, 1, false>(m, c, lds, nchunk, wave, nwaves);
+            }
+            wait_lgkm0();
+            return 0;
+        }
+    }
+    // A store whose rows do not start on a 16-byte boundary: one element per
+    // lane, consecutive lanes on consecutive addresses, rather than a
+    // 16-byte chunk per lane written an element at a time.
+    if constexpr (OP == ST_STORE) {
+        if (m.es[0] == 1 && (((int64_t)c[0] * m.esize) & 15) != 0) {
+            switch (m.esize) {
+            case 1: box_elements(m, c, lds, nchunk, wave, nwaves, [](gbyte* d, uint64_t b) { *d = (uint8_t)b; }); break;
+            case 2: box_elements(m, c, lds, nchunk, wave, nwaves, [](gbyte* d, uint64_t b) { *(ATT_GLOBAL uint16_t*)d = (uint16_t)b; }); break;
+            case 4: box_elements(m, c, lds, nchunk, wave, nwaves, [](gbyte* d, uint64_t b) { *(ATT_GLOBAL uint32_t*)d = (uint32_t)b; }); break;
+            default: box_elements(m, c, lds, nchunk, wave, nwaves, [](gbyte* d, uint64_t b) { *(ATT_GLOBAL uint64_t*)d = b; }); break;
             }
             wait_lgkm0();
             return 0;

@@ -297,6 +297,37 @@ def test_reduce_rank12_edges(dtype, rank, seed):
         np.testing.assert_array_equal(to_host(acc)[: c.buf.size], hw, err_msg=op)
 
 
+@pytest.mark.parametrize("dtype", ["u8", "u16", "f16", "bf16", "u32", "i32", "f32", "u64", "i64", "f64"])
+@pytest.mark.parametrize("rank", [1, 2, 3])
+@pytest.mark.parametrize("seed", range(3))
+def test_store_rows_at_any_alignment(dtype, rank, seed):
+    """Plain stores on maps with element stride 1 in dim 0, whose boxes
+    start anywhere in a row (rows not on a 16-byte boundary take one element
+    per lane): random images, one box per call so that overlapping boxes
+    end with the later one, against the oracle's stores in the same order
+    on a sentinel buffer (bytes outside every box untouched)."""
+    types = ["u8", "u16", "f16", "bf16", "u32", "i32", "f32", "u64", "i64", "f64"]
+    g = synthgen.rng(40000 + 1000 * types.index(dtype) + 100 * rank + seed)
+    while True:
+        c = random_case(g, dtype=dtype, rank=rank)
+        if c.estride[0] == 1:
+            break
+    coords = sweep_coords(g, c, 24)
+    say("case", dtype, rank, seed, c.dims, c.strides, c.box, c.estride, c.swizzle)
+    om = oracle.Map(c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, c.fill)
+    assert om.validate() == "OK"
+    dst = to_dev(np.full(c.buf.size, 0xA5, dtype=np.uint8))
+    md = encode(dst, c.dtype, c.dims, c.strides, c.box, c.estride, c.swizzle, c.fill)
+    bb = att.tmap_box_bytes(md)
+    imgs = synthgen.random_bytes(seed + 50 * rank + 5, len(coords) * bb).reshape(len(coords), bb)
+    cd, di = to_dev(coords), to_dev(imgs)
+    for i in range(len(coords)):
+        att.tile_store(md, cd[i * rank * 4:], 1, di[i * bb:], stream())
+    hw = np.full(c.buf.size, 0xA5, dtype=np.uint8)
+    om.store(hw, coords, imgs)
+    np.testing.assert_array_equal(to_host(dst), hw)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32", "f64"])
 def test_float_reduce_single_contribution_exact(dtype):
     """Non-overlapping boxes: one IEEE addition per element, rounded once;
