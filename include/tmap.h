@@ -384,11 +384,12 @@ tmap_status hbm_probe_box_copy(const void* d_src, void* d_dst, uint32_t width, u
 /* Consumer: bf16 GEMM mainloop C = A * B ([MLC] overview and "TMA in a
  * pipeline"; [H200] section 02 result).  A is M x K row-major (map dims
  * {K, M}), B is K x N column-major (map dims {K, N}), both bf16 with box
- * {64, 256} and TMAP_SWIZZLE_128B or TMAP_SWIZZLE_128B_K256; tiles are staged
- * by the tile loader into a
+ * {64, 256} and TMAP_SWIZZLE_128B or TMAP_SWIZZLE_128B_K256 (or the 32-deep
+ * box that gemm_bf16_ex describes); tiles are staged by the tile loader into a
  * `stages`-deep LDS ring and consumed by MFMA bf16 with fp32 accumulation.
  * d_C is M x N row-major bf16 (round to nearest even), leading dimension
- * ldc >= N elements.  Any M, N and K: partial tiles in M and N are clipped
+ * ldc >= N elements.  Any M and N, and any K >= 1 (the maps' dim 0 is K,
+ * and a map dimension is at least 1): partial tiles in M and N are clipped
  * by the epilogue, and a K that is not a multiple of the box depth is zero-
  * filled through the maps' OOB fill (with stages = 2 only the last K tile
  * takes that slower loader, with more stages every tile).  For the 64-deep K step, stages
@@ -396,8 +397,8 @@ tmap_status hbm_probe_box_copy(const void* d_src, void* d_dst, uint32_t width, u
  * LDS) and stages = 3 the operand ring: five 32 KiB slots holding A and B
  * boxes in turn, so that A runs three deep and B two deep; it takes K a
  * multiple of 64.  Errors: NULL, UNSUPPORTED (map shape, dtype, box,
- * swizzle, OOB fill other than zero, stages, K for stages = 3, ldc < N),
- * HIP.  M == 0 or N == 0 is a no-op. */
+ * swizzle, OOB fill other than zero, stages, K for stages = 3, K == 0,
+ * ldc < N), HIP.  M == 0 or N == 0 is a no-op. */
 tmap_status gemm_bf16(const tmap_t* A, const tmap_t* B, void* d_C, uint32_t M, uint32_t N,
                       uint32_t K, uint32_t ldc, uint32_t stages, void* stream);
 

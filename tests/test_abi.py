@@ -143,6 +143,23 @@ def test_launch_argument_errors_without_gpu():
         with pytest.raises(att.TmapError) as ei:
             att.hbm_probe_copy_ex(*args)
         assert ei.value.name == name, args
+    # gemm: empty outputs are no-ops, the rest is checked before any HIP call
+    mA = att.tmap_encode("bf16", 2, BASE, (96, 256), (192,), (64, 256), None, "128b")
+    mB = att.tmap_encode("bf16", 2, BASE, (96, 512), (192,), (64, 256), None, "128b")
+    mB128 = att.tmap_encode("bf16", 2, BASE, (96, 512), (192,), (64, 128), None, "128b")
+    att.gemm_bf16(mA, mB, BASE, 0, 512, 96, 512, 2)
+    att.gemm_bf16(mA, mB, BASE, 256, 0, 96, 512, 2)
+    for call, name in ((lambda: att.gemm_bf16(mA, mB, BASE, 256, 512, 0, 512, 2), "ERR_UNSUPPORTED"),   # K == 0
+                       (lambda: att.gemm_bf16(mA, mB, BASE, 256, 512, 64, 512, 2), "ERR_UNSUPPORTED"),  # dims != K
+                       (lambda: att.gemm_bf16(mA, mB, BASE, 256, 512, 96, 500, 2), "ERR_UNSUPPORTED"),  # ldc < N
+                       (lambda: att.gemm_bf16(mA, mB, 0, 256, 512, 96, 512, 2), "ERR_NULL"),
+                       (lambda: att.gemm_bf16(mA, mB, BASE, 256, 512, 96, 512, 3), "ERR_UNSUPPORTED"),  # K % 64
+                       (lambda: att.gemm_bf16(mA, mB, BASE, 256, 512, 96, 512, 4), "ERR_UNSUPPORTED"),  # stages
+                       (lambda: att.gemm_bf16_ex(mA, mB, BASE, 256, 512, 96, 512, 2, 0, 1, 0, 7), "ERR_UNSUPPORTED"),
+                       (lambda: att.gemm_bf16(mA, mB128, BASE, 256, 512, 96, 512, 2), "ERR_UNSUPPORTED")):  # box
+        with pytest.raises(att.TmapError) as ei:
+            call()
+        assert ei.value.name == name
     # txbar_selftest_ex: poll bound and extra bytes are checked on the host
     m = att.tmap_encode("bf16", 2, BASE, (64, 64), (128,), (64, 16), None, "128b")
     with pytest.raises(att.TmapError) as ei:
